@@ -1,0 +1,316 @@
+// Bidirectional attention of the recomputed rows over every cached row.
+//
+// In a diffusion LM every position attends to every other (EntropyCache
+// explainer, Italian summary section 1), so the r recomputed query rows of a
+// skip step attend over all L rows of the layer's K/V cache: the fresh rows
+// just written and the stale cached rows of every other position. There is
+// no mask.
+//
+// bf16 kernel (head_dim 128), flash-style with an online softmax, computed
+// transposed so that no register shuffles are needed between the two
+// products: a wavefront owns 32 query rows and, per 32-row K/V sub-tile,
+//   S^T = K Q^T        8 x v_mfma_f32_32x32x16_bf16 (A = K rows, B = Q rows)
+//   O^T += V^T P^T     8 x v_mfma_f32_32x32x16_bf16 (A = V^T from LDS, B = P^T)
+// In the 32x32 accumulator layout a lane holds one query column and 16 key
+// rows; those 16 values, converted to bf16 in order, are exactly the lane's
+// B operand of the second product for the two 16-key halves, provided V^T's
+// A operand supplies keys in the same slot order (two 8-byte LDS reads).
+// Softmax statistics are per lane (one query), completed with one
+// cross-half exchange. Q stays in registers; K and V^T tiles of 64 keys are
+// staged in LDS and shared by the 4 wavefronts (128 queries) of a
+// workgroup. When heads x query tiles under-fill the 256 CUs, the key range
+// is split over workgroups and a merge kernel combines (m, l, o) exactly.
+#include "ec_internal.h"
+
+#include <math.h>
+
+namespace ec {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int D = 128;       // head_dim of the MFMA kernel
+constexpr int BQ = 128;      // queries per workgroup (32 per wavefront)
+constexpr int BKV = 64;      // keys per LDS stage
+constexpr int KS = D + 8;    // LDS row stride of K tile (bf16)
+constexpr int VS = BKV + 8;  // LDS row stride of V^T tile (bf16)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// grid: (query tiles, heads, splits)
+template <bool SPLIT>
+__global__ void __launch_bounds__(kThreads)
+attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
+                 const bf16* __restrict__ vc, int r, int L, int H, float scale_log2,
+                 int kv_chunk, bf16* __restrict__ out, float* __restrict__ po,
+                 float* __restrict__ pml) {
+  __shared__ __align__(16) bf16 sK[BKV * KS];
+  __shared__ __align__(16) bf16 sVt[D * VS];
+
+  const int qt = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int lq = lane % 32, g = lane / 32;
+  const int64_t HD = (int64_t)H * D;
+  const int qrow = qt * BQ + wave * 32 + lq;  // this lane's query (column of S^T)
+  const bool qok = qrow < r;
+
+  // Q fragments (B operand): Q[qrow][16kk + 8g .. +7]
+  bf16x8 fq[D / 16];
+  {
+    const bf16* src = q + (int64_t)(qok ? qrow : 0) * HD + h * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      uint4 u = qok ? *reinterpret_cast<const uint4*>(src + 16 * kk) : make_uint4(0, 0, 0, 0);
+      fq[kk] = *reinterpret_cast<bf16x8*>(&u);
+    }
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kv_lo = split * kv_chunk;
+  const int kv_hi = min(L, kv_lo + kv_chunk);
+
+  for (int kv0 = kv_lo; kv0 < kv_hi; kv0 += BKV) {
+    // ---- stage K (row-major) and V^T into LDS: 64 keys x 128 dims, 4 vectors per thread
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < (BKV * D / 8) / kThreads; ++i) {
+      const int v = tid + i * kThreads;
+      const int row = v / (D / 8), dv = (v % (D / 8)) * 8;
+      const int key = kv0 + row;
+      uint4 ku = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
+      if (key < kv_hi) {
+        ku = *reinterpret_cast<const uint4*>(kc + (int64_t)key * HD + h * D + dv);
+        vu = *reinterpret_cast<const uint4*>(vc + (int64_t)key * HD + h * D + dv);
+      }
+      *reinterpret_cast<uint4*>(sK + row * KS + dv) = ku;
+      const bf16* ve = reinterpret_cast<const bf16*>(&vu);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sVt[(dv + e) * VS + row] = ve[e];
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int sub = 0; sub < BKV / 32; ++sub) {
+      // ---- S^T[32 keys, 32 queries]
+      f32x16 st;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st[v] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        bf16x8 fk = *reinterpret_cast<const bf16x8*>(sK + (sub * 32 + lq) * KS + 16 * kk + 8 * g);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk, fq[kk], st, 0, 0, 0);
+      }
+      // key of st[v]: kv0 + sub*32 + 8(v/4) + 4g + v%4
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kv0 + sub * 32 + 8 * (v / 4) + 4 * g + (v % 4);
+        st[v] = key < kv_hi ? st[v] * scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, st[v]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      float alpha, psum = 0.f;
+      bf16x8 fp[2];
+      if (m_new == -INFINITY) {  // nothing valid yet (cannot happen for L >= 1)
+        alpha = 1.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) fp[v / 8][v % 8] = (bf16)0.f;
+      } else {
+        alpha = exp2f(m_run - m_new);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = exp2f(st[v] - m_new);
+          psum += p;
+          fp[v / 8][v % 8] = (bf16)p;
+        }
+      }
+      psum += __shfl_xor(psum, 32);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+      // ---- O^T[d, q] += V^T[d, keys] P^T[keys, q], two 16-key chunks
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+          const bf16* vr = sVt + (32 * i + lq) * VS + sub * 32 + 16 * c + 4 * g;
+          bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+          bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 8);
+          bf16x8 fv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            fv[e] = lo[e];
+            fv[4 + e] = hi[e];
+          }
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv, fp[c], o[i], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  if (!qok) return;
+  // o[i][v]: dim = 32i + 8(v/4) + 4g + v%4 of query qrow
+  if (!SPLIT) {
+    const float inv = 1.0f / l_run;
+    bf16* dst = out + (int64_t)qrow * HD + h * D;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) dst[32 * i + 8 * (v / 4) + 4 * g + (v % 4)] = (bf16)(o[i][v] * inv);
+  } else {
+    float* dst = po + (((int64_t)split * r + qrow) * H + h) * D;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) dst[32 * i + 8 * (v / 4) + 4 * g + (v % 4)] = o[i][v];
+    if (g == 0) {
+      float* ml = pml + (((int64_t)split * r + qrow) * H + h) * 2;
+      ml[0] = m_run;
+      ml[1] = l_run;
+    }
+  }
+}
+
+// combine split partials: one thread per (query, head, dim)
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+attn_merge_kernel(const float* __restrict__ po, const float* __restrict__ pml, int S, int r,
+                  int H, int Dh, T* __restrict__ out) {
+  const int64_t t = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+  if (t >= (int64_t)r * H * Dh) return;
+  const int64_t qh = t / Dh;
+  const int d = (int)(t % Dh);
+  float m = -INFINITY;
+  for (int s = 0; s < S; ++s) m = fmaxf(m, pml[((int64_t)s * r * H + qh) * 2]);
+  float l = 0.f, acc = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float ms = pml[((int64_t)s * r * H + qh) * 2];
+    if (ms == -INFINITY) continue;
+    const float w = exp2f(ms - m);
+    l += pml[((int64_t)s * r * H + qh) * 2 + 1] * w;
+    acc += po[((int64_t)s * r * H + qh) * Dh + d] * w;
+  }
+  out[qh * Dh + d] = from_f<T>(acc / l);
+}
+
+// fp32 path: one workgroup per (query, head); scores in LDS, exact softmax.
+__global__ void __launch_bounds__(kThreads)
+attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ kc,
+                const float* __restrict__ vc, int L, int H, int Dh, float scale,
+                float* __restrict__ out) {
+  extern __shared__ float sc[];  // [L] scores, then [Dh] query
+  float* sq = sc + L;
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int64_t HD = (int64_t)H * Dh;
+  for (int d = threadIdx.x; d < Dh; d += kThreads) sq[d] = q[(int64_t)i * HD + h * Dh + d];
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j < L; j += kThreads) {
+    const float* kr = kc + (int64_t)j * HD + h * Dh;
+    float s = 0.f;
+    for (int d = 0; d < Dh; ++d) s = fmaf(sq[d], kr[d], s);
+    s *= scale;
+    sc[j] = s;
+    mx = fmaxf(mx, s);
+  }
+  __shared__ float red[kThreads];
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+  float sum = 0.f;
+  for (int j = threadIdx.x; j < L; j += kThreads) {
+    const float e = __expf(sc[j] - mx);
+    sc[j] = e;
+    sum += e;
+  }
+  red[threadIdx.x] = sum;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const float inv = 1.0f / red[0];
+  for (int d = threadIdx.x; d < Dh; d += kThreads) {
+    float acc = 0.f;
+    for (int j = 0; j < L; ++j) acc = fmaf(sc[j], vc[(int64_t)j * HD + h * Dh + d], acc);
+    out[(int64_t)i * HD + h * Dh + d] = acc * inv;
+  }
+}
+
+struct AttnPlan {
+  int qtiles, splits, chunk;
+};
+
+AttnPlan plan_attn(int r, int L, int H) {
+  AttnPlan p;
+  p.qtiles = (r + BQ - 1) / BQ;
+  const int base = p.qtiles * H;
+  int s = 1;
+  while (base * s < 256 && L / (2 * s) >= 2 * BKV) s *= 2;
+  p.chunk = ((L + s - 1) / s + BKV - 1) / BKV * BKV;
+  p.splits = (L + p.chunk - 1) / p.chunk;
+  return p;
+}
+
+}  // namespace
+
+size_t attn_ws_bytes(int r, int L, int H, int Dh) {
+  if (r <= 0 || Dh != D) return 0;
+  AttnPlan p = plan_attn(r, L, H);
+  if (p.splits <= 1) return 0;
+  return (size_t)p.splits * r * H * (Dh + 2) * sizeof(float) + 512;
+}
+
+ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, int L, int H,
+               int Dh, float scale, void* out, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (r == 0) return EC_OK;
+  EC_REQUIRE(L >= 1, EC_ERR_ARG, "attn: seq_len must be >= 1");
+  if (dt == EC_F32) {
+    EC_REQUIRE(Dh <= 1024 && (size_t)(L + Dh) * 4 <= 64 * 1024, EC_ERR_UNSUPPORTED,
+               "attn: f32 path supports L + head_dim <= 16384");
+    dim3 grid(r, H);
+    attn_f32_kernel<<<grid, kThreads, (L + Dh) * sizeof(float), s>>>(
+        (const float*)q, (const float*)k, (const float*)v, L, H, Dh, scale, (float*)out);
+    EC_CHECK_LAUNCH("attn_f32_kernel");
+    return EC_OK;
+  }
+  EC_REQUIRE(Dh == D, EC_ERR_UNSUPPORTED, "attn: bf16 path needs head_dim 128 (got %d)", Dh);
+  AttnPlan p = plan_attn(r, L, H);
+  const float sl = scale * kLog2e;
+  dim3 grid(p.qtiles, H, p.splits);
+  if (p.splits == 1) {
+    attn_bf16_kernel<false><<<grid, kThreads, 0, s>>>((const bf16*)q, (const bf16*)k,
+                                                      (const bf16*)v, r, L, H, sl, p.chunk,
+                                                      (bf16*)out, nullptr, nullptr);
+    EC_CHECK_LAUNCH("attn_bf16_kernel");
+    return EC_OK;
+  }
+  const size_t need = attn_ws_bytes(r, L, H, Dh);
+  EC_REQUIRE(ws && ws_bytes >= need, EC_ERR_WORKSPACE, "attn: workspace %zu < %zu", ws_bytes, need);
+  float* po = (float*)ws;
+  float* pml = po + (size_t)p.splits * r * H * Dh;
+  attn_bf16_kernel<true><<<grid, kThreads, 0, s>>>((const bf16*)q, (const bf16*)k, (const bf16*)v,
+                                                   r, L, H, sl, p.chunk, nullptr, po, pml);
+  EC_CHECK_LAUNCH("attn_bf16_kernel");
+  const int64_t n = (int64_t)r * H * Dh;
+  attn_merge_kernel<bf16><<<(int)((n + kThreads - 1) / kThreads), kThreads, 0, s>>>(
+      po, pml, p.splits, r, H, Dh, (bf16*)out);
+  EC_CHECK_LAUNCH("attn_merge_kernel");
+  return EC_OK;
+}
+
+}  // namespace ec

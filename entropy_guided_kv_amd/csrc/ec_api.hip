@@ -1,0 +1,436 @@
+// C ABI of libec.so: argument checks, workspace planning, and the per-step
+// orchestration of the EntropyCache denoising step (include/ec.h).
+#include "ec_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+namespace ec {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+ec_status hip_fail(hipError_t e, const char* what) {
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return EC_ERR_HIP;
+}
+
+namespace {
+
+size_t esize(ec_dtype dt) { return dt == EC_BF16 ? 2 : 4; }
+bool dtype_ok(ec_dtype dt) { return dt == EC_F32 || dt == EC_BF16; }
+
+ec_status check_model(const ec_model_desc* m) {
+  EC_REQUIRE(m && m->struct_size >= sizeof(ec_model_desc), EC_ERR_ARG, "model: null or struct_size too small");
+  EC_REQUIRE(dtype_ok(m->dtype), EC_ERR_DTYPE, "model: bad dtype %d", (int)m->dtype);
+  EC_REQUIRE(m->n_layers >= 1 && m->n_layers <= EC_MAX_LAYERS, EC_ERR_ARG, "model: n_layers %d", m->n_layers);
+  EC_REQUIRE(m->d_model > 0 && m->n_heads > 0 && m->head_dim > 0 && m->ffn_dim > 0 && m->vocab > 0,
+             EC_ERR_ARG, "model: non-positive dimension");
+  EC_REQUIRE(m->n_heads * m->head_dim == m->d_model, EC_ERR_ARG, "model: n_heads*head_dim != d_model");
+  EC_REQUIRE(m->head_dim % 2 == 0, EC_ERR_ARG, "model: head_dim must be even");
+  EC_REQUIRE(m->embed && m->layers && m->final_norm && m->lm_head && m->rope_cos && m->rope_sin,
+             EC_ERR_ARG, "model: null pointer");
+  for (int l = 0; l < m->n_layers; ++l) {
+    const ec_layer_weights& w = m->layers[l];
+    EC_REQUIRE(w.attn_norm && w.wqkv && w.wo && w.mlp_norm && w.w_gate && w.w_up && w.w_down,
+               EC_ERR_ARG, "model: null weight in layer %d", l);
+  }
+  if (m->dtype == EC_BF16) {
+    EC_REQUIRE(m->head_dim == 128, EC_ERR_UNSUPPORTED, "bf16 model: head_dim must be 128");
+    EC_REQUIRE(m->d_model % 256 == 0 && m->ffn_dim % 128 == 0 && m->vocab % 128 == 0,
+               EC_ERR_UNSUPPORTED, "bf16 model: need d %% 256, F %% 128, V %% 128 == 0");
+    EC_REQUIRE(m->d_model % 64 == 0 && m->ffn_dim % 64 == 0, EC_ERR_UNSUPPORTED,
+               "bf16 model: d and F must be multiples of 64");
+  } else {
+    EC_REQUIRE(m->d_model % 4 == 0, EC_ERR_UNSUPPORTED, "f32 model: d_model %% 4 != 0");
+  }
+  return EC_OK;
+}
+
+ec_status check_cache(const ec_cache_desc* c, const ec_model_desc* m) {
+  EC_REQUIRE(c && c->struct_size >= sizeof(ec_cache_desc), EC_ERR_ARG, "cache: null or struct_size too small");
+  EC_REQUIRE(c->seq_len >= 1 && c->k && c->v, EC_ERR_ARG, "cache: bad seq_len or null arrays");
+  EC_REQUIRE(c->seq_len <= m->rope_max_pos, EC_ERR_ARG, "cache: seq_len %d > rope_max_pos %d",
+             c->seq_len, m->rope_max_pos);
+  for (int l = 0; l < m->n_layers; ++l)
+    EC_REQUIRE(c->k[l] && c->v[l], EC_ERR_ARG, "cache: null pointer for layer %d", l);
+  return EC_OK;
+}
+
+struct FwdWs {
+  float* h;
+  void* a;
+  void* q;
+  void* o;
+  void* s;
+  void* xn;
+  float* splitk;
+  size_t splitk_bytes;
+  void* attn;
+  size_t attn_bytes;
+};
+
+size_t splitk_max(const ec_model_desc* m, int max_rows, int max_out) {
+  if (m->dtype != EC_BF16) return 0;
+  const int d = m->d_model, F = m->ffn_dim, V = m->vocab;
+  size_t best = 0;
+  for (int M = 1; M <= max_rows; ++M) {
+    best = std::max(best, gemm_splitk_ws_bytes(M, 3 * d, d, EPI_QKV, true));
+    best = std::max(best, gemm_splitk_ws_bytes(M, d, d, EPI_RESID, true));
+    best = std::max(best, gemm_splitk_ws_bytes(M, F, d, EPI_SWIGLU, true));
+    best = std::max(best, gemm_splitk_ws_bytes(M, d, F, EPI_RESID, true));
+  }
+  for (int M = 1; M <= max_out; ++M) best = std::max(best, gemm_splitk_ws_bytes(M, V, d, EPI_STORE, true));
+  return best;
+}
+
+size_t attn_max(const ec_model_desc* m, int max_rows, int L) {
+  size_t best = 0;
+  for (int r = 1; r <= max_rows; ++r)
+    best = std::max(best, attn_ws_bytes(r, L, m->n_heads, m->head_dim));
+  return best;
+}
+
+// carve the forward's workspace; with base == nullptr only computes the size
+size_t carve_fwd(const ec_model_desc* m, int max_rows, int max_out, int L, void* base, size_t cap,
+                 FwdWs* w) {
+  Carver c(base, cap);
+  const size_t es = esize(m->dtype);
+  const int d = m->d_model, F = m->ffn_dim;
+  FwdWs x;
+  x.h = c.take<float>((size_t)max_rows * d);
+  x.a = c.take<char>((size_t)max_rows * d * es);
+  x.q = c.take<char>((size_t)max_rows * d * es);
+  x.o = c.take<char>((size_t)max_rows * d * es);
+  x.s = c.take<char>((size_t)max_rows * F * es);
+  x.xn = c.take<char>((size_t)std::max(max_out, 1) * d * es);
+  x.splitk_bytes = splitk_max(m, max_rows, max_out);
+  x.splitk = c.take<float>(x.splitk_bytes / sizeof(float) + 1);
+  x.attn_bytes = attn_max(m, max_rows, L);
+  x.attn = c.take<char>(x.attn_bytes + 1);
+  if (w) *w = x;
+  return c.off + 256;
+}
+
+// The forward over `rows` (see ec_forward). All pointers validated by the caller.
+ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int32_t* tokens,
+                      const int32_t* rows, int n_rows, const int32_t* out_idx, int n_out,
+                      void* logits, float* hidden, const FwdWs& w, hipStream_t s) {
+  const ec_dtype dt = m->dtype;
+  const int d = m->d_model, F = m->ffn_dim, V = m->vocab, H = m->n_heads, Dh = m->head_dim;
+  const int L = c->seq_len;
+  const float scale = 1.0f / sqrtf((float)Dh);
+  ec_status st;
+#define EC_TRY(x)            \
+  do {                       \
+    st = (x);                \
+    if (st != EC_OK) return st; \
+  } while (0)
+  if (n_rows > 0) {
+    EC_TRY(embed(dt, m->embed, V, tokens, L, rows, n_rows, d, w.h, s));
+    for (int l = 0; l < m->n_layers; ++l) {
+      const ec_layer_weights& lw = m->layers[l];
+      EC_TRY(rmsnorm(dt, w.h, n_rows, nullptr, n_rows, d, lw.attn_norm, m->rms_eps, w.a, s));
+      EpiArgs e{};
+      e.kind = EPI_QKV;
+      e.out = w.q;
+      e.ldo = d;
+      e.k_cache = c->k[l];
+      e.v_cache = c->v[l];
+      e.rows = rows;
+      e.rope_cos = m->rope_cos;
+      e.rope_sin = m->rope_sin;
+      e.d_model = d;
+      e.head_dim = Dh;
+      e.seq_len = L;
+      EC_TRY(gemm(dt, w.a, lw.wqkv, nullptr, n_rows, 3 * d, d, e, w.splitk, w.splitk_bytes, s));
+      EC_TRY(attn(dt, w.q, c->k[l], c->v[l], n_rows, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
+      EpiArgs r{};
+      r.kind = EPI_RESID;
+      r.resid = w.h;
+      r.ldo = d;
+      EC_TRY(gemm(dt, w.o, lw.wo, nullptr, n_rows, d, d, r, w.splitk, w.splitk_bytes, s));
+      EC_TRY(rmsnorm(dt, w.h, n_rows, nullptr, n_rows, d, lw.mlp_norm, m->rms_eps, w.a, s));
+      EpiArgs g{};
+      g.kind = EPI_SWIGLU;
+      g.out = w.s;
+      g.ldo = F;
+      EC_TRY(gemm(dt, w.a, lw.w_gate, lw.w_up, n_rows, F, d, g, w.splitk, w.splitk_bytes, s));
+      EC_TRY(gemm(dt, w.s, lw.w_down, nullptr, n_rows, d, F, r, w.splitk, w.splitk_bytes, s));
+    }
+  }
+  if (hidden && n_rows > 0)
+    EC_CHECK_HIP(hipMemcpyAsync(hidden, w.h, (size_t)n_rows * d * sizeof(float),
+                                hipMemcpyDeviceToDevice, s));
+  if (n_out > 0) {
+    EC_TRY(rmsnorm(dt, w.h, n_rows, out_idx, n_out, d, m->final_norm, m->rms_eps, w.xn, s));
+    EpiArgs o{};
+    o.kind = EPI_STORE;
+    o.out = logits;
+    o.ldo = V;
+    EC_TRY(gemm(dt, w.xn, m->lm_head, nullptr, n_out, V, d, o, w.splitk, w.splitk_bytes, s));
+  }
+#undef EC_TRY
+  return EC_OK;
+}
+
+// ec_step workspace: forward (rows up to L, outputs up to B) + logits + reduction + result
+struct StepWs {
+  FwdWs fwd;
+  void* logits;
+  float* H;
+  int32_t* amax;
+  float* conf;
+  void* ent_ws;
+  size_t ent_bytes;
+};
+
+int max_cand(const ec_params* p) {
+  return std::max(1, std::min(p->block_len, p->seq_len - p->prompt_len));
+}
+
+size_t carve_step(const ec_model_desc* m, const ec_params* p, void* base, size_t cap, StepWs* w) {
+  const int L = p->seq_len, O = max_cand(p);
+  StepWs x;
+  const size_t fwd = carve_fwd(m, L, O, L, base, cap, &x.fwd);
+  Carver c(base, cap);
+  c.off = fwd;
+  x.logits = c.take<char>((size_t)O * m->vocab * esize(m->dtype));
+  x.H = c.take<float>(O);
+  x.amax = c.take<int32_t>(O);
+  x.conf = c.take<float>(O);
+  x.ent_bytes = entropy_ws_bytes(O, m->vocab);
+  x.ent_ws = c.take<char>(x.ent_bytes + 1);
+  if (w) *w = x;
+  return c.off + 256;
+}
+
+ec_status check_params(const ec_params* p, const ec_model_desc* m, const ec_cache_desc* c) {
+  EC_REQUIRE(p && p->struct_size >= sizeof(ec_params), EC_ERR_ARG, "params: null or struct_size too small");
+  EC_REQUIRE(p->seq_len >= 1 && p->prompt_len >= 0 && p->prompt_len <= p->seq_len, EC_ERR_ARG,
+             "params: bad seq_len / prompt_len");
+  EC_REQUIRE(p->block_len >= 1, EC_ERR_ARG, "params: block_len must be >= 1");
+  EC_REQUIRE(p->k_recent >= 0, EC_ERR_ARG, "params: k_recent must be >= 0");
+  EC_REQUIRE(p->tokens_per_step >= 1 && p->tokens_per_step <= EC_MAX_TOKENS_PER_STEP, EC_ERR_ARG,
+             "params: tokens_per_step must be in [1, %d]", EC_MAX_TOKENS_PER_STEP);
+  EC_REQUIRE(!(p->tau != p->tau), EC_ERR_ARG, "params: tau is NaN");
+  if (m) EC_REQUIRE(p->mask_id >= 0 && p->mask_id < m->vocab, EC_ERR_ARG, "params: mask_id out of range");
+  if (c) EC_REQUIRE(c->seq_len == p->seq_len, EC_ERR_ARG, "params: seq_len differs from cache");
+  return EC_OK;
+}
+
+}  // namespace
+}  // namespace ec
+
+using namespace ec;
+
+extern "C" {
+
+const char* ec_last_error(void) { return g_err; }
+int ec_version(void) { return EC_VERSION; }
+
+size_t ec_entropy_max_workspace_size(int32_t rows, int32_t vocab) {
+  return entropy_ws_bytes(rows, vocab);
+}
+
+ec_status ec_entropy_max(const void* logits, ec_dtype dtype, int32_t rows, int32_t vocab,
+                         int64_t row_stride, const int32_t* sel, int32_t n_sel, float* entropy,
+                         int32_t* argmax, float* maxprob, float* emax, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  EC_REQUIRE(dtype_ok(dtype), EC_ERR_DTYPE, "ec_entropy_max: bad dtype %d", (int)dtype);
+  EC_REQUIRE(rows >= 0 && vocab >= 1 && row_stride >= vocab, EC_ERR_ARG,
+             "ec_entropy_max: rows %d vocab %d stride %lld", rows, vocab, (long long)row_stride);
+  EC_REQUIRE(n_sel >= 0, EC_ERR_ARG, "ec_entropy_max: n_sel < 0");
+  if (rows > 0) {
+    EC_REQUIRE(logits && entropy && argmax && maxprob, EC_ERR_ARG, "ec_entropy_max: null pointer");
+    const size_t need = entropy_ws_bytes(rows, vocab);
+    EC_REQUIRE(workspace && workspace_bytes >= need, EC_ERR_WORKSPACE,
+               "ec_entropy_max: workspace %zu < %zu bytes", workspace_bytes, need);
+  }
+  return ec::entropy(dtype, logits, rows, vocab, row_stride, sel, n_sel, entropy, argmax, maxprob, emax,
+                 workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+ec_status ec_cache_scatter(void* k_cache, void* v_cache, int64_t seq_len, int32_t width,
+                           ec_dtype dtype, const void* k_rows, const void* v_rows,
+                           const int32_t* idx, int32_t n_rows, void* stream) {
+  EC_REQUIRE(dtype_ok(dtype), EC_ERR_DTYPE, "ec_cache_scatter: bad dtype %d", (int)dtype);
+  EC_REQUIRE(seq_len >= 0 && width >= 1 && n_rows >= 0, EC_ERR_ARG, "ec_cache_scatter: bad sizes");
+  if (n_rows == 0) return EC_OK;
+  EC_REQUIRE(k_cache && v_cache && k_rows && v_rows && idx, EC_ERR_ARG, "ec_cache_scatter: null pointer");
+  return scatter(dtype, k_cache, v_cache, seq_len, width, k_rows, v_rows, idx, n_rows,
+                 (hipStream_t)stream);
+}
+
+size_t ec_partial_attn_workspace_size(int32_t r, int32_t seq_len, int32_t n_heads, int32_t head_dim) {
+  return attn_ws_bytes(r, seq_len, n_heads, head_dim);
+}
+
+ec_status ec_partial_attn(const void* q, const void* k_cache, const void* v_cache, int32_t r,
+                          int32_t seq_len, int32_t n_heads, int32_t head_dim, float scale,
+                          ec_dtype dtype, void* out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  EC_REQUIRE(dtype_ok(dtype), EC_ERR_DTYPE, "ec_partial_attn: bad dtype %d", (int)dtype);
+  EC_REQUIRE(r >= 0 && seq_len >= 1 && n_heads >= 1 && head_dim >= 1, EC_ERR_ARG,
+             "ec_partial_attn: bad sizes");
+  if (r == 0) return EC_OK;
+  EC_REQUIRE(q && k_cache && v_cache && out, EC_ERR_ARG, "ec_partial_attn: null pointer");
+  return attn(dtype, q, k_cache, v_cache, r, seq_len, n_heads, head_dim, scale, out, workspace,
+              workspace_bytes, (hipStream_t)stream);
+}
+
+ec_status ec_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t head_dim,
+                        double base, void* stream) {
+  EC_REQUIRE(cos_out && sin_out && max_pos >= 1 && head_dim >= 2 && head_dim % 2 == 0 && base > 0,
+             EC_ERR_ARG, "ec_rope_table: bad arguments");
+  return rope_table(cos_out, sin_out, max_pos, head_dim, base, (hipStream_t)stream);
+}
+
+size_t ec_forward_workspace_size(const ec_model_desc* model, int32_t max_rows, int32_t max_out,
+                                 int32_t seq_len) {
+  if (check_model(model) != EC_OK || max_rows < 0 || max_out < 0 || seq_len < 1) return 0;
+  return carve_fwd(model, std::max(max_rows, 1), max_out, seq_len, nullptr, 0, nullptr);
+}
+
+ec_status ec_forward(const ec_model_desc* model, const ec_cache_desc* cache, const int32_t* tokens,
+                     const int32_t* rows, int32_t n_rows, const int32_t* out_idx, int32_t n_out,
+                     void* logits, float* hidden, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  ec_status st = check_model(model);
+  if (st != EC_OK) return st;
+  st = check_cache(cache, model);
+  if (st != EC_OK) return st;
+  EC_REQUIRE(n_rows >= 0 && n_rows <= cache->seq_len && n_out >= 0 && n_out <= std::max(n_rows, 0),
+             EC_ERR_ARG, "ec_forward: n_rows %d n_out %d", n_rows, n_out);
+  EC_REQUIRE(tokens && (rows || n_rows == 0) && (out_idx || n_out == 0) && (logits || n_out == 0),
+             EC_ERR_ARG, "ec_forward: null pointer");
+  const size_t need = carve_fwd(model, std::max(n_rows, 1), n_out, cache->seq_len, nullptr, 0, nullptr);
+  EC_REQUIRE(workspace && workspace_bytes >= need, EC_ERR_WORKSPACE,
+             "ec_forward: workspace %zu < %zu bytes", workspace_bytes, need);
+  FwdWs w;
+  carve_fwd(model, std::max(n_rows, 1), n_out, cache->seq_len, workspace, workspace_bytes, &w);
+  return run_forward(model, cache, tokens, rows, n_rows, out_idx, n_out, logits, hidden, w,
+                     (hipStream_t)stream);
+}
+
+size_t ec_state_plan_words(int32_t seq_len, int32_t k_recent) {
+  if (seq_len < 1) return 0;
+  return (size_t)PlanLayout(seq_len, k_recent).words;
+}
+
+size_t ec_step_workspace_size(const ec_model_desc* model, const ec_params* params) {
+  if (check_model(model) != EC_OK || check_params(params, model, nullptr) != EC_OK) return 0;
+  return carve_step(model, params, nullptr, 0, nullptr);
+}
+
+ec_status ec_state_reset(ec_state* state, const ec_params* params, void* stream) {
+  ec_status st = check_params(params, nullptr, nullptr);
+  if (st != EC_OK) return st;
+  EC_REQUIRE(state && state->struct_size >= sizeof(ec_state) && state->tokens && state->masked &&
+                 state->plan,
+             EC_ERR_ARG, "ec_state_reset: bad state");
+  hipStream_t s = (hipStream_t)stream;
+  StepResult* rec = (StepResult*)(state->plan + PlanLayout(params->seq_len, params->k_recent).RES);
+  st = plan_reset(state->tokens, state->masked, state->plan, *params, rec, s);
+  StepResult h;
+  if (st == EC_OK) {
+    hipError_t e = hipMemcpyAsync(&h, rec, sizeof(StepResult), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) st = hip_fail(e, "ec_state_reset: readback");
+  }
+  if (st != EC_OK) return st;
+  state->t = 0;
+  state->refresh_next = 1;
+  state->n_masked = h.n_masked;
+  state->n_decoded = 0;
+  state->next_rows = h.next_rows;
+  state->next_cand = h.next_cand;
+  return EC_OK;
+}
+
+ec_status ec_step(const ec_model_desc* model, const ec_cache_desc* cache, ec_state* state,
+                  const ec_params* params, void* workspace, size_t workspace_bytes, void* stream,
+                  ec_step_out* out) {
+  ec_status st = check_model(model);
+  if (st != EC_OK) return st;
+  st = check_cache(cache, model);
+  if (st != EC_OK) return st;
+  st = check_params(params, model, cache);
+  if (st != EC_OK) return st;
+  EC_REQUIRE(state && state->struct_size >= sizeof(ec_state) && state->tokens && state->masked &&
+                 state->plan,
+             EC_ERR_ARG, "ec_step: bad state");
+  EC_REQUIRE(out && out->struct_size >= sizeof(ec_step_out), EC_ERR_ARG, "ec_step: bad out");
+  const size_t need = carve_step(model, params, nullptr, 0, nullptr);
+  EC_REQUIRE(workspace && workspace_bytes >= need, EC_ERR_WORKSPACE,
+             "ec_step: workspace %zu < %zu bytes", workspace_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  const uint32_t osz = out->struct_size;
+  memset(out, 0, sizeof(ec_step_out));
+  out->struct_size = osz;
+  if (state->n_masked <= 0) return EC_OK;
+
+  StepWs w;
+  carve_step(model, params, workspace, workspace_bytes, &w);
+  const PlanLayout lay(params->seq_len, params->k_recent);
+  StepResult* res = (StepResult*)(state->plan + lay.RES);
+  const bool full = state->t == 0 || state->refresh_next;
+  const int L = params->seq_len;
+  const int n_rows = full ? L : state->next_rows;
+  const int n_cand = state->next_cand;
+  const int32_t* rows = state->plan + (full ? lay.J0 : lay.R0);
+  // candidate indices into rows: positions themselves on a full step
+  const int32_t* cidx = state->plan + (full ? lay.C0 : lay.I0);
+
+  st = run_forward(model, cache, state->tokens, rows, n_rows, cidx, n_cand, w.logits, nullptr,
+                   w.fwd, s);
+  if (st != EC_OK) return st;
+  st = entropy(model->dtype, w.logits, n_cand, model->vocab, model->vocab, nullptr, 0, w.H, w.amax,
+               w.conf, nullptr, w.ent_ws, w.ent_bytes, s);
+  if (st != EC_OK) return st;
+  st = select_decode(w.H, w.amax, w.conf, n_cand, state->tokens, state->masked, state->plan,
+                     *params, res, s);
+  if (st != EC_OK) return st;
+  StepResult h;
+  EC_CHECK_HIP(hipMemcpyAsync(&h, res, sizeof(StepResult), hipMemcpyDeviceToHost, s));
+  EC_CHECK_HIP(hipStreamSynchronize(s));
+
+  const bool nan = h.has_nan != 0;
+  const bool refresh = nan || (h.emax > params->tau);
+  out->status = nan ? EC_ERR_NAN : EC_OK;
+  out->refreshed = full ? 1 : 0;
+  out->rows = n_rows;
+  out->n_cand = n_cand;
+  out->n_decoded = h.n_picked;
+  out->refresh_next = refresh ? 1 : 0;
+  out->emax = h.emax;
+  for (int i = 0; i < h.n_picked && i < EC_MAX_TOKENS_PER_STEP; ++i) {
+    out->positions[i] = h.pos[i];
+    out->ids[i] = h.ids[i];
+    out->entropy[i] = h.ent[i];
+    out->maxprob[i] = h.conf[i];
+  }
+  state->t += 1;
+  state->refresh_next = refresh ? 1 : 0;
+  state->n_masked = h.n_masked;
+  state->n_decoded += h.n_picked;
+  state->next_rows = h.next_rows;
+  state->next_cand = h.next_cand;
+  if (nan) {
+    set_error("ec_step: E is NaN at step %d; next step refreshes", state->t - 1);
+    return EC_ERR_NAN;
+  }
+  return EC_OK;
+}
+
+}  // extern "C"

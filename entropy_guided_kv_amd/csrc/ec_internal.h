@@ -1,0 +1,150 @@
+// Internal declarations shared by the HIP sources of libec.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "ec.h"
+
+namespace ec {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+// ---------------------------------------------------------------- errors
+void set_error(const char* fmt, ...);
+ec_status hip_fail(hipError_t e, const char* what);
+
+#define EC_CHECK_HIP(call)                                   \
+  do {                                                       \
+    hipError_t _e = (call);                                  \
+    if (_e != hipSuccess) return ::ec::hip_fail(_e, #call);  \
+  } while (0)
+#define EC_CHECK_LAUNCH(what)                                \
+  do {                                                       \
+    hipError_t _e = hipGetLastError();                       \
+    if (_e != hipSuccess) return ::ec::hip_fail(_e, what);   \
+  } while (0)
+#define EC_REQUIRE(cond, code, ...)                          \
+  do {                                                       \
+    if (!(cond)) { ::ec::set_error(__VA_ARGS__); return code; } \
+  } while (0)
+
+// ---------------------------------------------------------------- workspace carving
+struct Carver {
+  char* base;
+  size_t off = 0;
+  size_t cap;
+  Carver(void* b, size_t c) : base((char*)b), cap(c) {}
+  template <typename T> T* take(size_t n) {
+    off = (off + 255) & ~size_t(255);
+    T* p = (T*)(base ? base + off : nullptr);
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+// ---------------------------------------------------------------- GEMM
+// C[M,N] = A[M,K] . B[N,K]^T with fused epilogues.
+enum EpiKind { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
+
+struct EpiArgs {
+  int kind;
+  void* out;          // STORE: T[M, ldo]; SWIGLU: T[M, ldo]; QKV: q rows T[M, d]
+  float* resid;       // RESID: float[M, ldo] updated in place (h += acc)
+  int64_t ldo;
+  // QKV: k/v cache rows at positions rows[m]
+  void* k_cache;
+  void* v_cache;
+  const int32_t* rows;
+  const float* rope_cos;
+  const float* rope_sin;
+  int d_model, head_dim;
+  int seq_len;        // QKV: rows[m] outside [0, seq_len) are not written
+};
+
+size_t gemm_splitk_ws_bytes(int M, int N, int K, int kind, bool bf16);
+ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M, int N, int K,
+               const EpiArgs& epi, float* splitk_ws, size_t splitk_ws_bytes, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+size_t attn_ws_bytes(int r, int L, int H, int D);
+ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, int L, int H, int D,
+               float scale, void* out, void* ws, size_t ws_bytes, hipStream_t s);
+
+// ---------------------------------------------------------------- entropy
+size_t entropy_ws_bytes(int rows, int vocab);
+ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t stride,
+                  const int32_t* sel, int n_sel, float* H, int32_t* amax, float* c, float* emax,
+                  void* ws, size_t ws_bytes, hipStream_t s);
+
+// ---------------------------------------------------------------- elementwise
+ec_status embed(ec_dtype dt, const void* table, int vocab, const int32_t* tokens, int L,
+                const int32_t* rows, int n, int d, float* h, hipStream_t s);
+ec_status rmsnorm(ec_dtype dt, const float* h, int n_src, const int32_t* idx, int n, int d,
+                  const void* gain, float eps, void* out, hipStream_t s);
+ec_status scatter(ec_dtype dt, void* kc, void* vc, int64_t L, int width, const void* kr,
+                  const void* vr, const int32_t* idx, int n, hipStream_t s);
+
+// ---------------------------------------------------------------- decode / plan
+// plan buffer layout (int32 words), L = seq_len, k = k_recent (ring size max(k,1)):
+//   [0]            ring count (decoded so far)
+//   [1]            rows in the recompute list R
+//   [2]            candidates
+//   [3]            masked positions left
+//   [8 .. 8+K)     ring of decoded positions (K = max(k,1))
+//   [R0 .. R0+L)   R (ascending positions), R0 = 8 + K
+//   [C0 .. C0+L)   candidate positions (ascending)
+//   [I0 .. I0+L)   candidate indices into R
+//   [J0 .. J0+L)   iota 0..L-1 (rows of a full forward)
+//   [RES ..)       StepResult record of the last reset / step
+struct StepResult;
+struct PlanLayout {
+  int K, R0, C0, I0, J0, RES, words;
+  __host__ __device__ inline PlanLayout(int L, int k);
+};
+
+// device result of one step, copied to the host once per step
+struct StepResult {
+  int32_t n_picked;
+  int32_t has_nan;
+  float emax;
+  int32_t next_rows;
+  int32_t next_cand;
+  int32_t n_masked;
+  int32_t pad[2];
+  int32_t pos[EC_MAX_TOKENS_PER_STEP];
+  int32_t ids[EC_MAX_TOKENS_PER_STEP];
+  float ent[EC_MAX_TOKENS_PER_STEP];
+  float conf[EC_MAX_TOKENS_PER_STEP];
+};
+
+__host__ __device__ inline PlanLayout::PlanLayout(int L, int k) {
+  K = k > 0 ? k : 1;
+  R0 = 8 + K;
+  C0 = R0 + L;
+  I0 = C0 + L;
+  J0 = I0 + L;
+  RES = J0 + L;
+  words = RES + (int)(sizeof(StepResult) / sizeof(int32_t));
+}
+
+ec_status plan_reset(int32_t* tokens, uint8_t* masked, int32_t* plan, const ec_params& p,
+                     StepResult* res, hipStream_t s);
+ec_status select_decode(const float* H, const int32_t* amax, const float* conf, int n_cand,
+                        int32_t* tokens, uint8_t* masked, int32_t* plan, const ec_params& p,
+                        StepResult* res, hipStream_t s);
+
+ec_status rope_table(float* c, float* sn, int max_pos, int head_dim, double base, hipStream_t s);
+
+}  // namespace ec

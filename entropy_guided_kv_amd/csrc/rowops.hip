@@ -1,0 +1,164 @@
+// Row-wise kernels of the forward: embedding gather, RMSNorm, K/V cache
+// scatter and the rotary-angle tables.
+//
+// All are bandwidth-bound and move whole rows with 16-byte vector accesses,
+// one workgroup per row (rows are d_model = 2048..4096 elements wide).
+#include "ec_internal.h"
+
+#include <math.h>
+
+namespace ec {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// h[i, :] = embed[tokens[rows[i]], :]  (fp32 residual stream)
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+embed_kernel(const T* __restrict__ table, int vocab, const int32_t* __restrict__ tokens, int L,
+             const int32_t* __restrict__ rows, int d, float* __restrict__ h) {
+  const int i = blockIdx.x;
+  const int p = rows[i];
+  const int tok = (p >= 0 && p < L) ? tokens[p] : -1;
+  float* dst = h + (int64_t)i * d;
+  if (tok < 0 || tok >= vocab) {  // invalid position or id: zero row
+    for (int j = threadIdx.x; j < d; j += kThreads) dst[j] = 0.f;
+    return;
+  }
+  const T* src = table + (int64_t)tok * d;
+  for (int j = threadIdx.x; j < d; j += kThreads) dst[j] = to_f(src[j]);
+}
+
+// out[i, :] = T(h[src, :] / sqrt(mean(h[src]^2) + eps) * gain), src = idx ? idx[i] : i
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+rmsnorm_kernel(const float* __restrict__ h, int n_src, const int32_t* __restrict__ idx, int d,
+               const T* __restrict__ gain, float eps, T* __restrict__ out) {
+  const int i = blockIdx.x;
+  int src = idx ? idx[i] : i;
+  if (src < 0 || src >= n_src) src = 0;  // invalid index: normalise row 0 (no out-of-range read)
+  const float* x = h + (int64_t)src * d;
+  float ss = 0.f;
+  for (int j = threadIdx.x * 4; j < d; j += kThreads * 4) {
+    float4 v = *reinterpret_cast<const float4*>(x + j);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  __shared__ float red[kThreads / 64];
+  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
+  const float rs = 1.0f / sqrtf(tot / (float)d + eps);
+  T* y = out + (int64_t)i * d;
+  for (int j = threadIdx.x * 4; j < d; j += kThreads * 4) {
+    float4 v = *reinterpret_cast<const float4*>(x + j);
+    y[j + 0] = from_f<T>(v.x * rs * to_f(gain[j + 0]));
+    y[j + 1] = from_f<T>(v.y * rs * to_f(gain[j + 1]));
+    y[j + 2] = from_f<T>(v.z * rs * to_f(gain[j + 2]));
+    y[j + 3] = from_f<T>(v.w * rs * to_f(gain[j + 3]));
+  }
+}
+
+// cache[idx[i], :] = rows[i, :] for K and V; 16-byte copies.
+__global__ void __launch_bounds__(kThreads)
+scatter_kernel(uint4* __restrict__ kc, uint4* __restrict__ vc, int64_t L, int vecs_per_row,
+               const uint4* __restrict__ kr, const uint4* __restrict__ vr,
+               const int32_t* __restrict__ idx) {
+  const int i = blockIdx.x;
+  const int p = idx[i];
+  if (p < 0 || p >= L) return;
+  const int64_t so = (int64_t)i * vecs_per_row, dof = (int64_t)p * vecs_per_row;
+  for (int j = threadIdx.x; j < vecs_per_row; j += kThreads) {
+    kc[dof + j] = kr[so + j];
+    vc[dof + j] = vr[so + j];
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+scatter_scalar_kernel(T* __restrict__ kc, T* __restrict__ vc, int64_t L, int width,
+                      const T* __restrict__ kr, const T* __restrict__ vr,
+                      const int32_t* __restrict__ idx) {
+  const int i = blockIdx.x;
+  const int p = idx[i];
+  if (p < 0 || p >= L) return;
+  for (int j = threadIdx.x; j < width; j += kThreads) {
+    kc[(int64_t)p * width + j] = kr[(int64_t)i * width + j];
+    vc[(int64_t)p * width + j] = vr[(int64_t)i * width + j];
+  }
+}
+
+// cos/sin(pos * base^(-2i/D)) in fp64, stored fp32; one thread per (pos, i).
+__global__ void rope_table_kernel(float* c, float* sn, int max_pos, int half, int D, double base) {
+  const int64_t n = (int64_t)max_pos * half;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int p = (int)(t / half), i = (int)(t % half);
+    const double theta = (double)p * pow(base, -2.0 * (double)i / (double)D);
+    c[t] = (float)cos(theta);
+    sn[t] = (float)sin(theta);
+  }
+}
+
+}  // namespace
+
+ec_status embed(ec_dtype dt, const void* table, int vocab, const int32_t* tokens, int L,
+                const int32_t* rows, int n, int d, float* h, hipStream_t s) {
+  if (n == 0) return EC_OK;
+  if (dt == EC_BF16)
+    embed_kernel<bf16><<<n, kThreads, 0, s>>>((const bf16*)table, vocab, tokens, L, rows, d, h);
+  else
+    embed_kernel<float><<<n, kThreads, 0, s>>>((const float*)table, vocab, tokens, L, rows, d, h);
+  EC_CHECK_LAUNCH("embed_kernel");
+  return EC_OK;
+}
+
+ec_status rmsnorm(ec_dtype dt, const float* h, int n_src, const int32_t* idx, int n, int d,
+                  const void* gain, float eps, void* out, hipStream_t s) {
+  if (n == 0) return EC_OK;
+  EC_REQUIRE(d % 4 == 0, EC_ERR_UNSUPPORTED, "rmsnorm: d_model %d not a multiple of 4", d);
+  if (dt == EC_BF16)
+    rmsnorm_kernel<bf16><<<n, kThreads, 0, s>>>(h, n_src, idx, d, (const bf16*)gain, eps, (bf16*)out);
+  else
+    rmsnorm_kernel<float><<<n, kThreads, 0, s>>>(h, n_src, idx, d, (const float*)gain, eps, (float*)out);
+  EC_CHECK_LAUNCH("rmsnorm_kernel");
+  return EC_OK;
+}
+
+ec_status scatter(ec_dtype dt, void* kc, void* vc, int64_t L, int width, const void* kr,
+                  const void* vr, const int32_t* idx, int n, hipStream_t s) {
+  if (n == 0) return EC_OK;
+  const size_t esz = dt == EC_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)width * esz;
+  const bool vec = row_bytes % 16 == 0 && (uintptr_t)kc % 16 == 0 && (uintptr_t)vc % 16 == 0 &&
+                   (uintptr_t)kr % 16 == 0 && (uintptr_t)vr % 16 == 0;
+  if (vec) {
+    scatter_kernel<<<n, kThreads, 0, s>>>((uint4*)kc, (uint4*)vc, L, (int)(row_bytes / 16),
+                                          (const uint4*)kr, (const uint4*)vr, idx);
+  } else if (dt == EC_BF16) {
+    scatter_scalar_kernel<bf16><<<n, kThreads, 0, s>>>((bf16*)kc, (bf16*)vc, L, width,
+                                                       (const bf16*)kr, (const bf16*)vr, idx);
+  } else {
+    scatter_scalar_kernel<float><<<n, kThreads, 0, s>>>((float*)kc, (float*)vc, L, width,
+                                                        (const float*)kr, (const float*)vr, idx);
+  }
+  EC_CHECK_LAUNCH("scatter_kernel");
+  return EC_OK;
+}
+
+ec_status rope_table(float* c, float* sn, int max_pos, int head_dim, double base, hipStream_t s) {
+  const int half = head_dim / 2;
+  const int64_t n = (int64_t)max_pos * half;
+  if (n == 0) return EC_OK;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  rope_table_kernel<<<blocks, 256, 0, s>>>(c, sn, max_pos, half, head_dim, base);
+  EC_CHECK_LAUNCH("rope_table_kernel");
+  return EC_OK;
+}
+
+}  // namespace ec

@@ -1,0 +1,144 @@
+"""GPU parity: whole denoising trajectories through ec_step against the oracle loop.
+
+Per step (EntropyCache explainer, Arabic technical summary section 2): the
+path taken (refresh or skip), the recompute-set size, the decoded positions
+and ids, E_{t+1} and the next step's flag. Decoded ids and positions must be
+identical wherever the oracle's top-1/top-2 logit margin of the decoded rows
+exceeds 1e-2 and the confidence gap at the selection cut exceeds 1e-2 (in
+log space); the first step that fails that gate ends the comparison (the two
+trajectories may legitimately part there). E within 1e-3 nats.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import loop as ol
+from oracle import model as om
+
+pytestmark = pytest.mark.gpu
+
+PEAKED_SCALE, PEAKED_TAU = 24.0, 2.15
+
+
+def _decoder(dm, cfg, tau):
+    from entropy_guided_kv_amd import api
+    dec = api.Decoder(dm, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len,
+                      cfg.k_recent, tau)
+    return dec
+
+
+def _gate_ok(rec, n):
+    where = {int(p): i for i, p in enumerate(rec.cand)}
+    idx = [where[int(p)] for p in rec.picked]
+    if any(rec.margin[i] <= 1e-2 for i in idx):
+        return False
+    c = np.sort(np.log(rec.maxprob))[::-1]
+    if len(c) > n and abs(c[n - 1] - c[n]) <= 1e-2:
+        return False
+    return True
+
+
+def _compare_run(cfg, w, tau, max_steps=None, e_tol=1e-3, expect_full_compare=True):
+    from entropy_guided_kv_amd import api
+    dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+    dec = _decoder(dm, cfg, tau)
+    prompt = synth.make_prompt(cfg)
+    dec.reset(torch.from_numpy(prompt))
+    outs = dec.run(max_steps=max_steps)
+    recs, st, _ = ol.run_entropycache(om.OracleModel(w), cfg, prompt, tau, max_steps=max_steps)
+    assert len(outs) == len(recs)
+    compared = 0
+    for o, r in zip(outs, recs):
+        assert o.refreshed == r.refreshed, f"step {r.t}: path differs"
+        assert o.rows == len(r.rows), f"step {r.t}: |R| {o.rows} vs {len(r.rows)}"
+        assert o.n_cand == len(r.cand)
+        gate = _gate_ok(r, cfg.tokens_per_step)
+        same = o.positions == [int(p) for p in r.picked] and o.ids == [int(i) for i in r.ids]
+        if not same:
+            assert not gate, f"step {r.t}: decoded {o.positions}/{o.ids} vs {list(r.picked)}/{list(r.ids)}"
+            print(f"trajectories part at step {r.t} (near tie, gated)")
+            break
+        assert abs(o.emax - r.emax) <= e_tol, f"step {r.t}: E {o.emax} vs {r.emax}"
+        if abs(float(np.float32(r.emax)) - tau) > e_tol:
+            assert o.refresh_next == r.refresh_next
+        compared += 1
+    if expect_full_compare:
+        assert compared == len(recs)
+    return outs, recs
+
+
+def test_tiny_trajectory_as_configured():
+    cfg = synth.CONFIGS["tiny"]
+    outs, recs = _compare_run(cfg, synth.make_model(cfg.model), cfg.tau)
+    assert len(outs) == cfg.steps and all(o.refreshed for o in outs)
+
+
+def test_tiny_trajectory_peaked_mixed_branches():
+    cfg = synth.CONFIGS["tiny"]
+    w = synth.make_model(cfg.model, lm_head_scale=PEAKED_SCALE)
+    outs, recs = _compare_run(cfg, w, PEAKED_TAU)
+    flags = [o.refreshed for o in outs]
+    assert any(flags[1:]) and not all(flags[1:])
+
+
+def test_tiny_tau_plus_inf_all_skips():
+    cfg = synth.CONFIGS["tiny"]
+    outs, recs = _compare_run(cfg, synth.make_model(cfg.model), math.inf)
+    assert [o.refreshed for o in outs] == [True] + [False] * (cfg.steps - 1)
+
+
+def test_tiny_multi_token_steps_and_ring_cut():
+    cfg = synth.DecodeConfig("t3", synth.TINY, 96, 32, 3, 8, 5, (math.inf,))
+    _compare_run(cfg, synth.make_model(cfg.model), math.inf)
+
+
+def test_tau_minus_inf_equals_vanilla_on_gpu():
+    """tau = -inf refreshes every step; it must match a run that forces a refresh each step."""
+    from entropy_guided_kv_amd import api
+    cfg = synth.CONFIGS["tiny"]
+    w = synth.make_model(cfg.model, lm_head_scale=PEAKED_SCALE)
+    dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+    prompt = torch.from_numpy(synth.make_prompt(cfg))
+    a = _decoder(dm, cfg, -math.inf)
+    a.reset(prompt)
+    oa = a.run()
+    b = _decoder(dm, cfg, math.inf)
+    b.reset(prompt)
+    ob = []
+    while not b.done:
+        b.state.refresh_next = 1
+        ob.append(b.step())
+    assert [(o.positions, o.ids, o.emax) for o in oa] == [(o.positions, o.ids, o.emax) for o in ob]
+    assert torch.equal(a.tokens, b.tokens)
+
+
+def test_small_bf16_first_steps():
+    """bf16 small config (8 layers, d=2048, V=32000, L=512, 2 tokens/step): first steps, tau as configured."""
+    cfg = synth.CONFIGS["small"]
+    _compare_run(cfg, synth.make_model(cfg.model), cfg.tau, max_steps=3, expect_full_compare=False)
+
+
+def test_small_bf16_skip_steps():
+    cfg = synth.CONFIGS["small"]
+    _compare_run(cfg, synth.make_model(cfg.model), math.inf, max_steps=6, expect_full_compare=False)
+
+
+def test_determinism_two_runs_bit_identical():
+    from entropy_guided_kv_amd import api
+    cfg = synth.CONFIGS["tiny"]
+    w = synth.make_model(cfg.model, lm_head_scale=PEAKED_SCALE)
+    dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+    prompt = torch.from_numpy(synth.make_prompt(cfg))
+    res = []
+    for _ in range(2):
+        d = _decoder(dm, cfg, PEAKED_TAU)
+        d.reset(prompt)
+        o = d.run()
+        res.append(([(x.positions, x.ids, x.emax, x.refreshed) for x in o], d.tokens.cpu(),
+                    [k.cpu() for k in d.cache.k]))
+    assert res[0][0] == res[1][0]
+    assert torch.equal(res[0][1], res[1][1])
+    assert all(torch.equal(a, b) for a, b in zip(res[0][2], res[1][2]))
