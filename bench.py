@@ -1,0 +1,376 @@
+#!/usr/bin/env python3
+"""EntropyCache denoising-step benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: the 8B-shaped bf16 model (32 layers, d=4096, 32x128 heads, SwiGLU
+12288, V=126464, RoPE) decoding L = 1024 = 768 prompt + 256 masked positions
+in blocks of 32, one token per step, k = 16, tau = 1.0 (the middle of the
+{0.25, 0.5, 1, 2} sweep). Weights are seeded N(0, 0.02) and prompts uniform
+random ids (synthetic stand-ins for trained weights and benchmark prompts).
+
+A step is one call of ec_step: forward (refresh or skip), entropy/argmax/
+confidence reduction, decode/decide/plan, and the one host readback of E.
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "denoising steps/s and gen tokens/s at L=1024,k=16 (1 GPU); % HBM/MFMA peak"
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ algorithmic work per step
+def step_work(m, L: int, r: int, n_cand: int):
+    """(flops, bytes) the method must do for one step that recomputes r rows.
+
+    flops: every projection over the r rows, attention of r queries over L keys,
+    the LM head over the candidate rows. bytes: every weight once, the K/V cache
+    read once (L rows) and the r recomputed rows written, the candidate logits
+    written and read by the reduction.
+    """
+    d, F, V, nl = m.d_model, m.ffn_dim, m.vocab, m.n_layers
+    per_layer_w = 4 * d * d + 3 * d * F
+    flops = nl * (2 * r * per_layer_w + 4 * r * L * d) + 2 * n_cand * V * d
+    bytes_ = 2 * (nl * per_layer_w + V * d) + nl * (2 * L * d * 2 + 2 * r * d * 2) + 2 * 2 * n_cand * V
+    return float(flops), float(bytes_)
+
+
+def t_roof(flops: float, bytes_: float) -> float:
+    return max(flops / MFMA_BF16_PEAK, bytes_ / HBM_PEAK)
+
+
+# ------------------------------------------------------------------ model upload
+def upload_model(cfg, keep_layers: int, device="cuda"):
+    """Generate seeded weights layer by layer on the host and upload them.
+
+    Returns (DeviceModel, host copy of embed / the first keep_layers layers / lm_head).
+    """
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    import synth
+    from entropy_guided_kv_amd import api
+
+    m = cfg.model
+    threads = min(16, len(os.sched_getaffinity(0)))
+    to_dev = lambda a: api._to_device(a, m.dtype, device)
+    host = {"layers": []}
+    t0 = time.time()
+    with ThreadPoolExecutor(threads) as pool:
+        emb = synth.make_embed(m, cfg.seed, pool)
+        head = synth.make_lm_head(m, cfg.seed, pool)
+        d_emb, d_head = to_dev(emb), to_dev(head)
+        host["embed"], host["lm_head"] = emb, head
+        layers = []
+        for i in range(m.n_layers):
+            lw = synth.make_layer(m, i, cfg.seed, pool)
+            layers.append({k: to_dev(v) for k, v in lw.items()})
+            if i < keep_layers:
+                host["layers"].append(lw)
+            if i % 8 == 7:
+                log(f"[bench] weights: {i + 1}/{m.n_layers} layers on device ({time.time() - t0:.1f}s)")
+    fn = synth.make_final_norm(m)
+    host["final_norm"] = fn
+    dm = api.DeviceModel(m, d_emb, layers, to_dev(fn), d_head, rope_max_pos=cfg.seq_len, device=device)
+    torch.cuda.synchronize()
+    return dm, host
+
+
+# ------------------------------------------------------------------ GPU runs
+def run_trajectory(dec, prompt, steps=None):
+    """Run one trajectory from reset; returns (outs, wall seconds, event ms)."""
+    import torch
+    dec.reset(prompt)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    outs = dec.run(max_steps=steps)
+    ev1.record()
+    torch.cuda.synchronize()
+    return outs, time.perf_counter() - t0, ev0.elapsed_time(ev1)
+
+
+def timed_steps(dec, prompt, K):
+    """Exactly K ec_step calls (restarting the trajectory when it completes)."""
+    import torch
+    dec.reset(prompt)
+    outs = []
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(K):
+        if dec.done:
+            dec.reset(prompt)
+        outs.append(dec.step())
+    ev1.record()
+    torch.cuda.synchronize()
+    return outs, time.perf_counter() - t0, ev0.elapsed_time(ev1)
+
+
+def kernel_breakdown(dec, prompt, n_refresh=4, n_skip=8):
+    """Per-kernel-group event timing for refresh steps and for skip steps."""
+    import math as _m
+    from entropy_guided_kv_amd import api
+    res = {}
+    tau0 = dec.params.tau
+    for label, tau, n in (("refresh", -_m.inf, n_refresh), ("skip", _m.inf, n_skip + 1)):
+        dec.set_tau(tau)
+        dec.reset(prompt)
+        if label == "skip":
+            dec.step()                  # the first step always refreshes
+        api.ec_timing_read(reset=True)
+        api.ec_timing_enable(True)
+        outs = [dec.step() for _ in range(n if label == "refresh" else n - 1)]
+        api.ec_timing_enable(False)
+        t = api.ec_timing_read(reset=True)
+        res[label] = {"steps": len(outs), "rows_mean": sum(o.rows for o in outs) / len(outs),
+                      "kernels": t}
+    dec.set_tau(tau0)
+    return res
+
+
+def _entropy_kernel_bench(iters=50):
+    """ec_entropy_max on 64 x 126464 bf16 logits: warm (one buffer) and cold (40 rotating buffers)."""
+    import torch
+    import synth
+    from entropy_guided_kv_amd import api
+    bits, _ = synth.make_entropy_logits()
+    import numpy as np
+    base = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    rows, V = base.shape
+    nbuf = 40  # 40 x 16.2 MB = 647 MB > 256 MB Infinity Cache
+    bufs = [base] + [base.roll(i * 7919, dims=1).contiguous() for i in range(1, nbuf)]
+    ws = torch.empty(api.load().ec_entropy_max_workspace_size(rows, V), dtype=torch.uint8, device="cuda")
+    for b in bufs[:4]:
+        api.ec_entropy_max(b, workspace=ws)
+    torch.cuda.synchronize()
+    out = {}
+    for mode in ("warm", "cold"):
+        api.ec_timing_read(reset=True)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(iters):
+            api.ec_entropy_max(bufs[0] if mode == "warm" else bufs[i % nbuf], workspace=ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / iters
+        out[mode] = {"us_per_call": ms * 1e3, "bytes": rows * V * 2,
+                     "GBps_call": rows * V * 2 / (ms * 1e-3) / 1e9}
+    return out
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+def cpu_baseline(cfg, host, prompt, n_layers_sample: int):
+    """Time the oracle's refresh step on the host cores with a bounded sample.
+
+    The sample: one refresh step (all L rows) of the model cut to its first
+    n_layers_sample layers, and the same step with no layers (embedding, final
+    norm, LM head over the candidates, entropy, selection). The per-step time
+    of the full model is estimated as T0 + (T1 - T0) * n_layers / n_sample.
+    """
+    import numpy as np
+    import synth
+    from oracle import loop as ol
+    from oracle import model as om
+
+    def run(nl):
+        w = synth.ModelWeights(cfg.model, host["embed"], host["layers"][:nl], host["final_norm"],
+                               host["lm_head"])
+        mdl = om.OracleModel(w, keep_f64=False)
+        st = ol.init_state(cfg, prompt)
+        cache = om.new_cache(mdl, cfg.seq_len)
+        t0 = time.perf_counter()
+        ol.step(mdl, cfg, st, cache, cfg.tau)
+        return time.perf_counter() - t0
+
+    t0 = run(0)
+    t1 = run(n_layers_sample)
+    per_step = t0 + (t1 - t0) * cfg.model.n_layers / n_layers_sample
+    threads = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 0) for i in info), default=None)
+    except Exception:
+        pass
+    cores = threads or len(os.sched_getaffinity(0))
+    return {
+        "value": 1.0 / per_step, "unit": "steps/s", "cores": cores, "kind": "oracle",
+        "sample": (f"one refresh step (L={cfg.seq_len}) with {n_layers_sample} of "
+                   f"{cfg.model.n_layers} layers ({t1:.1f}s) and with 0 layers ({t0:.1f}s); "
+                   f"per-step time scaled linearly in layers to {per_step:.1f}s; float64 numpy"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256, help="timed denoising steps")
+    ap.add_argument("--warmup", type=int, default=16, help="untimed steps before timing")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the tau sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-layers", type=int, default=2, help="layers in the CPU oracle sample")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the EntropyCache step of one sequence runs on one "
+              "MI355X with no sharding (see the design notes for how it would shard); run with "
+              "--gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    from entropy_guided_kv_amd import api
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    api.load()
+    cfg = synth.CONFIGS["8b"]
+    m = cfg.model
+    tau = 1.0
+    prompt_np = synth.make_prompt(cfg)
+    prompt = torch.from_numpy(prompt_np)
+    keep = 0 if args.no_cpu else args.cpu_layers
+    dm, host = upload_model(cfg, keep)
+    dec = api.Decoder(dm, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len,
+                      cfg.k_recent, tau)
+    log(f"[bench] model on device; workspace {dec.workspace.numel() / 2**20:.0f} MiB")
+
+    # warmup
+    dec.reset(prompt)
+    for _ in range(args.warmup):
+        if dec.done:
+            dec.reset(prompt)
+        dec.step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    # headline: exactly K steps of the configured trajectory
+    outs, wall, ev_ms = timed_steps(dec, prompt, args.steps)
+    steps_s = args.steps / wall
+    tokens = sum(len(o.positions) for o in outs)
+    refresh_rate = sum(o.refreshed for o in outs) / len(outs)
+    roof_s = 0.0
+    for o in outs:
+        f, b = step_work(m, cfg.seq_len, o.rows, o.n_cand)
+        roof_s += t_roof(f, b)
+    log(f"[bench] timed {args.steps} steps: {steps_s:.2f} steps/s, refresh rate {refresh_rate:.3f}, "
+        f"events {ev_ms:.1f} ms vs wall {wall * 1e3:.1f} ms")
+
+    # tau sweep (whole trajectories) + tau = +inf (one refresh, then skip steps)
+    sweep = {}
+    if not args.no_sweep:
+        for tv in (0.25, 0.5, 1.0, 2.0, math.inf):
+            dec.set_tau(tv)
+            o2, w2, _ = run_trajectory(dec, prompt)
+            f_roof = sum(t_roof(*step_work(m, cfg.seq_len, o.rows, o.n_cand)) for o in o2)
+            sweep[str(tv)] = {
+                "steps": len(o2), "steps_per_s": len(o2) / w2,
+                "gen_tokens_per_s": sum(len(o.positions) for o in o2) / w2,
+                "refresh_rate": sum(o.refreshed for o in o2) / len(o2),
+                "mean_rows": sum(o.rows for o in o2) / len(o2),
+                "roofline_frac": f_roof / w2,
+                "emax_mean": float(np.mean([o.emax for o in o2])),
+            }
+            log(f"[bench] tau={tv}: {sweep[str(tv)]['steps_per_s']:.2f} steps/s, "
+                f"refresh {sweep[str(tv)]['refresh_rate']:.3f}")
+        dec.set_tau(tau)
+
+    # per-kernel event timing (refresh steps and skip steps)
+    kb = kernel_breakdown(dec, prompt)
+    ref = kb["refresh"]["kernels"]
+    dom = max(ref, key=lambda k: ref[k]["ms"])
+    dk = ref[dom]
+    avg_ms = dk["ms"] / max(dk["launches"], 1)
+    flops_launch = dk["flops"] / max(dk["launches"], 1)
+    bytes_launch = dk["bytes"] / max(dk["launches"], 1)
+    if flops_launch > 0:
+        achieved = flops_launch / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_BF16_PEAK / 1e12,
+                    "unit": "TFLOP/s", "frac": achieved / (MFMA_BF16_PEAK / 1e12), "traffic": None,
+                    "avg_launch_us": avg_ms * 1e3, "flops_per_launch": flops_launch,
+                    "bytes_per_launch": bytes_launch}
+    else:
+        achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK / 1e9,
+                    "unit": "GB/s", "frac": achieved / (HBM_PEAK / 1e9), "traffic": None,
+                    "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": bytes_launch}
+    log(f"[bench] dominant kernel {dom}: {avg_ms * 1e3:.1f} us/launch, {roofline['frac']:.3f} of peak")
+    kernels = {}
+    for label, v in kb.items():
+        tot = sum(x["ms"] for x in v["kernels"].values())
+        kernels[label] = {
+            "rows_mean": v["rows_mean"],
+            "ms_per_step": tot / v["steps"],
+            "groups": {k: {"ms_per_step": x["ms"] / v["steps"],
+                           "TFLOPs": (x["flops"] / (x["ms"] * 1e-3) / 1e12) if x["ms"] > 0 else 0.0,
+                           "GBps": (x["bytes"] / (x["ms"] * 1e-3) / 1e9) if x["ms"] > 0 else 0.0}
+                       for k, x in v["kernels"].items() if x["launches"]},
+        }
+        dec_ms = v["kernels"]["entropy"]["ms"] + v["kernels"]["select"]["ms"]
+        kernels[label]["decision_overhead_frac"] = dec_ms / tot if tot > 0 else None
+
+    ent = _entropy_kernel_bench()
+    log(f"[bench] entropy kernel 64x126464: warm {ent['warm']['us_per_call']:.1f} us, "
+        f"cold {ent['cold']['us_per_call']:.1f} us")
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline ...")
+        cpu = cpu_baseline(cfg, host, prompt_np, args.cpu_layers)
+        log(f"[bench] CPU oracle: {cpu['value']:.4f} steps/s on {cpu['cores']} threads")
+
+    res = {
+        "metric": METRIC,
+        "value": steps_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, uniform random prompt ids)",
+        "config": {"workload": "EntropyCache decode, 8B-shaped bf16 model (32 layers, d=4096, 32x128 "
+                               "heads, SwiGLU 12288, V=126464), L=1024 = 768 prompt + 256 masked, "
+                               "blocks of 32, 1 token/step, k=16, tau=1.0",
+                   "seq_len": cfg.seq_len, "k_recent": cfg.k_recent, "tau": tau, "global_batch": 1},
+        "gen_tokens_per_s": tokens / wall,
+        "refresh_rate": refresh_rate,
+        "step_roofline_frac": roof_s / wall,
+        "event_ms_timed_region": ev_ms,
+        "tau_sweep": sweep,
+        "roofline": roofline,
+        "kernels": kernels,
+        "entropy_kernel_64x126464": ent,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,7 +8,8 @@ from ._lib import ECError, load  # noqa: F401
 
 __all__ = [
     "ECError", "load", "ec_entropy_max", "ec_cache_scatter", "ec_partial_attn", "ec_rope_table",
-    "ec_forward", "DeviceModel", "KVCache", "Decoder", "StepOut",
+    "ec_forward", "DeviceModel", "KVCache", "Decoder", "StepOut", "ec_timing_enable",
+    "ec_timing_read",
 ]
 
 

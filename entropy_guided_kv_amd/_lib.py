@@ -20,8 +20,13 @@ EXPORTS = (
     "ec_entropy_max_workspace_size", "ec_entropy_max", "ec_cache_scatter",
     "ec_partial_attn_workspace_size", "ec_partial_attn", "ec_rope_table",
     "ec_forward_workspace_size", "ec_forward", "ec_state_plan_words", "ec_state_reset",
-    "ec_step_workspace_size", "ec_step", "ec_last_error", "ec_version",
+    "ec_step_workspace_size", "ec_step", "ec_timing_enable", "ec_timing_read", "ec_last_error",
+    "ec_version",
 )
+
+EC_T_KINDS = 10
+TIMING_KINDS = ("embed", "norm", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "entropy",
+                "select")
 
 
 class ec_layer_weights(C.Structure):
@@ -69,6 +74,12 @@ class ec_step_out(C.Structure):
                 ("maxprob", C.c_float * EC_MAX_TOKENS_PER_STEP)]
 
 
+class ec_timing(C.Structure):
+    _fields_ = [("struct_size", C.c_uint32), ("n_kinds", C.c_int32),
+                ("ms", C.c_double * EC_T_KINDS), ("launches", C.c_int64 * EC_T_KINDS),
+                ("flops", C.c_double * EC_T_KINDS), ("bytes", C.c_double * EC_T_KINDS)]
+
+
 _lib = None
 
 
@@ -103,6 +114,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ec_step_workspace_size": (sz, [C.POINTER(ec_model_desc), C.POINTER(ec_params)]),
         "ec_step": (C.c_int, [C.POINTER(ec_model_desc), C.POINTER(ec_cache_desc), C.POINTER(ec_state),
                               C.POINTER(ec_params), vp, sz, vp, C.POINTER(ec_step_out)]),
+        "ec_timing_enable": (C.c_int, [C.c_int]),
+        "ec_timing_read": (C.c_int, [C.POINTER(ec_timing), C.c_int]),
         "ec_last_error": (C.c_char_p, []),
         "ec_version": (C.c_int, []),
     }

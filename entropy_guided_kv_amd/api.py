@@ -294,3 +294,18 @@ class Decoder:
         while not self.done and (max_steps is None or len(outs) < max_steps):
             outs.append(self.step(stream))
         return outs
+
+
+# ---------------------------------------------------------------------- measurement aid
+def ec_timing_enable(on: bool) -> None:
+    check(load().ec_timing_enable(1 if on else 0), "ec_timing_enable")
+
+
+def ec_timing_read(reset: bool = True) -> dict:
+    """Per kernel group: summed event ms, launches, algorithmic flops and bytes."""
+    t = _lib.ec_timing()
+    t.struct_size = C.sizeof(_lib.ec_timing)
+    check(load().ec_timing_read(C.byref(t), 1 if reset else 0), "ec_timing_read")
+    return {name: {"ms": t.ms[i], "launches": int(t.launches[i]), "flops": t.flops[i],
+                   "bytes": t.bytes[i]}
+            for i, name in enumerate(_lib.TIMING_KINDS)}

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 namespace ec {
 
@@ -26,6 +27,59 @@ ec_status hip_fail(hipError_t e, const char* what) {
 }
 
 namespace {
+
+// ---------------------------------------------------------------- timing aid
+struct TimingState {
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // pairs: 2*i start, 2*i+1 stop
+  struct Rec {
+    int kind, slot;
+    double flops, bytes;
+  };
+  std::vector<Rec> pending;
+  int used = 0;
+  double ms[EC_T_KINDS] = {}, flops[EC_T_KINDS] = {}, bytes[EC_T_KINDS] = {};
+  int64_t launches[EC_T_KINDS] = {};
+};
+TimingState g_tm;
+
+struct TScope {
+  int kind, slot = -1;
+  hipStream_t s;
+  double fl, by;
+  TScope(int k, hipStream_t st, double f, double b) : kind(k), s(st), fl(f), by(b) {
+    if (!g_tm.on) return;
+    if ((int)g_tm.ev.size() < 2 * (g_tm.used + 1)) {
+      hipEvent_t a, z;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&z) != hipSuccess) return;
+      g_tm.ev.push_back(a);
+      g_tm.ev.push_back(z);
+    }
+    slot = g_tm.used++;
+    hipEventRecord(g_tm.ev[2 * slot], s);
+  }
+  ~TScope() {
+    if (slot < 0) return;
+    hipEventRecord(g_tm.ev[2 * slot + 1], s);
+    g_tm.pending.push_back({kind, slot, fl, by});
+  }
+};
+
+void timing_collect() {
+  for (const auto& r : g_tm.pending) {
+    float ms = 0.f;
+    hipEventSynchronize(g_tm.ev[2 * r.slot + 1]);
+    if (hipEventElapsedTime(&ms, g_tm.ev[2 * r.slot], g_tm.ev[2 * r.slot + 1]) == hipSuccess) {
+      g_tm.ms[r.kind] += ms;
+      g_tm.launches[r.kind] += 1;
+      g_tm.flops[r.kind] += r.flops;
+      g_tm.bytes[r.kind] += r.bytes;
+    }
+  }
+  g_tm.pending.clear();
+  g_tm.used = 0;
+}
 
 size_t esize(ec_dtype dt) { return dt == EC_BF16 ? 2 : 4; }
 bool dtype_ok(ec_dtype dt) { return dt == EC_F32 || dt == EC_BF16; }
@@ -136,11 +190,19 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
     st = (x);                \
     if (st != EC_OK) return st; \
   } while (0)
+  const double es = (double)esize(dt);
+  const double M = n_rows, Lq = L, dd = d, FF = F, VV = V, NO = n_out;
   if (n_rows > 0) {
-    EC_TRY(embed(dt, m->embed, V, tokens, L, rows, n_rows, d, w.h, s));
+    {
+      TScope t(EC_T_EMBED, s, 0.0, M * dd * (es + 4));
+      EC_TRY(embed(dt, m->embed, V, tokens, L, rows, n_rows, d, w.h, s));
+    }
     for (int l = 0; l < m->n_layers; ++l) {
       const ec_layer_weights& lw = m->layers[l];
-      EC_TRY(rmsnorm(dt, w.h, n_rows, nullptr, n_rows, d, lw.attn_norm, m->rms_eps, w.a, s));
+      {
+        TScope t(EC_T_NORM, s, 0.0, M * dd * (4 + es));
+        EC_TRY(rmsnorm(dt, w.h, n_rows, nullptr, n_rows, d, lw.attn_norm, m->rms_eps, w.a, s));
+      }
       EpiArgs e{};
       e.kind = EPI_QKV;
       e.out = w.q;
@@ -153,26 +215,45 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
       e.d_model = d;
       e.head_dim = Dh;
       e.seq_len = L;
-      EC_TRY(gemm(dt, w.a, lw.wqkv, nullptr, n_rows, 3 * d, d, e, w.splitk, w.splitk_bytes, s));
-      EC_TRY(attn(dt, w.q, c->k[l], c->v[l], n_rows, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
+      {
+        TScope t(EC_T_QKV, s, 2 * M * 3 * dd * dd, (3 * dd * dd + M * dd + 3 * M * dd) * es);
+        EC_TRY(gemm(dt, w.a, lw.wqkv, nullptr, n_rows, 3 * d, d, e, w.splitk, w.splitk_bytes, s));
+      }
+      {
+        TScope t(EC_T_ATTN, s, 4 * M * Lq * dd, (2 * Lq * dd + 2 * M * dd) * es);
+        EC_TRY(attn(dt, w.q, c->k[l], c->v[l], n_rows, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
+      }
       EpiArgs r{};
       r.kind = EPI_RESID;
       r.resid = w.h;
       r.ldo = d;
-      EC_TRY(gemm(dt, w.o, lw.wo, nullptr, n_rows, d, d, r, w.splitk, w.splitk_bytes, s));
-      EC_TRY(rmsnorm(dt, w.h, n_rows, nullptr, n_rows, d, lw.mlp_norm, m->rms_eps, w.a, s));
+      {
+        TScope t(EC_T_OPROJ, s, 2 * M * dd * dd, (dd * dd + M * dd) * es + 8 * M * dd);
+        EC_TRY(gemm(dt, w.o, lw.wo, nullptr, n_rows, d, d, r, w.splitk, w.splitk_bytes, s));
+      }
+      {
+        TScope t(EC_T_NORM, s, 0.0, M * dd * (4 + es));
+        EC_TRY(rmsnorm(dt, w.h, n_rows, nullptr, n_rows, d, lw.mlp_norm, m->rms_eps, w.a, s));
+      }
       EpiArgs g{};
       g.kind = EPI_SWIGLU;
       g.out = w.s;
       g.ldo = F;
-      EC_TRY(gemm(dt, w.a, lw.w_gate, lw.w_up, n_rows, F, d, g, w.splitk, w.splitk_bytes, s));
-      EC_TRY(gemm(dt, w.s, lw.w_down, nullptr, n_rows, d, F, r, w.splitk, w.splitk_bytes, s));
+      {
+        TScope t(EC_T_GATEUP, s, 4 * M * FF * dd, (2 * FF * dd + M * dd + M * FF) * es);
+        EC_TRY(gemm(dt, w.a, lw.w_gate, lw.w_up, n_rows, F, d, g, w.splitk, w.splitk_bytes, s));
+      }
+      {
+        TScope t(EC_T_DOWN, s, 2 * M * dd * FF, (dd * FF + M * FF) * es + 8 * M * dd);
+        EC_TRY(gemm(dt, w.s, lw.w_down, nullptr, n_rows, d, F, r, w.splitk, w.splitk_bytes, s));
+      }
     }
   }
   if (hidden && n_rows > 0)
     EC_CHECK_HIP(hipMemcpyAsync(hidden, w.h, (size_t)n_rows * d * sizeof(float),
                                 hipMemcpyDeviceToDevice, s));
   if (n_out > 0) {
+    TScope t(EC_T_LMHEAD, s, 2 * NO * VV * dd, (VV * dd + NO * dd + NO * VV) * es + NO * dd * 4);
     EC_TRY(rmsnorm(dt, w.h, n_rows, out_idx, n_out, d, m->final_norm, m->rms_eps, w.xn, s));
     EpiArgs o{};
     o.kind = EPI_STORE;
@@ -237,6 +318,32 @@ using namespace ec;
 extern "C" {
 
 const char* ec_last_error(void) { return g_err; }
+
+ec_status ec_timing_enable(int on) {
+  if (!on) timing_collect();
+  g_tm.on = on != 0;
+  return EC_OK;
+}
+
+ec_status ec_timing_read(ec_timing* out, int reset) {
+  EC_REQUIRE(out && out->struct_size >= sizeof(ec_timing), EC_ERR_ARG, "ec_timing_read: bad out");
+  timing_collect();
+  const uint32_t sz = out->struct_size;
+  memset(out, 0, sizeof(ec_timing));
+  out->struct_size = sz;
+  out->n_kinds = EC_T_KINDS;
+  for (int k = 0; k < EC_T_KINDS; ++k) {
+    out->ms[k] = g_tm.ms[k];
+    out->launches[k] = g_tm.launches[k];
+    out->flops[k] = g_tm.flops[k];
+    out->bytes[k] = g_tm.bytes[k];
+    if (reset) {
+      g_tm.ms[k] = g_tm.flops[k] = g_tm.bytes[k] = 0;
+      g_tm.launches[k] = 0;
+    }
+  }
+  return EC_OK;
+}
 int ec_version(void) { return EC_VERSION; }
 
 size_t ec_entropy_max_workspace_size(int32_t rows, int32_t vocab) {
@@ -395,15 +502,22 @@ ec_status ec_step(const ec_model_desc* model, const ec_cache_desc* cache, ec_sta
   st = run_forward(model, cache, state->tokens, rows, n_rows, cidx, n_cand, w.logits, nullptr,
                    w.fwd, s);
   if (st != EC_OK) return st;
-  st = entropy(model->dtype, w.logits, n_cand, model->vocab, model->vocab, nullptr, 0, w.H, w.amax,
-               w.conf, nullptr, w.ent_ws, w.ent_bytes, s);
+  {
+    TScope t(EC_T_ENTROPY, s, 0.0, (double)n_cand * model->vocab * esize(model->dtype));
+    st = entropy(model->dtype, w.logits, n_cand, model->vocab, model->vocab, nullptr, 0, w.H,
+                 w.amax, w.conf, nullptr, w.ent_ws, w.ent_bytes, s);
+  }
   if (st != EC_OK) return st;
-  st = select_decode(w.H, w.amax, w.conf, n_cand, state->tokens, state->masked, state->plan,
-                     *params, res, s);
+  {
+    TScope t(EC_T_SELECT, s, 0.0, 0.0);
+    st = select_decode(w.H, w.amax, w.conf, n_cand, state->tokens, state->masked, state->plan,
+                       *params, res, s);
+  }
   if (st != EC_OK) return st;
   StepResult h;
   EC_CHECK_HIP(hipMemcpyAsync(&h, res, sizeof(StepResult), hipMemcpyDeviceToHost, s));
   EC_CHECK_HIP(hipStreamSynchronize(s));
+  if (g_tm.on) timing_collect();
 
   const bool nan = h.has_nan != 0;
   const bool refresh = nan || (h.emax > params->tau);

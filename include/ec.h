@@ -268,6 +268,32 @@ ec_status ec_step(const ec_model_desc* model, const ec_cache_desc* cache, ec_sta
                   const ec_params* params, void* workspace, size_t workspace_bytes,
                   void* stream, ec_step_out* out);
 
+/* ------------------------------------------------------------------------
+ * Measurement aid: per-kernel-group timing with HIP events.
+ *
+ * While enabled, ec_forward and ec_step bracket each kernel group with a pair
+ * of hipEvents recorded on the caller's stream and accumulate, per group, the
+ * elapsed time, the number of launches and the algorithmic work of those
+ * launches (flops of the contraction, bytes the method must move). Process-
+ * wide state, for one thread at a time; it costs two event records per
+ * group, so keep it off for headline timings. ec_timing_read synchronizes
+ * the recorded events, fills `out` and optionally clears the totals.
+ * ---------------------------------------------------------------------- */
+enum {
+  EC_T_EMBED = 0, EC_T_NORM, EC_T_QKV, EC_T_ATTN, EC_T_OPROJ, EC_T_GATEUP, EC_T_DOWN,
+  EC_T_LMHEAD, EC_T_ENTROPY, EC_T_SELECT, EC_T_KINDS
+};
+typedef struct ec_timing {
+  uint32_t struct_size;
+  int32_t n_kinds;
+  double ms[EC_T_KINDS];        /* summed event time per group */
+  int64_t launches[EC_T_KINDS]; /* number of timed launches per group */
+  double flops[EC_T_KINDS];     /* algorithmic flops (2*M*N*K for a GEMM) */
+  double bytes[EC_T_KINDS];     /* algorithmic bytes (weights + activations read / written) */
+} ec_timing;
+ec_status ec_timing_enable(int on);
+ec_status ec_timing_read(ec_timing* out, int reset);
+
 /* Message of the calling thread's last failed call ("" if none). */
 const char* ec_last_error(void);
 int ec_version(void);
