@@ -115,7 +115,6 @@ __device__ void build_plan(const uint8_t* masked, int32_t* plan, int L, int P, i
   int32_t* C = plan + lay.C0;
   for (int p = max(lo, clo); p < min(hi, chi); ++p)
     if (masked[p]) C[coff++] = p;
-  __threadfence();
   __syncthreads();
   // index of each candidate in R (R ascending): lower bound
   int32_t* I = plan + lay.I0;
@@ -150,7 +149,6 @@ reset_kernel(int32_t* tokens, uint8_t* masked, int32_t* plan, int L, int P, int 
   }
   if (threadIdx.x == 0) plan[0] = 0;
   for (int e = threadIdx.x; e < lay.K; e += kThreads) plan[8 + e] = -1;
-  __threadfence();
   __syncthreads();
   build_plan(masked, plan, L, P, B, k, res);
   if (threadIdx.x == 0) {
@@ -202,7 +200,6 @@ select_kernel(const float* __restrict__ H, const int32_t* __restrict__ amax,
     nan_sh[threadIdx.x] = h != h;
     emax_sh[threadIdx.x] = h;
   }
-  __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
     float e = -INFINITY;
@@ -216,7 +213,6 @@ select_kernel(const float* __restrict__ H, const int32_t* __restrict__ amax,
     res->emax = nan ? NAN : e;
     plan[0] = count0 + npick;
   }
-  __threadfence();
   __syncthreads();
   build_plan(masked, plan, L, P, B, k, res);
 }

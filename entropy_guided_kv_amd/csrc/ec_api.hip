@@ -137,6 +137,10 @@ struct FwdWs {
 size_t splitk_max(const ec_model_desc* m, int max_rows, int max_out) {
   if (m->dtype != EC_BF16) return 0;
   const int d = m->d_model, F = m->ffn_dim, V = m->vocab;
+  // memo of the last query (the bound is recomputed only when a shape changes)
+  static thread_local int key[5] = {-1, -1, -1, -1, -1};
+  static thread_local size_t memo = 0;
+  if (key[0] == d && key[1] == F && key[2] == V && key[3] == max_rows && key[4] == max_out) return memo;
   size_t best = 0;
   for (int M = 1; M <= max_rows; ++M) {
     best = std::max(best, gemm_splitk_ws_bytes(M, 3 * d, d, EPI_QKV, true));
@@ -145,13 +149,20 @@ size_t splitk_max(const ec_model_desc* m, int max_rows, int max_out) {
     best = std::max(best, gemm_splitk_ws_bytes(M, d, F, EPI_RESID, true));
   }
   for (int M = 1; M <= max_out; ++M) best = std::max(best, gemm_splitk_ws_bytes(M, V, d, EPI_STORE, true));
+  key[0] = d; key[1] = F; key[2] = V; key[3] = max_rows; key[4] = max_out;
+  memo = best;
   return best;
 }
 
 size_t attn_max(const ec_model_desc* m, int max_rows, int L) {
+  static thread_local int key[4] = {-1, -1, -1, -1};
+  static thread_local size_t memo = 0;
+  if (key[0] == m->n_heads && key[1] == m->head_dim && key[2] == max_rows && key[3] == L) return memo;
   size_t best = 0;
   for (int r = 1; r <= max_rows; ++r)
     best = std::max(best, attn_ws_bytes(r, L, m->n_heads, m->head_dim));
+  key[0] = m->n_heads; key[1] = m->head_dim; key[2] = max_rows; key[3] = L;
+  memo = best;
   return best;
 }
 

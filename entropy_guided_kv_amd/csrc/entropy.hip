@@ -5,20 +5,22 @@
 // and does not depend on sequence length or depth (EntropyCache explainer,
 // Arabic technical summary, section 2, "Decode and evaluate entropy").
 //
-// Single pass over the logits with an online (running-max) form: with m the
-// running max, Z = sum exp(x - m) and S = sum (x - m) exp(x - m), the entropy
-// is ln Z - S/Z, the confidence max_j p_j = 1/Z and the argmax the first
-// index holding m. Two states merge exactly:
+// With m the row max, Z = sum exp(x - m) and S = sum (x - m) exp(x - m), the
+// entropy is ln Z - S/Z, the confidence max_j p_j = 1/Z and the argmax the
+// first index holding m. Partial states over disjoint slices merge exactly:
 //   m = max(ma, mb); Z = Za e^(ma-m) + Zb e^(mb-m);
 //   S = (Sa + (ma-m) Za) e^(ma-m) + (Sb + (mb-m) Zb) e^(mb-m).
-// One exponential per element; each 16-byte vector first updates the max once.
 //
-// Layout: grid (splits, rows); each workgroup streams one contiguous slice of
-// one row with coalesced 16-byte loads (consecutive lanes, consecutive
-// vectors), reduces (m, Z, S, idx) across the wavefront with shuffles and
-// across waves through LDS, and writes one partial state. A second small
-// kernel merges the splits of every row in split order (deterministic) and
-// takes the max entropy over the selected rows.
+// Kernel 1 (grid: slices x rows, 256 threads): each workgroup owns one slice
+// of one row and reads it exactly once from HBM with 16-byte loads, all issued
+// up front (U vectors per thread held in registers; consecutive lanes read
+// consecutive vectors). The slice max and first argmax come from a wavefront
+// shuffle + LDS reduction; then every element is exponentiated once against
+// the slice max (exp2 of (x - max) * log2 e) and Z, S are summed the same
+// way. No per-element rescaling and no data reread.
+// Kernel 2 (grid: rows, one wavefront each): merges the slices of a row in a
+// fixed order (deterministic) and writes entropy / argmax / confidence.
+// Kernel 3 (one workgroup, only when E is requested): max over selected rows.
 #include "ec_internal.h"
 
 #include <math.h>
@@ -28,193 +30,225 @@ namespace ec {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kU = 4;  // 16-byte vectors per thread per slice
 constexpr float kNegInf = -INFINITY;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct Part {
-  float m, z, s;
+  float m, z, s;  // s in natural units: sum (x - m) e^(x - m)
   int idx;
   int nan;
+  int pad[3];
 };
 
-__device__ __forceinline__ void merge(Part& a, const Part& b) {
-  a.nan |= b.nan;
-  float m = fmaxf(a.m, b.m);
-  if (m == kNegInf) {  // both empty (all -inf so far); keep the lower index
-    a.idx = min(a.idx, b.idx);
-    return;
-  }
-  float za = 0.f, sa = 0.f, zb = 0.f, sb = 0.f;
-  if (a.m != kNegInf) {
-    float d = a.m - m, f = __expf(d);
-    za = a.z * f;
-    sa = (a.s + d * a.z) * f;
-  }
-  if (b.m != kNegInf) {
-    float d = b.m - m, f = __expf(d);
-    zb = b.z * f;
-    sb = (b.s + d * b.z) * f;
-  }
-  int idx;
-  if (a.m == b.m) idx = min(a.idx, b.idx);
-  else idx = (a.m > b.m) ? a.idx : b.idx;
-  a.m = m;
-  a.z = za + zb;
-  a.s = sa + sb;
-  a.idx = idx;
-}
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-// Add n values (n <= 8) at global indices j0..j0+n-1, in increasing order.
-__device__ __forceinline__ void absorb(Part& p, const float* x, int n, int j0) {
-  float cm = kNegInf;
-  int ci = 0x7fffffff;
+template <typename T> struct Vec;
+template <> struct Vec<bf16> {
+  static constexpr int E = 8;
+  __device__ static void unpack(const v4u& u, float* x) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    if (k < n) {
-      float v = x[k];
-      p.nan |= (v != v);
-      if (v > cm) { cm = v; ci = j0 + k; }
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(u[k] << 16);
+      x[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
     }
   }
-  if (cm > p.m) {
-    if (p.m != kNegInf) {
-      float d = p.m - cm, f = __expf(d);
-      p.s = (p.s + d * p.z) * f;
-      p.z = p.z * f;
-    }
-    p.m = cm;
-    p.idx = ci;
-  } else if (cm == p.m && ci < p.idx) {
-    p.idx = ci;
-  }
-  if (p.m == kNegInf) return;
+};
+template <> struct Vec<float> {
+  static constexpr int E = 4;
+  __device__ static void unpack(const v4u& u, float* x) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    if (k < n) {
-      float t = x[k] - p.m;
-      float e = __expf(t);
-      p.z += e;
-      p.s += (e > 0.f) ? t * e : 0.f;
-    }
+    for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(u[k]);
+  }
+};
+
+// (value, index) max with the lower index on ties
+__device__ __forceinline__ void vmax(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
   }
 }
 
-__device__ __forceinline__ void load8(const bf16* base, int64_t j, float* x) {
-  uint4 u = *reinterpret_cast<const uint4*>(base + j);
-  uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    x[2 * k] = __uint_as_float(w[k] << 16);
-    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void load8(const float* base, int64_t j, float* x) {
-  float4 a = *reinterpret_cast<const float4*>(base + j);
-  float4 b = *reinterpret_cast<const float4*>(base + j + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-
-__device__ __forceinline__ Part shfl_part(const Part& p, int mask) {
-  Part o;
-  o.m = __shfl_xor(p.m, mask);
-  o.z = __shfl_xor(p.z, mask);
-  o.s = __shfl_xor(p.s, mask);
-  o.idx = __shfl_xor(p.idx, mask);
-  o.nan = __shfl_xor(p.nan, mask);
-  return o;
-}
-
-// grid: (splits, rows). Slice of row r: [split * chunk, min(V, (split+1) * chunk)).
 template <typename T, bool VEC>
 __global__ void __launch_bounds__(kThreads)
-entropy_partial_kernel(const T* __restrict__ logits, int V, int64_t stride, int chunk,
-                       Part* __restrict__ parts) {
+entropy_slice_kernel(const T* __restrict__ logits, int V, int64_t stride, int chunk,
+                     Part* __restrict__ parts) {
+  constexpr int E = Vec<T>::E;
+  constexpr int NV = kU * E;  // values per thread
   const int split = blockIdx.x, row = blockIdx.y, splits = gridDim.x;
   const T* base = logits + (int64_t)row * stride;
   const int lo = split * chunk;
   const int hi = min(V, lo + chunk);
-  Part p{kNegInf, 0.f, 0.f, 0x7fffffff, 0};
-  float x[8];
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+
+  float x[NV];
+  int j0[kU];
   if (VEC) {
-    // chunk is a multiple of 8, so [lo, hi8) is made of whole 8-element vectors
-    const int hi8 = lo + ((hi - lo) & ~7);
-    int j = lo + threadIdx.x * 8;
-    for (; j + 3 * kThreads * 8 < hi8; j += 4 * kThreads * 8) {
-      float y[3][8];
-      load8(base, j, x);
-      load8(base, j + kThreads * 8, y[0]);
-      load8(base, j + 2 * kThreads * 8, y[1]);
-      load8(base, j + 3 * kThreads * 8, y[2]);
-      absorb(p, x, 8, j);
-      absorb(p, y[0], 8, j + kThreads * 8);
-      absorb(p, y[1], 8, j + 2 * kThreads * 8);
-      absorb(p, y[2], 8, j + 3 * kThreads * 8);
+    const int hiv = lo + ((hi - lo) / E) * E;  // end of the whole vectors
+    v4u u[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      j0[k] = lo + (tid + k * kThreads) * E;
+      if (j0[k] < hiv) u[k] = *reinterpret_cast<const v4u*>(base + j0[k]);
     }
-    for (; j < hi8; j += kThreads * 8) {
-      load8(base, j, x);
-      absorb(p, x, 8, j);
-    }
-    // ragged tail (< 8 elements), only in the last slice of a row
-    if (threadIdx.x == 0 && hi8 < hi) {
-      int n = hi - hi8;
-      for (int k = 0; k < n; ++k) x[k] = to_f(base[hi8 + k]);
-      absorb(p, x, n, hi8);
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      if (j0[k] < hiv) {
+        Vec<T>::unpack(u[k], x + k * E);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int j = j0[k] + e;
+          x[k * E + e] = (j >= hiv && j < hi) ? to_f(base[j]) : kNegInf;  // ragged row end
+        }
+      }
     }
   } else {
-    for (int j = lo + threadIdx.x; j < hi; j += kThreads) {
-      x[0] = to_f(base[j]);
-      absorb(p, x, 1, j);
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      j0[k] = lo + (tid + k * kThreads) * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int j = j0[k] + e;
+        x[k * E + e] = j < hi ? to_f(base[j]) : kNegInf;
+      }
     }
   }
-  // wavefront reduction (64 lanes)
+
+  // ---- slice max and first argmax
+  float mv = kNegInf;
+  int mi = 0x7fffffff;
+  int nan = 0;
 #pragma unroll
-  for (int mask = 32; mask >= 1; mask >>= 1) {
-    Part o = shfl_part(p, mask);
-    merge(p, o);
+  for (int k = 0; k < kU; ++k)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float v = x[k * E + e];
+      nan |= (v != v);
+      if (v > mv) {  // strict: first index within the thread (indices increase with k, e)
+        mv = v;
+        mi = j0[k] + e;
+      }
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v2 = __shfl_xor(mv, o);
+    const int i2 = __shfl_xor(mi, o);
+    vmax(mv, mi, v2, i2);
+    nan |= __shfl_xor(nan, o);
   }
-  __shared__ Part wp[kThreads / 64];
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  if (lane == 0) wp[wave] = p;
+  __shared__ float sm[kThreads / 64];
+  __shared__ int si[kThreads / 64], sn[kThreads / 64];
+  __shared__ float sz[kThreads / 64], ss[kThreads / 64];
+  if (lane == 0) {
+    sm[wave] = mv;
+    si[wave] = mi;
+    sn[wave] = nan;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    Part a = wp[0];
-    for (int w = 1; w < kThreads / 64; ++w) merge(a, wp[w]);
-    parts[(int64_t)row * splits + split] = a;
+  mv = sm[0];
+  mi = si[0];
+  nan = sn[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) {
+    vmax(mv, mi, sm[w], si[w]);
+    nan |= sn[w];
+  }
+
+  // ---- Z and S against the slice max (log2 domain, one exp2 per element)
+  float z = 0.f, s2 = 0.f;
+  if (mv != kNegInf) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const float t = (x[q] - mv) * kLog2e;  // exactly 0 at the max
+      const float e = exp2f(t);
+      z += e;
+      s2 += e > 0.f ? t * e : 0.f;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    z += __shfl_xor(z, o);
+    s2 += __shfl_xor(s2, o);
+  }
+  if (lane == 0) {
+    sz[wave] = z;
+    ss[wave] = s2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float zt = 0.f, st = 0.f;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      zt += sz[w];
+      st += ss[w];
+    }
+    Part p;
+    p.m = mv;
+    p.z = zt;
+    p.s = st * kLn2;
+    p.idx = mi;
+    p.nan = nan;
+    parts[(int64_t)row * splits + split] = p;
   }
 }
 
-// One workgroup: merges the splits of every row (in split order), writes
-// entropy / argmax / confidence, then the max entropy over the selected rows.
-__global__ void __launch_bounds__(kThreads)
-entropy_merge_kernel(const Part* __restrict__ parts, int rows, int splits,
-                     const int32_t* __restrict__ sel, int n_sel, float* __restrict__ H,
-                     int32_t* __restrict__ amax, float* __restrict__ conf,
-                     float* __restrict__ emax) {
-  for (int r = threadIdx.x; r < rows; r += kThreads) {
-    Part a = parts[(int64_t)r * splits];
-    for (int s = 1; s < splits; ++s) merge(a, parts[(int64_t)r * splits + s]);
-    float h, c;
-    if (a.nan || a.m == kNegInf) {
-      h = NAN;
-      c = NAN;
-    } else {
-      h = __logf(a.z) - a.s / a.z;
-      c = 1.0f / a.z;
-    }
-    H[r] = h;
-    conf[r] = c;
-    amax[r] = a.idx == 0x7fffffff ? 0 : a.idx;
+// One wavefront per row: merge the row's slices (lane l takes slices l, l+64, ...).
+__global__ void __launch_bounds__(64)
+entropy_merge_kernel(const Part* __restrict__ parts, int splits, float* __restrict__ H,
+                     int32_t* __restrict__ amax, float* __restrict__ conf) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const Part* pr = parts + (int64_t)row * splits;
+  float mv = kNegInf;
+  int mi = 0x7fffffff, nan = 0;
+  for (int s = lane; s < splits; s += 64) {
+    vmax(mv, mi, pr[s].m, pr[s].idx);
+    nan |= pr[s].nan;
   }
-  if (emax == nullptr) return;
-  __syncthreads();
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v2 = __shfl_xor(mv, o);
+    const int i2 = __shfl_xor(mi, o);
+    vmax(mv, mi, v2, i2);
+    nan |= __shfl_xor(nan, o);
+  }
+  float z = 0.f, s = 0.f;
+  if (mv != kNegInf) {
+    for (int q = lane; q < splits; q += 64) {
+      const Part p = pr[q];
+      if (p.m == kNegInf) continue;
+      const float d = p.m - mv, f = __expf(d);
+      z += p.z * f;
+      s += (p.s + d * p.z) * f;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    z += __shfl_xor(z, o);
+    s += __shfl_xor(s, o);
+  }
+  if (lane == 0) {
+    const bool bad = nan || mv == kNegInf;
+    H[row] = bad ? NAN : __logf(z) - s / z;
+    conf[row] = bad ? NAN : 1.0f / z;
+    amax[row] = mi == 0x7fffffff ? 0 : mi;
+  }
+}
+
+// E = max entropy over the selected rows (NaN if any selected row is NaN).
+__global__ void __launch_bounds__(kThreads)
+entropy_emax_kernel(const float* __restrict__ H, int rows, const int32_t* __restrict__ sel,
+                    int n_sel, float* __restrict__ emax) {
   __shared__ float red[kThreads];
   __shared__ int rnan[kThreads];
   float m = kNegInf;
   int nan = 0;
   const int n = sel ? n_sel : rows;
   for (int i = threadIdx.x; i < n; i += kThreads) {
-    int r = sel ? sel[i] : i;
-    float h = (r >= 0 && r < rows) ? H[r] : NAN;
+    const int r = sel ? sel[i] : i;
+    const float h = (r >= 0 && r < rows) ? H[r] : NAN;
     if (h != h) nan = 1;
     else m = fmaxf(m, h);
   }
@@ -233,23 +267,14 @@ entropy_merge_kernel(const Part* __restrict__ parts, int rows, int splits,
 
 __global__ void fill_kernel(float* p, float v) { *p = v; }
 
-void choose_split(int rows, int V, int& splits, int& chunk) {
-  splits = (V + 8191) / 8192;
-  if (rows * splits < 1024) splits = (1024 + rows - 1) / rows;
-  int max_splits = (V + 2047) / 2048;
-  if (splits > max_splits) splits = max_splits;
-  if (splits > 128) splits = 128;
-  if (splits < 1) splits = 1;
-  chunk = ((V + splits - 1) / splits + 7) & ~7;
-  splits = (V + chunk - 1) / chunk;
-}
+// slice length: kU vectors per thread -> 8192 bf16 / 4096 f32 elements per workgroup
+int slice_len(ec_dtype dt) { return kThreads * kU * (dt == EC_BF16 ? 8 : 4); }
 
 }  // namespace
 
 size_t entropy_ws_bytes(int rows, int vocab) {
   if (rows <= 0 || vocab <= 0) return 0;
-  int splits, chunk;
-  choose_split(rows, vocab, splits, chunk);
+  const int splits = (vocab + slice_len(EC_F32) - 1) / slice_len(EC_F32);  // the larger count
   return (size_t)rows * splits * sizeof(Part) + 256;
 }
 
@@ -263,26 +288,30 @@ ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t 
     }
     return EC_OK;
   }
-  int splits, chunk;
-  choose_split(rows, vocab, splits, chunk);
+  const int chunk = slice_len(dt);
+  const int splits = (vocab + chunk - 1) / chunk;
   Part* parts = (Part*)ws;
   const size_t esz = dt == EC_BF16 ? 2 : 4;
   const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * esz) % 16 == 0);
   dim3 grid(splits, rows);
   if (dt == EC_BF16) {
     if (vec)
-      entropy_partial_kernel<bf16, true><<<grid, kThreads, 0, s>>>((const bf16*)logits, vocab, stride, chunk, parts);
+      entropy_slice_kernel<bf16, true><<<grid, kThreads, 0, s>>>((const bf16*)logits, vocab, stride, chunk, parts);
     else
-      entropy_partial_kernel<bf16, false><<<grid, kThreads, 0, s>>>((const bf16*)logits, vocab, stride, chunk, parts);
+      entropy_slice_kernel<bf16, false><<<grid, kThreads, 0, s>>>((const bf16*)logits, vocab, stride, chunk, parts);
   } else {
     if (vec)
-      entropy_partial_kernel<float, true><<<grid, kThreads, 0, s>>>((const float*)logits, vocab, stride, chunk, parts);
+      entropy_slice_kernel<float, true><<<grid, kThreads, 0, s>>>((const float*)logits, vocab, stride, chunk, parts);
     else
-      entropy_partial_kernel<float, false><<<grid, kThreads, 0, s>>>((const float*)logits, vocab, stride, chunk, parts);
+      entropy_slice_kernel<float, false><<<grid, kThreads, 0, s>>>((const float*)logits, vocab, stride, chunk, parts);
   }
-  EC_CHECK_LAUNCH("entropy_partial_kernel");
-  entropy_merge_kernel<<<1, kThreads, 0, s>>>(parts, rows, splits, sel, n_sel, H, amax, c, emax);
+  EC_CHECK_LAUNCH("entropy_slice_kernel");
+  entropy_merge_kernel<<<rows, 64, 0, s>>>(parts, splits, H, amax, c);
   EC_CHECK_LAUNCH("entropy_merge_kernel");
+  if (emax) {
+    entropy_emax_kernel<<<1, kThreads, 0, s>>>(H, rows, sel, n_sel, emax);
+    EC_CHECK_LAUNCH("entropy_emax_kernel");
+  }
   return EC_OK;
 }
 

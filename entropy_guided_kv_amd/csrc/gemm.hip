@@ -39,6 +39,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int BK = 64;
+// native 16-byte vector (a plain vector load/store, unlike the uint4 struct)
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (144 bytes)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -90,25 +92,35 @@ __device__ __forceinline__ int xcd_remap(int pid, int nblk) {
 }
 
 // -------------------------------------------------------------------- bf16 MFMA GEMM
-// BM x BN workgroup tile, WM x WN per wavefront (4 wavefronts).
+// BM x BN workgroup tile, WM x WN per wavefront, (BM/WM)*(BN/WN) wavefronts,
+// K staged BKT at a time through two LDS buffers; STAGES register sets hold
+// the next K-steps' tiles in flight (prefetch depth).
 // DUAL: B rows [0, BN/2) come from B (gate), rows [BN/2, BN) from B2 (up);
 //       the workgroup writes BN/2 output columns.
 // SPLIT: write raw fp32 partials to `part` ([S][M][ncols]) instead of the epilogue.
-template <int BM, int BN, int WM, int WN, int EPI, bool DUAL, bool SPLIT>
-__global__ void __launch_bounds__(kThreads)
+template <int BM, int BN, int WM, int WN, int BKT, int STAGES, int EPI, bool DUAL, bool SPLIT>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
                  const bf16* __restrict__ B2, int M, int N, int K, int k_chunk, int splits,
                  EpiArgs epi, float* __restrict__ part) {
   constexpr int WAVES_N = BN / WN;
+  constexpr int NT = (BM / WM) * (BN / WN) * 64;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_VECS = BM * BK / 8 / kThreads;  // 16-byte vectors per thread
-  constexpr int B_VECS = BN * BK / 8 / kThreads;
-  static_assert((BM / WM) * (BN / WN) == 4, "4 wavefronts");
-  static_assert(A_VECS >= 1 && B_VECS >= 1, "tile too small");
+  constexpr int LS = BKT + 8;                    // LDS row stride (bf16), 16-byte pad
+  constexpr int CPR = BKT / 8;                   // 16-byte chunks per row
+  constexpr int A_VECS = BM * CPR / NT;          // 16-byte vectors per thread
+  constexpr int B_VECS = BN * CPR / NT;
+  // paired epilogues: a wavefront's first TN/2 column tiles pair with its last TN/2
+  // (rotary halves c / c+64 of one head, or gate / up of the same output columns)
+  constexpr bool PAIRED = DUAL || EPI == EPI_QKV;
+  static_assert(EPI != EPI_QKV || BN == 128, "QKV tiles are one head (128 columns) wide");
+  static_assert(!PAIRED || TN % 2 == 0, "paired epilogue needs an even number of column tiles");
+  static_assert(A_VECS >= 1 && B_VECS >= 1 && A_VECS * NT == BM * CPR && B_VECS * NT == BN * CPR,
+                "tile / thread mismatch");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16* sA = (bf16*)smem;                        // [2][BM][LDS_STRIDE]
-  bf16* sB = sA + 2 * BM * LDS_STRIDE;           // [2][BN][LDS_STRIDE]
+  bf16* sA = (bf16*)smem;                        // [2][BM][LS]
+  bf16* sB = sA + 2 * BM * LS;                   // [2][BN][LS]
 
   const int MT = (M + BM - 1) / BM;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -120,31 +132,27 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
   const int NOUT = DUAL ? BN / 2 : BN;           // output columns per workgroup
   const int n0 = nt * NOUT;                      // first output column (B row for non-dual)
   const int kbeg = kz * k_chunk;
-  const int nk = k_chunk / BK;
+  const int nk = k_chunk / BKT;
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-  // global source pointers for this thread's vectors
   const bf16* a_src[A_VECS];
-  bool a_ok[A_VECS];
   int a_lds[A_VECS];
 #pragma unroll
   for (int i = 0; i < A_VECS; ++i) {
-    const int v = tid + i * kThreads;
-    const int r = v / (BK / 8), kv = v % (BK / 8);
-    a_ok[i] = (m0 + r) < M;
-    a_src[i] = A + (int64_t)(a_ok[i] ? m0 + r : 0) * K + kbeg + kv * 8;
-    a_lds[i] = r * LDS_STRIDE + kv * 8;
+    const int v = tid + i * NT;
+    const int r = v / CPR, kv = v % CPR;
+    a_src[i] = A + (int64_t)min(m0 + r, M - 1) * K + kbeg + kv * 8;
+    a_lds[i] = r * LS + kv * 8;
   }
   const bf16* b_src[B_VECS];
-  bool b_ok[B_VECS];
   int b_lds[B_VECS];
 #pragma unroll
   for (int i = 0; i < B_VECS; ++i) {
-    const int v = tid + i * kThreads;
-    const int r = v / (BK / 8), kv = v % (BK / 8);
+    const int v = tid + i * NT;
+    const int r = v / CPR, kv = v % CPR;
     int grow;
     const bf16* mat = B;
     if (DUAL) {
@@ -154,34 +162,35 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
     } else {
       grow = n0 + r;
     }
-    b_ok[i] = grow < N;
-    b_src[i] = mat + (int64_t)(b_ok[i] ? grow : 0) * K + kbeg + kv * 8;
-    b_lds[i] = r * LDS_STRIDE + kv * 8;
+    b_src[i] = mat + (int64_t)min(grow, N - 1) * K + kbeg + kv * 8;
+    b_lds[i] = r * LS + kv * 8;
   }
 
-  uint4 ra[A_VECS], rb[B_VECS];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_VECS; ++i)
-      ra[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < B_VECS; ++i)
-      rb[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(b_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
-  };
-  auto sstore = [&](int buf) {
-    bf16* a = sA + buf * BM * LDS_STRIDE;
-    bf16* b = sB + buf * BN * LDS_STRIDE;
-#pragma unroll
-    for (int i = 0; i < A_VECS; ++i) *reinterpret_cast<uint4*>(a + a_lds[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_VECS; ++i) *reinterpret_cast<uint4*>(b + b_lds[i]) = rb[i];
-  };
+  // D register sets of prefetched tiles: the global loads of K-step k+D are in
+  // flight while step k computes, so D steps of MFMA work cover the load latency
+  constexpr int D = STAGES;
+  v4u ra[D][A_VECS], rb[D][B_VECS];
+#define EC_GLOAD(KT, XA, XB)                                                          \
+  do {                                                                                \
+    _Pragma("unroll") for (int i_ = 0; i_ < A_VECS; ++i_)                             \
+      XA[i_] = *reinterpret_cast<const v4u*>(a_src[i_] + (KT) * BKT);               \
+    _Pragma("unroll") for (int i_ = 0; i_ < B_VECS; ++i_)                             \
+      XB[i_] = *reinterpret_cast<const v4u*>(b_src[i_] + (KT) * BKT);               \
+  } while (0)
+#define EC_SSTORE(BUF, XA, XB)                                                        \
+  do {                                                                                \
+    bf16* a_ = sA + (BUF) * BM * LS;                                                  \
+    bf16* b_ = sB + (BUF) * BN * LS;                                                  \
+    _Pragma("unroll") for (int i_ = 0; i_ < A_VECS; ++i_)                             \
+      *reinterpret_cast<v4u*>(a_ + a_lds[i_]) = XA[i_];                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < B_VECS; ++i_)                             \
+      *reinterpret_cast<v4u*>(b_ + b_lds[i_]) = XB[i_];                             \
+  } while (0)
 
-  // LDS row of this wavefront's column tile j
   int brow[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    if (DUAL) {
+    if (PAIRED) {
       const int jj = j % (TN / 2);
       brow[j] = (j < TN / 2 ? 0 : BN / 2) + wn * (WN / 2) + 32 * jj;
     } else {
@@ -197,34 +206,49 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
   const int lrow = lane % 32, lk = 8 * (lane / 32);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const bf16* a = sA + cur * BM * LDS_STRIDE;
-    const bf16* b = sB + cur * BN * LDS_STRIDE;
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const bf16* a = sA + buf * BM * LS;
+    const bf16* b = sB + buf * BN * LS;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    for (int kk = 0; kk < BKT / 16; ++kk) {
       bf16x8 fa[TM], fb[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(a + (wm * WM + 32 * i + lrow) * LDS_STRIDE + kk * 16 + lk);
+        fa[i] = *reinterpret_cast<const bf16x8*>(a + (wm * WM + 32 * i + lrow) * LS + kk * 16 + lk);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(b + (brow[j] + lrow) * LDS_STRIDE + kk * 16 + lk);
+        fb[j] = *reinterpret_cast<const bf16x8*>(b + (brow[j] + lrow) * LS + kk * 16 + lk);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+  };
+
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < nk) EC_GLOAD(j, ra[j], rb[j]);
+  EC_SSTORE(0, ra[0], rb[0]);
+  if (D < nk) EC_GLOAD(D, ra[0], rb[0]);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int k = kt + j;
+      if (k < nk) {
+        compute(k & 1);
+        if (k + 1 < nk) {
+          EC_SSTORE((k + 1) & 1, ra[(j + 1) % D], rb[(j + 1) % D]);
+          if (k + 1 + D < nk) EC_GLOAD(k + 1 + D, ra[(j + 1) % D], rb[(j + 1) % D]);
+        }
+        __syncthreads();
+      }
+    }
   }
+#undef EC_GLOAD
+#undef EC_SSTORE
 
   // ---------------------------------------------------------------- epilogue
   // acc[i][j][v]: row = m0 + wm*WM + 32i + 8(v/4) + 4(lane/32) + v%4, column lane%32 of tile j
@@ -241,7 +265,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
           const int jj = j % (TN / 2);
           col = (j < TN / 2 ? 0 : N) + n0 + wn * (WN / 2) + 32 * jj + lrow;
         } else {
-          col = n0 + wn * WN + 32 * j + lrow;
+          col = n0 + brow[j] + lrow;
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -257,14 +281,15 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
     for (int v = 0; v < 16; ++v) {
       const int m = rbase + 32 * i + 8 * (v / 4) + (v % 4);
       if (m >= M) continue;
-      if (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
+      if (PAIRED) {
 #pragma unroll
         for (int j = 0; j < TN / 2; ++j) {
           const float x1 = acc[i][j][v], x2 = acc[i][j + TN / 2][v];
+          const int col = n0 + wn * (WN / 2) + 32 * j + lrow;
           if (EPI == EPI_QKV) {
-            epi_qkv_pair<bf16>(epi, m, n0 + wn * WN + 32 * j + lrow, x1, x2);
+            epi_qkv_pair<bf16>(epi, m, col, x1, x2);
           } else {
-            epi_swiglu<bf16>(epi, m, n0 + wn * (WN / 2) + 32 * j + lrow, x1, x2);
+            epi_swiglu<bf16>(epi, m, col, x1, x2);
           }
         }
       } else {
@@ -368,55 +393,55 @@ gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
 // -------------------------------------------------------------------- host-side planning
 struct Plan {
   int BM, BN, S, k_chunk, MT, NT;
+  bool skinny;  // M <= 64: 64-row tiles
 };
 
 constexpr int kCUs = 256;
 
+// Tile choice, measured on MI355X for the projection shapes of the 2k / 4k models:
+// 128x128 workgroup tiles with 8 or 16 wavefronts (two or four per SIMD hide the LDS
+// and global latency); 64x128 tiles when M <= 64 (LM head over the candidates, skinny
+// skip steps). K is split only when the tiles cannot give every CU one workgroup.
 Plan plan_bf16(int M, int N, int K, int kind) {
   Plan p{};
   const bool dual = kind == EPI_SWIGLU;
-  // tile shape: QKV / SwiGLU need a 128-column wavefront (head / gate-up pairing)
-  if (kind == EPI_QKV || kind == EPI_SWIGLU) {
-    p.BM = 128;
-    p.BN = 256;
-  } else {
-    p.BM = 128;
-    p.BN = 128;
-  }
+  p.skinny = M <= 64 && kind != EPI_QKV && kind != EPI_SWIGLU;
+  p.BM = p.skinny ? 64 : 128;
+  p.BN = 128;
   const int nout = dual ? p.BN / 2 : p.BN;
   p.MT = (M + p.BM - 1) / p.BM;
   p.NT = (N + nout - 1) / nout;
   const int tiles = p.MT * p.NT;
   int S = 1;
   const int nk = K / BK;
-  // split K while the grid is under two workgroups per CU and each split keeps >= 8 k-steps
-  while (tiles * S < 2 * kCUs && S < 8 && nk % (2 * S) == 0 && nk / (2 * S) >= 8) S *= 2;
+  while (tiles * S < kCUs && S < 8 && nk % (2 * S) == 0 && nk / (2 * S) >= 8) S *= 2;
   p.S = S;
   p.k_chunk = K / S;
   return p;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool DUAL>
+template <int BM, int BN, int WM, int WN, int BKT, int STAGES, int EPI, bool DUAL>
 ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, const bf16* B2, int M, int N,
                       int K, const EpiArgs& epi, float* part, hipStream_t s) {
-  const size_t lds = (size_t)2 * (BM + BN) * LDS_STRIDE * sizeof(bf16);
+  constexpr int NT = (BM / WM) * (BN / WN) * 64;
+  const size_t lds = (size_t)2 * (BM + BN) * (BKT + 8) * sizeof(bf16);
   const int grid = p.MT * p.NT * p.S;
   if (p.S > 1) {
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI, DUAL, true>;
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, BKT, STAGES, EPI, DUAL, true>;
     static bool attr = false;
     if (!attr) {
       EC_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
       attr = true;
     }
-    kern<<<grid, kThreads, lds, s>>>(A, B, B2, M, N, K, p.k_chunk, p.S, epi, part);
+    kern<<<grid, NT, lds, s>>>(A, B, B2, M, N, K, p.k_chunk, p.S, epi, part);
   } else {
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI, DUAL, false>;
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, BKT, STAGES, EPI, DUAL, false>;
     static bool attr = false;
     if (!attr) {
       EC_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
       attr = true;
     }
-    kern<<<grid, kThreads, lds, s>>>(A, B, B2, M, N, K, p.k_chunk, p.S, epi, part);
+    kern<<<grid, NT, lds, s>>>(A, B, B2, M, N, K, p.k_chunk, p.S, epi, part);
   }
   EC_CHECK_LAUNCH("gemm_bf16_kernel");
   return EC_OK;
@@ -447,8 +472,8 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
   EC_REQUIRE(K % BK == 0, EC_ERR_UNSUPPORTED, "gemm: K=%d not a multiple of %d", K, BK);
   Plan p = plan_bf16(M, N, K, kind);
   if (kind == EPI_QKV)
-    EC_REQUIRE(epi.head_dim == 128 && N % 256 == 0, EC_ERR_UNSUPPORTED,
-               "gemm: bf16 QKV needs head_dim 128 and 3d %% 256 == 0");
+    EC_REQUIRE(epi.head_dim == 128 && N % 128 == 0, EC_ERR_UNSUPPORTED,
+               "gemm: bf16 QKV needs head_dim 128");
   if (kind == EPI_SWIGLU)
     EC_REQUIRE(N % 128 == 0, EC_ERR_UNSUPPORTED, "gemm: bf16 SwiGLU needs F %% 128 == 0");
   float* part = nullptr;
@@ -464,16 +489,20 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
   ec_status st;
   switch (kind) {
     case EPI_QKV:
-      st = launch_bf16<128, 256, 64, 128, EPI_QKV, false>(p, a, b, b2, M, N, K, epi, part, s);
+      st = launch_bf16<128, 128, 32, 64, 64, 3, EPI_QKV, false>(p, a, b, b2, M, N, K, epi, part, s);
       break;
     case EPI_SWIGLU:
-      st = launch_bf16<128, 256, 64, 128, EPI_SWIGLU, true>(p, a, b, b2, M, N, K, epi, part, s);
+      st = launch_bf16<128, 128, 32, 64, 64, 2, EPI_SWIGLU, true>(p, a, b, b2, M, N, K, epi, part, s);
       break;
     case EPI_RESID:
-      st = launch_bf16<128, 128, 64, 64, EPI_RESID, false>(p, a, b, b2, M, N, K, epi, part, s);
+      st = p.skinny
+               ? launch_bf16<64, 128, 32, 32, 64, 3, EPI_RESID, false>(p, a, b, b2, M, N, K, epi, part, s)
+               : launch_bf16<128, 128, 32, 32, 64, 2, EPI_RESID, false>(p, a, b, b2, M, N, K, epi, part, s);
       break;
     default:
-      st = launch_bf16<128, 128, 64, 64, EPI_STORE, false>(p, a, b, b2, M, N, K, epi, part, s);
+      st = p.skinny
+               ? launch_bf16<64, 128, 32, 32, 64, 3, EPI_STORE, false>(p, a, b, b2, M, N, K, epi, part, s)
+               : launch_bf16<128, 128, 32, 64, 64, 3, EPI_STORE, false>(p, a, b, b2, M, N, K, epi, part, s);
       break;
   }
   if (st != EC_OK) return st;

@@ -50,9 +50,10 @@ def candidates(masked: np.ndarray, prompt_len: int, block_len: int) -> np.ndarra
 def select(cand: np.ndarray, conf32: np.ndarray, n: int) -> np.ndarray:
     """The min(n, len(cand)) candidates with the largest confidence, ties to the lower position.
 
-    Returned in ascending position order.
+    A NaN confidence ranks below every number. Returned in ascending position order.
     """
-    order = sorted(range(len(cand)), key=lambda i: (-float(conf32[i]), int(cand[i])))
+    key = lambda i: (-(float(conf32[i]) if conf32[i] == conf32[i] else -1.0), int(cand[i]))
+    order = sorted(range(len(cand)), key=key)
     pick = [int(cand[i]) for i in order[: min(n, len(cand))]]
     return np.array(sorted(pick), dtype=np.int64)
 
@@ -73,6 +74,7 @@ class StepRecord:
     argmax: np.ndarray
     maxprob: np.ndarray
     margin: np.ndarray        # top-1 minus top-2 logit of each candidate row
+    top1: np.ndarray          # top-1 logit of each candidate row
     picked: np.ndarray        # decoded positions, ascending
     ids: np.ndarray           # decoded token ids, same order
     emax: float               # E_{t+1} (float32 value)
@@ -130,8 +132,8 @@ def step(model: OracleModel, cfg, st: DecodeState, cache, tau: float,
     else:
         emax = float(np.float32(hp.max()))
     st.refresh_next = bool(math.isnan(emax) or np.float32(emax) > np.float32(tau))
-    rec = StepRecord(st.t, full, rows, cand, h, a, c, _top2_margin(logits), picked, ids, emax,
-                     st.refresh_next, logits if keep_logits else None)
+    rec = StepRecord(st.t, full, rows, cand, h, a, c, _top2_margin(logits), logits.max(axis=1),
+                     picked, ids, emax, st.refresh_next, logits if keep_logits else None)
     st.t += 1
     return rec
 

@@ -37,3 +37,17 @@ def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
 def f64_to_bf16_tensor(x: np.ndarray, device="cuda") -> torch.Tensor:
     """float64 values that are exactly bf16 (e.g. the oracle's mirrored cache) -> bf16 tensor."""
     return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).to(device)
+
+
+MARGIN_GATE = 1e-2
+
+
+def margin_gate(top1, margin):
+    """Rows whose top-1/top-2 logit margin exceeds 1e-2 of max(1, |top-1|).
+
+    An absolute 1e-2 is below one bf16 step for |logit| >= 2 (the step there is
+    1/64), so the gate is taken relative to the logit's magnitude; for
+    |logit| <= 1 it is the absolute 1e-2.
+    """
+    top1 = np.asarray(top1, dtype=np.float64)
+    return np.asarray(margin) > MARGIN_GATE * np.maximum(1.0, np.abs(top1))

@@ -14,7 +14,7 @@ import torch
 import synth
 from oracle import model as om
 from oracle.entropy import entropy_rows
-from tests.gpu_util import f64_to_bf16_tensor, rel_err, row_rel_err, to_f64
+from tests.gpu_util import f64_to_bf16_tensor, margin_gate, rel_err, row_rel_err, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -63,12 +63,16 @@ def _compare(shape, om_model, dm, cache, ocache, tokens, rows, out_pos):
     ev = max(rel_err(to_f64(cache.v[i]), ocache[i][1]) for i in range(len(ocache)))
     print(f"{shape.name}: rows={len(rows)} hidden {eh:.2e} logits {el:.2e} K {ek:.2e} V {ev:.2e}")
     assert eh <= tol and el <= tol and ek <= tol and ev <= tol
-    # argmax ids: identical wherever the oracle's top-1/top-2 margin exceeds 1e-2
+    # argmax ids: identical wherever the oracle's top-1/top-2 margin clears the gate
     lg = to_f64(logits)
     srt = np.sort(ref["logits"], axis=1)
     margin = srt[:, -1] - srt[:, -2]
-    gate = margin > 1e-2
-    np.testing.assert_array_equal(lg.argmax(1)[gate], ref["logits"].argmax(1)[gate])
+    gate = margin_gate(srt[:, -1], margin) if shape.dtype == "bf16" else margin > 1e-2
+    bad = np.flatnonzero(gate & (lg.argmax(1) != ref["logits"].argmax(1)))
+    for i in bad:
+        print(f"row {i}: device argmax {lg[i].argmax()} oracle {ref['logits'][i].argmax()} "
+              f"margin {margin[i]:.4f} top1 {srt[i, -1]:.4f}")
+    assert bad.size == 0
     # entropy of the device logits through the oracle vs the oracle's own: end-to-end drift only
     return lg, ref
 

@@ -4,9 +4,13 @@ Per step (EntropyCache explainer, Arabic technical summary section 2): the
 path taken (refresh or skip), the recompute-set size, the decoded positions
 and ids, E_{t+1} and the next step's flag. Decoded ids and positions must be
 identical wherever the oracle's top-1/top-2 logit margin of the decoded rows
-exceeds 1e-2 and the confidence gap at the selection cut exceeds 1e-2 (in
-log space); the first step that fails that gate ends the comparison (the two
-trajectories may legitimately part there). E within 1e-3 nats.
+exceeds 1e-2 (of max(1, |top-1|) for bf16 models, whose logits are stored
+with a step of 1/64 at |logit| >= 2) and the confidence gap at the selection
+cut exceeds 1e-2 (in log space); the first step that fails that gate ends the
+comparison (the two trajectories may legitimately part there). E within 1e-3
+nats for fp32 models; for bf16 models E is checked against the oracle's
+entropy of the device's own logits (within 1e-3) by the forward tests, and
+end to end within 2e-2.
 """
 import math
 
@@ -17,6 +21,7 @@ import torch
 import synth
 from oracle import loop as ol
 from oracle import model as om
+from tests.gpu_util import margin_gate
 
 pytestmark = pytest.mark.gpu
 
@@ -30,10 +35,11 @@ def _decoder(dm, cfg, tau):
     return dec
 
 
-def _gate_ok(rec, n):
+def _gate_ok(rec, n, dtype):
     where = {int(p): i for i, p in enumerate(rec.cand)}
     idx = [where[int(p)] for p in rec.picked]
-    if any(rec.margin[i] <= 1e-2 for i in idx):
+    ok = margin_gate(rec.top1, rec.margin) if dtype == "bf16" else rec.margin > 1e-2
+    if not all(ok[i] for i in idx):
         return False
     c = np.sort(np.log(rec.maxprob))[::-1]
     if len(c) > n and abs(c[n - 1] - c[n]) <= 1e-2:
@@ -41,8 +47,10 @@ def _gate_ok(rec, n):
     return True
 
 
-def _compare_run(cfg, w, tau, max_steps=None, e_tol=1e-3, expect_full_compare=True):
+def _compare_run(cfg, w, tau, max_steps=None, e_tol=None, expect_full_compare=True):
     from entropy_guided_kv_amd import api
+    if e_tol is None:
+        e_tol = 1e-3 if cfg.model.dtype == "f32" else 2e-2
     dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
     dec = _decoder(dm, cfg, tau)
     prompt = synth.make_prompt(cfg)
@@ -55,7 +63,7 @@ def _compare_run(cfg, w, tau, max_steps=None, e_tol=1e-3, expect_full_compare=Tr
         assert o.refreshed == r.refreshed, f"step {r.t}: path differs"
         assert o.rows == len(r.rows), f"step {r.t}: |R| {o.rows} vs {len(r.rows)}"
         assert o.n_cand == len(r.cand)
-        gate = _gate_ok(r, cfg.tokens_per_step)
+        gate = _gate_ok(r, cfg.tokens_per_step, cfg.model.dtype)
         same = o.positions == [int(p) for p in r.picked] and o.ids == [int(i) for i in r.ids]
         if not same:
             assert not gate, f"step {r.t}: decoded {o.positions}/{o.ids} vs {list(r.picked)}/{list(r.ids)}"

@@ -148,3 +148,10 @@ def test_decode_log_keeps_order_within_step(tiny):
     # step 2 recomputes the 24 still-masked positions plus the last 6 of the 8 logged ones
     # (the cut falls inside step 0's four picks)
     assert recs[-1].rows.tolist() == sorted(set(range(96, 128)) - set(flat[:8]) | set(flat[2:8]))
+
+
+def test_select_ranks_nan_confidence_last():
+    cand = np.array([3, 5, 9])
+    conf = np.array([np.nan, 0.2, 0.1], dtype=np.float32)
+    np.testing.assert_array_equal(ol.select(cand, conf, 1), [5])
+    np.testing.assert_array_equal(ol.select(cand, conf, 3), [3, 5, 9])
