@@ -132,6 +132,8 @@ def kernel_breakdown(dec, prompt, n_refresh=4, n_skip=8):
     res = {}
     tau0 = dec.params.tau
     for label, tau, n in (("refresh", -_m.inf, n_refresh), ("skip", _m.inf, n_skip + 1)):
+        if n <= 1 and label == "skip":
+            continue
         dec.set_tau(tau)
         dec.reset(prompt)
         if label == "skip":
@@ -230,6 +232,13 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the tau sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=2, help="layers in the CPU oracle sample")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-kernel event timing (and the roofline object)")
+    ap.add_argument("--breakdown", choices=("refresh", "both"), default="both",
+                    help="which step kinds the per-kernel event timing covers")
+    ap.add_argument("--no-entropy", action="store_true", help="skip the 64x126464 entropy kernel run")
+    ap.add_argument("--entropy-only", action="store_true",
+                    help="only the 64x126464 entropy kernel run (no model)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -247,6 +256,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     api.load()
+    if args.entropy_only:
+        ent = _entropy_kernel_bench()
+        print(json.dumps({"entropy_kernel_64x126464": ent}), flush=True)
+        return
     cfg = synth.CONFIGS["8b"]
     m = cfg.model
     tau = 1.0
@@ -299,7 +312,28 @@ def main():
         dec.set_tau(tau)
 
     # per-kernel event timing (refresh steps and skip steps)
-    kb = kernel_breakdown(dec, prompt)
+    roofline, kernels = None, {}
+    if not args.no_breakdown:
+        roofline, kernels = breakdown_report(dec, prompt, args.breakdown == "both")
+
+    ent = None
+    if not args.no_entropy:
+        ent = _entropy_kernel_bench()
+        log(f"[bench] entropy kernel 64x126464: warm {ent['warm']['us_per_call']:.1f} us, "
+            f"cold {ent['cold']['us_per_call']:.1f} us")
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline ...")
+        cpu = cpu_baseline(cfg, host, prompt_np, args.cpu_layers)
+        log(f"[bench] CPU oracle: {cpu['value']:.4f} steps/s on {cpu['cores']} threads")
+    emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, sweep, roofline, kernels,
+         ent, cpu)
+
+
+def breakdown_report(dec, prompt, with_skip=True):
+    """Per-kernel-group timing, and the roofline object of the dominant kernel of a refresh step."""
+    kb = kernel_breakdown(dec, prompt, n_skip=8 if with_skip else 0)
     ref = kb["refresh"]["kernels"]
     dom = max(ref, key=lambda k: ref[k]["ms"])
     dk = ref[dom]
@@ -331,17 +365,11 @@ def main():
         }
         dec_ms = v["kernels"]["entropy"]["ms"] + v["kernels"]["select"]["ms"]
         kernels[label]["decision_overhead_frac"] = dec_ms / tot if tot > 0 else None
+    return roofline, kernels
 
-    ent = _entropy_kernel_bench()
-    log(f"[bench] entropy kernel 64x126464: warm {ent['warm']['us_per_call']:.1f} us, "
-        f"cold {ent['cold']['us_per_call']:.1f} us")
 
-    cpu = None
-    if not args.no_cpu:
-        log("[bench] CPU oracle baseline ...")
-        cpu = cpu_baseline(cfg, host, prompt_np, args.cpu_layers)
-        log(f"[bench] CPU oracle: {cpu['value']:.4f} steps/s on {cpu['cores']} threads")
-
+def emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, sweep, roofline,
+         kernels, ent, cpu):
     res = {
         "metric": METRIC,
         "value": steps_s,

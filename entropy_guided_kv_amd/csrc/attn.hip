@@ -122,10 +122,10 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
 #pragma unroll
         for (int v = 0; v < 16; ++v) fp[v / 8][v % 8] = (bf16)0.f;
       } else {
-        alpha = exp2f(m_run - m_new);
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float p = exp2f(st[v] - m_new);
+          const float p = __builtin_amdgcn_exp2f(st[v] - m_new);
           psum += p;
           fp[v / 8][v % 8] = (bf16)p;
         }

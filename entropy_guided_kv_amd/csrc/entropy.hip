@@ -11,13 +11,14 @@
 //   m = max(ma, mb); Z = Za e^(ma-m) + Zb e^(mb-m);
 //   S = (Sa + (ma-m) Za) e^(ma-m) + (Sb + (mb-m) Zb) e^(mb-m).
 //
-// Kernel 1 (grid: slices x rows, 256 threads): each workgroup owns one slice
-// of one row and reads it exactly once from HBM with 16-byte loads, all issued
-// up front (U vectors per thread held in registers; consecutive lanes read
-// consecutive vectors). The slice max and first argmax come from a wavefront
-// shuffle + LDS reduction; then every element is exponentiated once against
-// the slice max (exp2 of (x - max) * log2 e) and Z, S are summed the same
-// way. No per-element rescaling and no data reread.
+// Kernel 1: each wavefront owns one slice of one row and reads it exactly once
+// from HBM with 16-byte loads, all issued up front (U vectors per lane held in
+// registers; consecutive lanes read consecutive vectors). The slice max and its
+// first index come from DPP wavefront reductions (no LDS, no barrier); then
+// every element is exponentiated once against the slice max (exp2 of
+// x log2 e - max log2 e, one FMA) and Z, S are summed the same way. No
+// per-element rescaling and no data reread. A NaN logit is skipped by the max
+// but turns Z into NaN, so the row's entropy and confidence come out NaN.
 // Kernel 2 (grid: rows, one wavefront each): merges the slices of a row in a
 // fixed order (deterministic) and writes entropy / argmax / confidence.
 // Kernel 3 (one workgroup, only when E is requested): max over selected rows.
@@ -30,7 +31,7 @@ namespace ec {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kU = 4;  // 16-byte vectors per thread per slice
+constexpr int kU = 2;  // 16-byte vectors per lane per slice (measured best of 1, 2, 4)
 constexpr float kNegInf = -INFINITY;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -71,30 +72,62 @@ __device__ __forceinline__ void vmax(float& v, int& i, float v2, int i2) {
   }
 }
 
-template <typename T, bool VEC>
-__global__ void __launch_bounds__(kThreads)
+// ---- wavefront reductions with DPP (no LDS round trip). After the six steps
+// lane 63 holds the result over all 64 lanes; readlane broadcasts it.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROW_MASK, 0xF, false);
+}
+#define EC_WAVE_REDUCE(NAME, TYPE, OP, TO, FROM)                                 \
+  __device__ __forceinline__ TYPE NAME(TYPE v) {                                 \
+    int x = TO(v);                                                               \
+    x = TO(OP(FROM(x), FROM(dpp<0xB1>(x, x))));        /* quad_perm 1,0,3,2 */   \
+    x = TO(OP(FROM(x), FROM(dpp<0x4E>(x, x))));        /* quad_perm 2,3,0,1 */   \
+    x = TO(OP(FROM(x), FROM(dpp<0x141>(x, x))));       /* row_half_mirror */     \
+    x = TO(OP(FROM(x), FROM(dpp<0x140>(x, x))));       /* row_mirror */          \
+    x = TO(OP(FROM(x), FROM(dpp<0x142, 0xA>(x, x))));  /* row_bcast15 */         \
+    x = TO(OP(FROM(x), FROM(dpp<0x143, 0xC>(x, x))));  /* row_bcast31 */         \
+    return FROM(__builtin_amdgcn_readlane(x, 63));                               \
+  }
+__device__ __forceinline__ int f2i(float v) { return __float_as_int(v); }
+__device__ __forceinline__ float i2f(int v) { return __int_as_float(v); }
+__device__ __forceinline__ int iid(int v) { return v; }
+__device__ __forceinline__ float fadd(float a, float b) { return a + b; }
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+EC_WAVE_REDUCE(wave_max_f, float, fmaxf, f2i, i2f)
+EC_WAVE_REDUCE(wave_sum_f, float, fadd, f2i, i2f)
+EC_WAVE_REDUCE(wave_min_i, int, imin, iid, iid)
+#undef EC_WAVE_REDUCE
+
+// One wavefront per slice of one row (grid: ceil(slices / 4) x rows, 256 threads).
+// Lane l reads vectors l, l+64, ... of the slice (coalesced 1 KB per step), all
+// loads issued before any use. Two register passes: the max (and its first
+// index), then one exp2 per element against that max for Z and S.
+template <typename T, bool VEC, int U>
+__global__ void __launch_bounds__(256)
 entropy_slice_kernel(const T* __restrict__ logits, int V, int64_t stride, int chunk,
-                     Part* __restrict__ parts) {
+                     int slices, Part* __restrict__ parts) {
   constexpr int E = Vec<T>::E;
-  constexpr int NV = kU * E;  // values per thread
-  const int split = blockIdx.x, row = blockIdx.y, splits = gridDim.x;
+  constexpr int NV = U * E;  // values per lane
+  const int lane = threadIdx.x % 64;
+  const int slice = blockIdx.x * 4 + threadIdx.x / 64, row = blockIdx.y;
+  if (slice >= slices) return;
   const T* base = logits + (int64_t)row * stride;
-  const int lo = split * chunk;
+  const int lo = slice * chunk;
   const int hi = min(V, lo + chunk);
-  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
 
   float x[NV];
-  int j0[kU];
+  int j0[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) j0[k] = lo + (lane + 64 * k) * E;
   if (VEC) {
     const int hiv = lo + ((hi - lo) / E) * E;  // end of the whole vectors
-    v4u u[kU];
+    v4u u[U];
 #pragma unroll
-    for (int k = 0; k < kU; ++k) {
-      j0[k] = lo + (tid + k * kThreads) * E;
+    for (int k = 0; k < U; ++k)
       if (j0[k] < hiv) u[k] = *reinterpret_cast<const v4u*>(base + j0[k]);
-    }
 #pragma unroll
-    for (int k = 0; k < kU; ++k) {
+    for (int k = 0; k < U; ++k) {
       if (j0[k] < hiv) {
         Vec<T>::unpack(u[k], x + k * E);
       } else {
@@ -107,95 +140,59 @@ entropy_slice_kernel(const T* __restrict__ logits, int V, int64_t stride, int ch
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < kU; ++k) {
-      j0[k] = lo + (tid + k * kThreads) * E;
+    for (int k = 0; k < U; ++k)
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int j = j0[k] + e;
         x[k * E + e] = j < hi ? to_f(base[j]) : kNegInf;
       }
-    }
   }
 
-  // ---- slice max and first argmax
-  float mv = kNegInf;
+  // ---- pass 1: max (NaN is skipped here; it reaches Z below and makes H NaN)
+  float lm = kNegInf;
+#pragma unroll
+  for (int q = 0; q < NV; ++q) lm = fmaxf(lm, x[q]);
+  const float mv = wave_max_f(lm);
+  // first index of the max: only lanes holding it search their values
   int mi = 0x7fffffff;
-  int nan = 0;
+  if (lm == mv) {
 #pragma unroll
-  for (int k = 0; k < kU; ++k)
+    for (int k = U - 1; k >= 0; --k)
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float v = x[k * E + e];
-      nan |= (v != v);
-      if (v > mv) {  // strict: first index within the thread (indices increase with k, e)
-        mv = v;
-        mi = j0[k] + e;
-      }
-    }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float v2 = __shfl_xor(mv, o);
-    const int i2 = __shfl_xor(mi, o);
-    vmax(mv, mi, v2, i2);
-    nan |= __shfl_xor(nan, o);
+      for (int e = E - 1; e >= 0; --e)
+        if (x[k * E + e] == mv) mi = j0[k] + e;  // ends at this lane's first hit
   }
-  __shared__ float sm[kThreads / 64];
-  __shared__ int si[kThreads / 64], sn[kThreads / 64];
-  __shared__ float sz[kThreads / 64], ss[kThreads / 64];
-  if (lane == 0) {
-    sm[wave] = mv;
-    si[wave] = mi;
-    sn[wave] = nan;
-  }
-  __syncthreads();
-  mv = sm[0];
-  mi = si[0];
-  nan = sn[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) {
-    vmax(mv, mi, sm[w], si[w]);
-    nan |= sn[w];
-  }
+  mi = wave_min_i(mi);
 
-  // ---- Z and S against the slice max (log2 domain, one exp2 per element)
+  // ---- pass 2: Z and S against the max, log2 domain, one exp2 per element:
+  // t = x log2e - m log2e, e = 2^t, Z += e, S2 += max(t, -1000) e. The clamp
+  // makes a -inf logit (e = 0) add -1000 * 0 = 0 instead of -inf * 0 = NaN;
+  // a NaN logit gives e = NaN, which still reaches Z and S.
   float z = 0.f, s2 = 0.f;
   if (mv != kNegInf) {
+    const float mb = mv * kLog2e;
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
-      const float t = (x[q] - mv) * kLog2e;  // exactly 0 at the max
-      const float e = exp2f(t);
+      const float t = fmaf(x[q], kLog2e, -mb);
+      const float e = __builtin_amdgcn_exp2f(t);  // v_exp_f32; results below 2^-126 flush to 0
       z += e;
-      s2 += e > 0.f ? t * e : 0.f;
+      s2 = fmaf(fmaxf(t, -1000.f), e, s2);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    z += __shfl_xor(z, o);
-    s2 += __shfl_xor(s2, o);
-  }
+  z = wave_sum_f(z);
+  s2 = wave_sum_f(s2);
   if (lane == 0) {
-    sz[wave] = z;
-    ss[wave] = s2;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float zt = 0.f, st = 0.f;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
-      zt += sz[w];
-      st += ss[w];
-    }
     Part p;
     p.m = mv;
-    p.z = zt;
-    p.s = st * kLn2;
+    p.z = z;
+    p.s = s2 * kLn2;
     p.idx = mi;
-    p.nan = nan;
-    parts[(int64_t)row * splits + split] = p;
+    p.nan = 0;
+    parts[(int64_t)row * slices + slice] = p;
   }
 }
 
-// One wavefront per row: merge the row's slices (lane l takes slices l, l+64, ...).
+// Kernel 2, one wavefront per row: merge the row's slices (lane l takes slices l, l+64, ...).
 __global__ void __launch_bounds__(64)
 entropy_merge_kernel(const Part* __restrict__ parts, int splits, float* __restrict__ H,
                      int32_t* __restrict__ amax, float* __restrict__ conf) {
@@ -267,8 +264,8 @@ entropy_emax_kernel(const float* __restrict__ H, int rows, const int32_t* __rest
 
 __global__ void fill_kernel(float* p, float v) { *p = v; }
 
-// slice length: kU vectors per thread -> 8192 bf16 / 4096 f32 elements per workgroup
-int slice_len(ec_dtype dt) { return kThreads * kU * (dt == EC_BF16 ? 8 : 4); }
+// slice length: kU vectors per lane of one wavefront -> 1024 bf16 / 512 f32 elements
+int slice_len(ec_dtype dt) { return 64 * kU * (dt == EC_BF16 ? 8 : 4); }
 
 }  // namespace
 
@@ -293,17 +290,17 @@ ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t 
   Part* parts = (Part*)ws;
   const size_t esz = dt == EC_BF16 ? 2 : 4;
   const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * esz) % 16 == 0);
-  dim3 grid(splits, rows);
+  dim3 grid((splits + 3) / 4, rows);
   if (dt == EC_BF16) {
     if (vec)
-      entropy_slice_kernel<bf16, true><<<grid, kThreads, 0, s>>>((const bf16*)logits, vocab, stride, chunk, parts);
+      entropy_slice_kernel<bf16, true, kU><<<grid, 256, 0, s>>>((const bf16*)logits, vocab, stride, chunk, splits, parts);
     else
-      entropy_slice_kernel<bf16, false><<<grid, kThreads, 0, s>>>((const bf16*)logits, vocab, stride, chunk, parts);
+      entropy_slice_kernel<bf16, false, kU><<<grid, 256, 0, s>>>((const bf16*)logits, vocab, stride, chunk, splits, parts);
   } else {
     if (vec)
-      entropy_slice_kernel<float, true><<<grid, kThreads, 0, s>>>((const float*)logits, vocab, stride, chunk, parts);
+      entropy_slice_kernel<float, true, kU><<<grid, 256, 0, s>>>((const float*)logits, vocab, stride, chunk, splits, parts);
     else
-      entropy_slice_kernel<float, false><<<grid, kThreads, 0, s>>>((const float*)logits, vocab, stride, chunk, parts);
+      entropy_slice_kernel<float, false, kU><<<grid, 256, 0, s>>>((const float*)logits, vocab, stride, chunk, splits, parts);
   }
   EC_CHECK_LAUNCH("entropy_slice_kernel");
   entropy_merge_kernel<<<rows, 64, 0, s>>>(parts, splits, H, amax, c);

@@ -60,7 +60,7 @@ def test_entropy_edge_rows(dtype):
     Hg, h0 = _check(x, ref)
     got = dict(zip(names, Hg))
     assert abs(got["uniform"] - math.log(V)) <= H_TOL
-    assert got["one_hot"] == 0.0
+    assert abs(got["one_hot"]) <= 1e-6  # 0 up to the rounding of max * log2(e)
     assert abs(got["tie4"] - math.log(4)) <= H_TOL
 
 
