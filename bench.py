@@ -27,6 +27,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "denoising steps/s and gen tokens/s at L=1024,k=16 (1 GPU); % HBM/MFMA peak"
+# kernel the library launches for each timed group at M = 1024 (must match the profile's tag)
+KERNEL_TAGS = {"gateup": "gemm_bf16_kernel<128,128,32,64,64,2,EPI_SWIGLU,true,false>"}
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16
 
@@ -49,6 +52,22 @@ def step_work(m, L: int, r: int, n_cand: int):
     flops = nl * (2 * r * per_layer_w + 4 * r * L * d) + 2 * n_cand * V * d
     bytes_ = 2 * (nl * per_layer_w + V * d) + nl * (2 * L * d * 2 + 2 * r * d * 2) + 2 * 2 * n_cand * V
     return float(flops), float(bytes_)
+
+
+def measured_traffic(group: str):
+    """HBM bytes per launch from the committed PMC summary, if it covers the kernel in use."""
+    import re
+    tag = KERNEL_TAGS.get(group)
+    if tag is None or not os.path.isdir(PROFILE_DIR):
+        return None
+    for f in sorted(os.listdir(PROFILE_DIR)):
+        if not f.endswith((".md", ".txt")):
+            continue
+        for line in open(os.path.join(PROFILE_DIR, f)):
+            m = re.match(r"traffic_bytes_per_launch: (\d+) kernel: (\S+)", line.strip())
+            if m and m.group(2) == tag:
+                return int(m.group(1))
+    return None
 
 
 def t_roof(flops: float, bytes_: float) -> float:
@@ -239,6 +258,8 @@ def main():
     ap.add_argument("--no-entropy", action="store_true", help="skip the 64x126464 entropy kernel run")
     ap.add_argument("--entropy-only", action="store_true",
                     help="only the 64x126464 entropy kernel run (no model)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (a known-size reference for HBM counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -256,6 +277,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     api.load()
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.entropy_only:
         ent = _entropy_kernel_bench()
         print(json.dumps({"entropy_kernel_64x126464": ent}), flush=True)
@@ -343,13 +371,15 @@ def breakdown_report(dec, prompt, with_skip=True):
     if flops_launch > 0:
         achieved = flops_launch / (avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_BF16_PEAK / 1e12,
-                    "unit": "TFLOP/s", "frac": achieved / (MFMA_BF16_PEAK / 1e12), "traffic": None,
+                    "unit": "TFLOP/s", "frac": achieved / (MFMA_BF16_PEAK / 1e12),
+                    "traffic": measured_traffic(dom),
                     "avg_launch_us": avg_ms * 1e3, "flops_per_launch": flops_launch,
                     "bytes_per_launch": bytes_launch}
     else:
         achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK / 1e9,
-                    "unit": "GB/s", "frac": achieved / (HBM_PEAK / 1e9), "traffic": None,
+                    "unit": "GB/s", "frac": achieved / (HBM_PEAK / 1e9),
+                    "traffic": measured_traffic(dom),
                     "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": bytes_launch}
     log(f"[bench] dominant kernel {dom}: {avg_ms * 1e3:.1f} us/launch, {roofline['frac']:.3f} of peak")
     kernels = {}

@@ -1,0 +1,110 @@
+"""The C ABI library loads, exports every symbol include/ec.h declares, and rejects bad
+arguments before touching the GPU (CPU-only: no compute call is made)."""
+import ctypes as C
+import math
+import os
+import re
+
+import pytest
+
+from entropy_guided_kv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "ec.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ec_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libec.so is not built; run `python -m entropy_guided_kv_amd.build`")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ec.h but not exported"
+    assert set(_lib.EXPORTS) <= set(names)
+
+
+def test_version_and_error_string(lib):
+    assert lib.ec_version() == 10000
+    assert isinstance(lib.ec_last_error(), bytes)
+
+
+def test_workspace_queries_are_host_only(lib):
+    assert lib.ec_entropy_max_workspace_size(64, 126464) >= 64 * 62 * 32
+    assert lib.ec_entropy_max_workspace_size(0, 10) == 0
+    assert lib.ec_partial_attn_workspace_size(1, 1024, 32, 128) > 0  # split-L partials
+    assert lib.ec_partial_attn_workspace_size(1024, 1024, 32, 128) == 0
+    assert lib.ec_state_plan_words(1024, 16) >= 8 + 16 + 4 * 1024
+    assert lib.ec_state_plan_words(0, 16) == 0
+
+
+def _model_desc(dtype=_lib.EC_BF16, d=4096, H=32, Dh=128, F=12288, V=126464, n_layers=32):
+    lw = (_lib.ec_layer_weights * n_layers)()
+    for i in range(n_layers):
+        for f in ("attn_norm", "wqkv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"):
+            setattr(lw[i], f, 0x1000)  # non-null; never dereferenced by the size queries
+    m = _lib.ec_model_desc()
+    m.struct_size = C.sizeof(_lib.ec_model_desc)
+    m.dtype = dtype
+    m.n_layers, m.d_model, m.n_heads, m.head_dim, m.ffn_dim, m.vocab = n_layers, d, H, Dh, F, V
+    m.rms_eps = 1e-5
+    m.embed = m.final_norm = m.lm_head = m.rope_cos = m.rope_sin = 0x1000
+    m.layers = C.cast(lw, C.POINTER(_lib.ec_layer_weights))
+    m.rope_max_pos = 4096
+    return m, lw
+
+
+def _params(L=1024, P=768, k=16, n=1, B=32, tau=1.0, mask=126463):
+    p = _lib.ec_params()
+    p.struct_size = C.sizeof(_lib.ec_params)
+    p.tau, p.k_recent, p.tokens_per_step, p.block_len = tau, k, n, B
+    p.prompt_len, p.seq_len, p.mask_id = P, L, mask
+    return p
+
+
+def test_step_workspace_size_for_the_8b_config(lib):
+    m, _keep = _model_desc()
+    p = _params()
+    ws = lib.ec_step_workspace_size(C.byref(m), C.byref(p))
+    # h fp32 + 3 bf16 [L, d] buffers + SwiGLU [L, F] + logits [B, V] at least
+    assert ws >= 1024 * 4096 * 4 + 3 * 1024 * 4096 * 2 + 1024 * 12288 * 2 + 32 * 126464 * 2
+    assert ws < 512 << 20
+
+
+def test_unsupported_shapes_and_bad_params_are_rejected(lib):
+    m, _keep = _model_desc(Dh=64, H=64)  # bf16 path needs head_dim 128
+    p = _params()
+    assert lib.ec_step_workspace_size(C.byref(m), C.byref(p)) == 0
+    m2, _keep2 = _model_desc()
+    bad = _params(n=0)
+    assert lib.ec_step_workspace_size(C.byref(m2), C.byref(bad)) == 0
+    bad = _params(tau=math.nan)
+    assert lib.ec_step_workspace_size(C.byref(m2), C.byref(bad)) == 0
+
+
+def test_argument_errors_return_before_any_gpu_work(lib):
+    E = _lib
+    # bad dtype / sizes: rejected by the host checks, nothing is launched
+    assert lib.ec_entropy_max(None, 7, 1, 10, 10, None, 0, None, None, None, None, None, 0, None) == E.EC_ERR_DTYPE
+    assert lib.ec_entropy_max(None, E.EC_BF16, 1, 10, 5, None, 0, None, None, None, None, None, 0, None) == E.EC_ERR_ARG
+    assert lib.ec_entropy_max(0x1000, E.EC_BF16, 4, 10, 10, None, 0, 0x1000, 0x1000, 0x1000, None, None, 0, None) == E.EC_ERR_WORKSPACE
+    assert lib.ec_cache_scatter(None, None, 10, 8, E.EC_F32, None, None, None, 3, None) == E.EC_ERR_ARG
+    assert lib.ec_cache_scatter(None, None, 10, 8, E.EC_F32, None, None, None, 0, None) == E.EC_OK
+    assert lib.ec_partial_attn(None, None, None, 4, 16, 2, 128, 1.0, E.EC_BF16, None, None, 0, None) == E.EC_ERR_ARG
+    assert lib.ec_step(None, None, None, None, None, 0, None, None) == E.EC_ERR_ARG
+    assert b"model" in lib.ec_last_error()
+    m, _keep = _model_desc()
+    assert lib.ec_forward(C.byref(m), None, None, None, 0, None, 0, None, None, None, 0, None) == E.EC_ERR_ARG
+    assert lib.ec_rope_table(None, None, 16, 128, 10000.0, None) == E.EC_ERR_ARG
+    st = _lib.ec_state()
+    st.struct_size = C.sizeof(_lib.ec_state)
+    assert lib.ec_state_reset(C.byref(st), C.byref(_params()), None) == E.EC_ERR_ARG
