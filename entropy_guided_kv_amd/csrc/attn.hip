@@ -10,16 +10,22 @@
 // transposed so that no register shuffles are needed between the two
 // products: a wavefront owns 32 query rows and, per 32-row K/V sub-tile,
 //   S^T = K Q^T        8 x v_mfma_f32_32x32x16_bf16 (A = K rows, B = Q rows)
-//   O^T += V^T P^T     8 x v_mfma_f32_32x32x16_bf16 (A = V^T from LDS, B = P^T)
+//   O^T += V^T P^T     8 x v_mfma_f32_32x32x16_bf16 (A = V^T, B = P^T)
 // In the 32x32 accumulator layout a lane holds one query column and 16 key
 // rows; those 16 values, converted to bf16 in order, are exactly the lane's
 // B operand of the second product for the two 16-key halves, provided V^T's
-// A operand supplies keys in the same slot order (two 8-byte LDS reads).
+// A operand supplies keys in the same slot order. V stays in its natural
+// [key][dim] layout in LDS and the V^T operand comes from gfx950's
+// transposing LDS read (ds_read_tr16_b64: within 16 lanes, lane j receives
+// element j of each of four source lanes' 8-byte rows), two per fragment.
 // Softmax statistics are per lane (one query), completed with one
-// cross-half exchange. Q stays in registers; K and V^T tiles of 64 keys are
-// staged in LDS and shared by the 4 wavefronts (128 queries) of a
-// workgroup. When heads x query tiles under-fill the 256 CUs, the key range
-// is split over workgroups and a merge kernel combines (m, l, o) exactly.
+// cross-half exchange; the reference max is only moved (and O, l rescaled)
+// when a row max exceeds it by 2^8, so most tiles skip the rescale. Q stays
+// in registers; K and V tiles of 64 keys are double-buffered in LDS, the next
+// tile's global loads in flight during the current tile's MFMAs, shared by the
+// 4 wavefronts (128 queries) of a workgroup. When heads x query tiles
+// under-fill the 256 CUs, the key range is split over workgroups and a merge
+// kernel combines (m, l, o) exactly.
 #include "ec_internal.h"
 
 #include <math.h>
@@ -32,9 +38,13 @@ constexpr int kThreads = 256;
 constexpr int D = 128;       // head_dim of the MFMA kernel
 constexpr int BQ = 128;      // queries per workgroup (32 per wavefront)
 constexpr int BKV = 64;      // keys per LDS stage
-constexpr int KS = D + 8;    // LDS row stride of K tile (bf16)
-constexpr int VS = BKV + 8;  // LDS row stride of V^T tile (bf16)
+constexpr int KS = D + 16;   // LDS row stride (bf16): 288 bytes keeps b128 and transpose reads conflict-free
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.f;  // lazy rescale: keep the reference max until a row max exceeds it by 2^8
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) bf16 lds_bf16;
 
 // grid: (query tiles, heads, splits)
 template <bool SPLIT>
@@ -43,8 +53,9 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                  const bf16* __restrict__ vc, int r, int L, int H, float scale_log2,
                  int kv_chunk, bf16* __restrict__ out, float* __restrict__ po,
                  float* __restrict__ pml) {
-  __shared__ __align__(16) bf16 sK[BKV * KS];
-  __shared__ __align__(16) bf16 sVt[D * VS];
+  // K and V tiles in natural [key][dim] layout, double-buffered
+  __shared__ __align__(16) bf16 sK[2][BKV * KS];
+  __shared__ __align__(16) bf16 sV[2][BKV * KS];
 
   const int qt = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -53,15 +64,12 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   const int qrow = qt * BQ + wave * 32 + lq;  // this lane's query (column of S^T)
   const bool qok = qrow < r;
 
-  // Q fragments (B operand): Q[qrow][16kk + 8g .. +7]
+  // Q fragments (B operand of S^T): Q[qrow][16kk + 8g .. +7]
   bf16x8 fq[D / 16];
   {
     const bf16* src = q + (int64_t)(qok ? qrow : 0) * HD + h * D + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      uint4 u = qok ? *reinterpret_cast<const uint4*>(src + 16 * kk) : make_uint4(0, 0, 0, 0);
-      fq[kk] = *reinterpret_cast<bf16x8*>(&u);
-    }
+    for (int kk = 0; kk < D / 16; ++kk) fq[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
   }
 
   f32x16 o[D / 32];
@@ -69,92 +77,115 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;  // reference max (log2 units) and row sum
 
   const int kv_lo = split * kv_chunk;
   const int kv_hi = min(L, kv_lo + kv_chunk);
+  const int ntiles = (kv_hi - kv_lo + BKV - 1) / BKV;
 
-  for (int kv0 = kv_lo; kv0 < kv_hi; kv0 += BKV) {
-    // ---- stage K (row-major) and V^T into LDS: 64 keys x 128 dims, 4 vectors per thread
-    __syncthreads();
+  // staging: 64 keys x 16 vectors of 8 dims per tile, 4 vectors per thread for K and for V
+  constexpr int NV = BKV * (D / 8) / kThreads;
+  bf16x8 rk[NV], rv[NV];
+  auto gload = [&](int t) __attribute__((always_inline)) {
+    const int kv0 = kv_lo + t * BKV;
 #pragma unroll
-    for (int i = 0; i < (BKV * D / 8) / kThreads; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int v = tid + i * kThreads;
-      const int row = v / (D / 8), dv = (v % (D / 8)) * 8;
-      const int key = kv0 + row;
-      uint4 ku = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
-      if (key < kv_hi) {
-        ku = *reinterpret_cast<const uint4*>(kc + (int64_t)key * HD + h * D + dv);
-        vu = *reinterpret_cast<const uint4*>(vc + (int64_t)key * HD + h * D + dv);
-      }
-      *reinterpret_cast<uint4*>(sK + row * KS + dv) = ku;
-      const bf16* ve = reinterpret_cast<const bf16*>(&vu);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sVt[(dv + e) * VS + row] = ve[e];
+      const int key = min(kv0 + v / (D / 8), L - 1);  // rows past the end are masked below
+      const int dv = (v % (D / 8)) * 8;
+      rk[i] = *reinterpret_cast<const bf16x8*>(kc + (int64_t)key * HD + h * D + dv);
+      rv[i] = *reinterpret_cast<const bf16x8*>(vc + (int64_t)key * HD + h * D + dv);
     }
-    __syncthreads();
+  };
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = tid + i * kThreads;
+      const int off = (v / (D / 8)) * KS + (v % (D / 8)) * 8;
+      *reinterpret_cast<bf16x8*>(&sK[buf][off]) = rk[i];
+      *reinterpret_cast<bf16x8*>(&sV[buf][off]) = rv[i];
+    }
+  };
 
+  // transpose-read coordinates for the V^T operand: within each 16-lane group, source lane
+  // s points at (key base + s/4, dim base + 4 (s%4)); ds_read_tr16_b64 then hands lane j the
+  // four keys of dim base + j
+  const int tr_key = (lane % 16) / 4, tr_dim = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+
+  if (ntiles > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int kv0 = kv_lo + t * BKV;
+    if (t + 1 < ntiles) gload(t + 1);
+    const bf16* kt = sK[buf];
+    const lds_bf16* vt = (const lds_bf16*)sV[buf];
 #pragma unroll
     for (int sub = 0; sub < BKV / 32; ++sub) {
-      // ---- S^T[32 keys, 32 queries]
+      // ---- S^T[32 keys, 32 queries] (raw dot products)
       f32x16 st;
 #pragma unroll
       for (int v = 0; v < 16; ++v) st[v] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        bf16x8 fk = *reinterpret_cast<const bf16x8*>(sK + (sub * 32 + lq) * KS + 16 * kk + 8 * g);
+        const bf16x8 fk = *reinterpret_cast<const bf16x8*>(kt + (sub * 32 + lq) * KS + 16 * kk + 8 * g);
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk, fq[kk], st, 0, 0, 0);
       }
-      // key of st[v]: kv0 + sub*32 + 8(v/4) + 4g + v%4
+      // key of st[v]: kv0 + sub*32 + 8(v/4) + 4g + v%4; mask keys past the end of the range
+      if (kv0 + sub * 32 + 32 > kv_hi) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (kv0 + sub * 32 + 8 * (v / 4) + 4 * g + (v % 4) >= kv_hi) st[v] = -INFINITY;
+      }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = kv0 + sub * 32 + 8 * (v / 4) + 4 * g + (v % 4);
-        st[v] = key < kv_hi ? st[v] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, st[v]);
+      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, st[v]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;
+      // lazy rescale: only when some row's max moved past the reference by 2^kRescale
+      if (__any(tmax > m_ref + kRescale)) {
+        const float m_new = fmaxf(m_ref, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+        m_ref = m_new;
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      float alpha, psum = 0.f;
+      float psum = 0.f;
       bf16x8 fp[2];
-      if (m_new == -INFINITY) {  // nothing valid yet (cannot happen for L >= 1)
-        alpha = 1.f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) fp[v / 8][v % 8] = (bf16)0.f;
-      } else {
-        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(st[v] - m_new);
-          psum += p;
-          fp[v / 8][v % 8] = (bf16)p;
-        }
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[v], scale_log2, -m_ref));
+        psum += p;
+        fp[v / 8][v % 8] = (bf16)p;
       }
-      psum += __shfl_xor(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-      // ---- O^T[d, q] += V^T[d, keys] P^T[keys, q], two 16-key chunks
+      l_run += psum + __shfl_xor(psum, 32);
+      // ---- O^T[d, q] += V^T[d, keys] P^T[keys, q]; A operand by transpose reads
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
-          const bf16* vr = sVt + (32 * i + lq) * VS + sub * 32 + 16 * c + 4 * g;
-          bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-          bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 8);
+          const int kb = sub * 32 + 16 * c + 4 * g + tr_key;
+          const lds_bf16* p0 = vt + kb * KS + 32 * i + tr_dim;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * KS));
           bf16x8 fv;
+          const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            fv[e] = lo[e];
-            fv[4 + e] = hi[e];
+            fv[e] = l4[e];
+            fv[4 + e] = h4[e];
           }
           o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv, fp[c], o[i], 0, 0, 0);
         }
       }
     }
+    if (t + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
   }
 
   if (!qok) return;
@@ -174,7 +205,7 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
       for (int v = 0; v < 16; ++v) dst[32 * i + 8 * (v / 4) + 4 * g + (v % 4)] = o[i][v];
     if (g == 0) {
       float* ml = pml + (((int64_t)split * r + qrow) * H + h) * 2;
-      ml[0] = m_run;
+      ml[0] = m_ref;
       ml[1] = l_run;
     }
   }

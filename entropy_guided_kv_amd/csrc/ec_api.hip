@@ -403,6 +403,7 @@ ec_status ec_partial_attn(const void* q, const void* k_cache, const void* v_cach
              "ec_partial_attn: bad sizes");
   if (r == 0) return EC_OK;
   EC_REQUIRE(q && k_cache && v_cache && out, EC_ERR_ARG, "ec_partial_attn: null pointer");
+  EC_REQUIRE(scale > 0.f, EC_ERR_ARG, "ec_partial_attn: scale must be positive");
   return attn(dtype, q, k_cache, v_cache, r, seq_len, n_heads, head_dim, scale, out, workspace,
               workspace_bytes, (hipStream_t)stream);
 }

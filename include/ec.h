@@ -110,7 +110,7 @@ ec_status ec_cache_scatter(void* k_cache, void* v_cache, int64_t seq_len, int32_
  *
  * out[i, h, :] = softmax_j(q[i,h,:] . k_cache[j,h,:] * scale) @ v_cache[:,h,:]
  * q, out: [r, n_heads * head_dim]; k_cache, v_cache: [seq_len, n_heads *
- * head_dim]; all of dtype. bf16 runs on MFMA with fp32 softmax; the
+ * head_dim]; all of dtype; scale > 0. bf16 runs on MFMA with fp32 softmax; the
  * probabilities enter the P.V product rounded to bf16.
  * Supported: head_dim == 128 for bf16, head_dim <= 256 for f32.
  * workspace: >= ec_partial_attn_workspace_size(...) bytes (may be 0 -> NULL ok).
