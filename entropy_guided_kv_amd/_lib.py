@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(PKG, "libec.so")
 
 EC_OK, EC_ERR_ARG, EC_ERR_DTYPE, EC_ERR_WORKSPACE, EC_ERR_HIP, EC_ERR_NAN, EC_ERR_UNSUPPORTED = range(7)
 EC_F32, EC_BF16 = 0, 1
+EC_LAYOUT_PLAIN, EC_LAYOUT_PACKED = 0, 1
 EC_MAX_TOKENS_PER_STEP = 64
 
 STATUS_NAMES = {
@@ -21,7 +22,7 @@ EXPORTS = (
     "ec_partial_attn_workspace_size", "ec_partial_attn", "ec_rope_table",
     "ec_forward_workspace_size", "ec_forward", "ec_state_plan_words", "ec_state_reset",
     "ec_step_workspace_size", "ec_step", "ec_timing_enable", "ec_timing_read", "ec_last_error",
-    "ec_version",
+    "ec_version", "ec_pack_weights",
 )
 
 EC_T_KINDS = 10
@@ -43,6 +44,7 @@ class ec_model_desc(C.Structure):
         ("embed", C.c_void_p), ("layers", C.POINTER(ec_layer_weights)),
         ("final_norm", C.c_void_p), ("lm_head", C.c_void_p),
         ("rope_cos", C.c_void_p), ("rope_sin", C.c_void_p), ("rope_max_pos", C.c_int32),
+        ("weight_layout", C.c_int32),
     ]
 
 
@@ -118,6 +120,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ec_timing_read": (C.c_int, [C.POINTER(ec_timing), C.c_int]),
         "ec_last_error": (C.c_char_p, []),
         "ec_version": (C.c_int, []),
+        "ec_pack_weights": (C.c_int, [C.c_int, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

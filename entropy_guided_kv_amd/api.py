@@ -136,6 +136,21 @@ def _to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
     return t.to(device)
 
 
+def pack_weights(shape, wqkv: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, stream=None):
+    """ec_pack_weights: plain [3d, d] and [F, d] x2 device matrices -> packed
+    (wqkv [3d, d], gate/up [2F, d]) for the MFMA kernels."""
+    lib = load()
+    d, F = shape.d_model, shape.ffn_dim
+    for t, rows in ((wqkv, 3 * d), (w_gate, F), (w_up, F)):
+        assert t.is_contiguous() and tuple(t.shape) == (rows, d), "pack_weights: bad matrix shape"
+    qp = torch.empty_like(wqkv)
+    gu = torch.empty(2 * F, d, dtype=w_gate.dtype, device=w_gate.device)
+    dt = _lib.EC_BF16 if wqkv.dtype == torch.bfloat16 else _lib.EC_F32
+    check(lib.ec_pack_weights(dt, d, shape.head_dim, F, _ptr(wqkv), _ptr(w_gate), _ptr(w_up),
+                              _ptr(qp), _ptr(gu), _stream(stream)), "ec_pack_weights")
+    return qp, gu
+
+
 class DeviceModel:
     """Weights on the GPU plus the ec_model_desc that points at them."""
 
@@ -148,10 +163,16 @@ class DeviceModel:
         self.rope_cos, self.rope_sin = ec_rope_table(rope_max_pos, shape.head_dim, shape.rope_base,
                                                      self.device)
         n = len(layers)
+        if shape.dtype == "bf16":
+            # the MFMA kernels read the packed layout; repack each layer on the device
+            # in place of the plain matrices (ec_pack_weights)
+            for lw in layers:
+                lw["wqkv"], lw["w_gate"] = pack_weights(shape, lw["wqkv"], lw["w_gate"], lw["w_up"])
+                lw["w_up"] = None
         self._lw = (_lib.ec_layer_weights * n)()
         for i, lw in enumerate(layers):
             for name in ("attn_norm", "wqkv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"):
-                setattr(self._lw[i], name, lw[name].data_ptr())
+                setattr(self._lw[i], name, lw[name].data_ptr() if lw[name] is not None else None)
         d = _lib.ec_model_desc()
         d.struct_size = C.sizeof(_lib.ec_model_desc)
         d.dtype = _lib.EC_BF16 if shape.dtype == "bf16" else _lib.EC_F32
@@ -161,6 +182,7 @@ class DeviceModel:
         d.embed, d.final_norm, d.lm_head = embed.data_ptr(), final_norm.data_ptr(), lm_head.data_ptr()
         d.layers = C.cast(self._lw, C.POINTER(_lib.ec_layer_weights))
         d.rope_cos, d.rope_sin, d.rope_max_pos = self.rope_cos.data_ptr(), self.rope_sin.data_ptr(), rope_max_pos
+        d.weight_layout = _lib.EC_LAYOUT_PACKED if shape.dtype == "bf16" else _lib.EC_LAYOUT_PLAIN
         self.desc = d
         _ = lib
 

@@ -94,9 +94,13 @@ ec_status check_model(const ec_model_desc* m) {
   EC_REQUIRE(m->head_dim % 2 == 0, EC_ERR_ARG, "model: head_dim must be even");
   EC_REQUIRE(m->embed && m->layers && m->final_norm && m->lm_head && m->rope_cos && m->rope_sin,
              EC_ERR_ARG, "model: null pointer");
+  const bool packed = m->dtype == EC_BF16;
+  EC_REQUIRE(m->weight_layout == (packed ? EC_LAYOUT_PACKED : EC_LAYOUT_PLAIN), EC_ERR_ARG,
+             "model: weight_layout must be %s for %s models (see ec_pack_weights)",
+             packed ? "EC_LAYOUT_PACKED" : "EC_LAYOUT_PLAIN", packed ? "bf16" : "fp32");
   for (int l = 0; l < m->n_layers; ++l) {
     const ec_layer_weights& w = m->layers[l];
-    EC_REQUIRE(w.attn_norm && w.wqkv && w.wo && w.mlp_norm && w.w_gate && w.w_up && w.w_down,
+    EC_REQUIRE(w.attn_norm && w.wqkv && w.wo && w.mlp_norm && w.w_gate && (packed || w.w_up) && w.w_down,
                EC_ERR_ARG, "model: null weight in layer %d", l);
   }
   if (m->dtype == EC_BF16) {
@@ -356,6 +360,24 @@ ec_status ec_timing_read(ec_timing* out, int reset) {
   return EC_OK;
 }
 int ec_version(void) { return EC_VERSION; }
+
+ec_status ec_pack_weights(ec_dtype dtype, int32_t d_model, int32_t head_dim, int32_t ffn_dim,
+                          const void* wqkv, const void* w_gate, const void* w_up,
+                          void* wqkv_packed, void* gateup_packed, void* stream) {
+  EC_REQUIRE(dtype_ok(dtype), EC_ERR_DTYPE, "ec_pack_weights: bad dtype %d", (int)dtype);
+  EC_REQUIRE(d_model > 0 && head_dim > 0 && ffn_dim > 0, EC_ERR_ARG, "ec_pack_weights: non-positive size");
+  if (wqkv_packed) {
+    EC_REQUIRE(wqkv, EC_ERR_ARG, "ec_pack_weights: wqkv is NULL");
+    EC_REQUIRE(head_dim % 32 == 0 && d_model % head_dim == 0, EC_ERR_ARG,
+               "ec_pack_weights: need head_dim %% 32 == 0 and d_model %% head_dim == 0");
+  }
+  if (gateup_packed) {
+    EC_REQUIRE(w_gate && w_up, EC_ERR_ARG, "ec_pack_weights: w_gate or w_up is NULL");
+    EC_REQUIRE(ffn_dim % 16 == 0, EC_ERR_ARG, "ec_pack_weights: need ffn_dim %% 16 == 0");
+  }
+  return pack_weights((int)esize(dtype), d_model, head_dim, ffn_dim, wqkv, w_gate, w_up, wqkv_packed,
+                      gateup_packed, (hipStream_t)stream);
+}
 
 size_t ec_entropy_max_workspace_size(int32_t rows, int32_t vocab) {
   return entropy_ws_bytes(rows, vocab);

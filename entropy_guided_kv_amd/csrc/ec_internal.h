@@ -74,8 +74,14 @@ struct EpiArgs {
 };
 
 size_t gemm_splitk_ws_bytes(int M, int N, int K, int kind, bool bf16);
+// f32: plain weights (QKV [3d, K]; SwiGLU B = gate [N, K], B2 = up [N, K]).
+// bf16: packed weights (QKV rotary-interleaved [3d, K]; SwiGLU B = [2N, K] gate/up
+// interleave, B2 unused). N is the number of output columns.
 ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M, int N, int K,
                const EpiArgs& epi, float* splitk_ws, size_t splitk_ws_bytes, hipStream_t s);
+ec_status pack_weights(int elem_bytes, int d, int head_dim, int F, const void* wqkv,
+                       const void* w_gate, const void* w_up, void* wqkv_packed,
+                       void* gateup_packed, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 size_t attn_ws_bytes(int r, int L, int H, int D);

@@ -5,19 +5,17 @@
 //                 K/V cache at positions rows[m] (the recomputed rows' cache
 //                 update of a skip step; every row on a refresh);
 //   EPI_RESID  -- residual add into the fp32 hidden state (O-proj, down-proj);
-//   EPI_SWIGLU -- two weight matrices (gate, up) share the A tile; the
-//                 epilogue writes silu(gate) * up;
+//   EPI_SWIGLU -- gate and up rows interleaved in one packed weight matrix;
+//                 the epilogue writes silu(gate) * up;
 //   EPI_STORE  -- plain store (LM head logits).
 //
-// bf16 path: MFMA v_mfma_f32_32x32x16_bf16 (gfx950). Both operands are
-// K-contiguous, so every fragment is one 16-byte LDS read. 256 threads = 4
-// wavefronts; a wavefront owns a WM x WN block made of 32x32 MFMA tiles.
-// With WN = 128 a wavefront's four column tiles are one attention head
-// (columns c and c + 64 sit in tiles j and j + 2 of the same lane and
-// register), so the rotary pairs and the gate/up pairs are register-local.
-// Tiles are staged global -> registers -> LDS (row stride padded by 16 bytes
-// against bank conflicts), double-buffered over BK = 64, with the next tile's
-// global loads in flight during the current tile's MFMAs.
+// bf16 path: MFMA v_mfma_f32_32x32x16_bf16 (gfx950), both operands K-contiguous.
+// Global tiles are loaded straight into LDS (global_load_lds_dwordx4) in a
+// swizzled, unpadded layout; several K-steps are in flight while the MFMAs of
+// the current one run. The rotary and SwiGLU pairs come from packed weights
+// (ec_pack_weights) that place the two members of a pair 16 columns apart in
+// one 32-column MFMA tile, so the pair is exchanged with one lane swizzle and
+// any tile width that is a multiple of 32 works for every epilogue.
 //
 // Block order is XCD-aware: MI355X dispatches consecutive workgroups round-
 // robin over its 8 XCDs (each with its own L2), so block ids are remapped to
@@ -41,14 +39,16 @@ constexpr int kThreads = 256;
 constexpr int BK = 64;
 // native 16-byte vector (a plain vector load/store, unlike the uint4 struct)
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (144 bytes)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // -------------------------------------------------------------------- epilogue helpers
+// Rotary pair (x1, x2) at columns (col, col + D/2) of the [3d] q|k|v output, col in
+// the first half of its head. WHICH bit 0 writes the rotated first element, bit 1
+// the second (q to the compact buffer, k and v to the cache row of position rows[m]).
 template <typename T>
-__device__ __forceinline__ void epi_qkv_pair(const EpiArgs& e, int m, int col, float x1, float x2) {
-  // col: column of the first element of the pair within [0, 3d); partner is col + D/2
+__device__ __forceinline__ void epi_qkv_pair(const EpiArgs& e, int m, int col, float x1, float x2,
+                                             int which = 3) {
   const int d = e.d_model, D = e.head_dim, half = D / 2;
   const int sec = col / d;
   const int hc = col % d;            // column within the q / k / v section
@@ -66,8 +66,8 @@ __device__ __forceinline__ void epi_qkv_pair(const EpiArgs& e, int m, int col, f
   if (sec == 0) dst = (T*)e.out + (int64_t)m * d;
   else if (sec == 1) dst = (T*)e.k_cache + (int64_t)pos * d;
   else dst = (T*)e.v_cache + (int64_t)pos * d;
-  dst[hc] = from_f<T>(y1);
-  dst[hc + half] = from_f<T>(y2);
+  if (which & 1) dst[hc] = from_f<T>(y1);
+  if (which & 2) dst[hc + half] = from_f<T>(y2);
 }
 
 template <typename T>
@@ -92,35 +92,74 @@ __device__ __forceinline__ int xcd_remap(int pid, int nblk) {
 }
 
 // -------------------------------------------------------------------- bf16 MFMA GEMM
-// BM x BN workgroup tile, WM x WN per wavefront, (BM/WM)*(BN/WN) wavefronts,
-// K staged BKT at a time through two LDS buffers; STAGES register sets hold
-// the next K-steps' tiles in flight (prefetch depth).
-// DUAL: B rows [0, BN/2) come from B (gate), rows [BN/2, BN) from B2 (up);
-//       the workgroup writes BN/2 output columns.
-// SPLIT: write raw fp32 partials to `part` ([S][M][ncols]) instead of the epilogue.
-template <int BM, int BN, int WM, int WN, int BKT, int STAGES, int EPI, bool DUAL, bool SPLIT>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
-                 const bf16* __restrict__ B2, int M, int N, int K, int k_chunk, int splits,
-                 EpiArgs epi, float* __restrict__ part) {
-  constexpr int WAVES_N = BN / WN;
-  constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int LS = BKT + 8;                    // LDS row stride (bf16), 16-byte pad
-  constexpr int CPR = BKT / 8;                   // 16-byte chunks per row
-  constexpr int A_VECS = BM * CPR / NT;          // 16-byte vectors per thread
-  constexpr int B_VECS = BN * CPR / NT;
-  // paired epilogues: a wavefront's first TN/2 column tiles pair with its last TN/2
-  // (rotary halves c / c+64 of one head, or gate / up of the same output columns)
-  constexpr bool PAIRED = DUAL || EPI == EPI_QKV;
-  static_assert(EPI != EPI_QKV || BN == 128, "QKV tiles are one head (128 columns) wide");
-  static_assert(!PAIRED || TN % 2 == 0, "paired epilogue needs an even number of column tiles");
-  static_assert(A_VECS >= 1 && B_VECS >= 1 && A_VECS * NT == BM * CPR && B_VECS * NT == BN * CPR,
-                "tile / thread mismatch");
+// Packed weight layouts (built once by ec_pack_weights) put the two operands of
+// every paired epilogue 16 columns apart inside one 32-column MFMA tile, so a
+// lane finds its partner in lane ^ 16 of the same accumulator register:
+//   rotary (QKV):  inside each head of D columns, 32-column group g holds the
+//                  first-half columns 16g .. 16g+15 followed by their partners
+//                  D/2 + 16g .. D/2 + 16g + 15;
+//   SwiGLU:        [2F, d] with 32-row group g = gate rows 16g .. 16g+15, then up
+//                  rows 16g .. 16g+15.
+// Any column tile that is a multiple of 32 then keeps every pair in one wavefront.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+// workgroup barrier for LDS produced by direct-to-LDS loads: the waits are explicit
+// (the loads are tracked by vmcnt only), the fences keep the compiler from moving
+// LDS accesses across it
+__device__ __forceinline__ void lds_stage_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// value of lane ^ 16 (ds_swizzle bit mode, xor mask 0x10 within 32-lane groups)
+__device__ __forceinline__ float swap16(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+
+// C tile BM x BN from A[M, K] (row stride K) and B[N, K] (row stride K), bf16 in,
+// fp32 accumulate on v_mfma_f32_32x32x16_bf16. Wavefront tile WM x WN.
+//
+// Staging: K advances 64 at a time; each stage of LDS holds BM + BN rows of 128
+// bytes, unpadded, with the 16-byte chunk c of row r stored at chunk c ^ ((r/2) % 8)
+// so that the 32 rows a fragment read touches fall in distinct banks. Global tiles
+// go straight to LDS with global_load_lds_dwordx4 (no staging registers): lane l
+// of a load instruction fills bytes 16 l of the wavefront's 1 KB slice, and is
+// given the global address of the chunk that belongs there. NSTG stages rotate;
+// AHEAD of them are in flight. With LATE the stage refilled after the barrier of
+// K-step t is the one read during step t-1 (no LDS wait before the barrier);
+// otherwise it is the one just read (deeper prefetch, an LDS wait first).
+//
+// Fragment reads of the next 16-wide K slice are issued in the middle of the
+// current slice's MFMAs; the first slice of K-step t+1 is read right after the
+// barrier that publishes it.
+template <int BM, int BN, int WM, int WN, int NSTG, bool LATE, int EPI, bool SPLIT>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K,
+                 int k_chunk, int splits, EpiArgs epi, float* __restrict__ part) {
+  constexpr int NW = (BM / WM) * (BN / WN);
+  constexpr int NT = NW * 64;
+  constexpr int WAVES_N = BN / WN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int ROWB = 128;                        // LDS bytes per tile row (64 bf16)
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int LPA = BM * 8 / NT, LPB = BN * 8 / NT, LPT = LPA + LPB;
+  constexpr int AHEAD = LATE ? NSTG - 1 : NSTG;   // stages in flight
+  constexpr int RD_AT = (TM * TN) / 2;             // fragment reads after this many MFMAs
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % WM == 0 && BN % WN == 0, "tile shape");
+  static_assert(LPA >= 1 && LPB >= 1 && LPA * NT == BM * 8 && LPB * NT == BN * 8, "load split");
+  static_assert(AHEAD >= 2 && (AHEAD - 1) * LPT < 64, "pipeline depth");
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16* sA = (bf16*)smem;                        // [2][BM][LS]
-  bf16* sB = sA + 2 * BM * LS;                   // [2][BN][LS]
 
   const int MT = (M + BM - 1) / BM;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -128,75 +167,52 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
   const int rest = bid / MT;
   const int kz = rest % splits;
   const int nt = rest / splits;
-  const int m0 = mt * BM;
-  const int NOUT = DUAL ? BN / 2 : BN;           // output columns per workgroup
-  const int n0 = nt * NOUT;                      // first output column (B row for non-dual)
+  const int m0 = mt * BM, n0 = nt * BN;
   const int kbeg = kz * k_chunk;
-  const int nk = k_chunk / BKT;
+  const int nk = k_chunk / 64;
 
-  const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-  const bf16* a_src[A_VECS];
-  int a_lds[A_VECS];
+  // per-lane global source of each direct-to-LDS load (rows past M / N clamp to the
+  // last row; their products land in rows / columns the epilogue skips)
+  const bf16* ga[LPA];
+  const bf16* gb[LPB];
 #pragma unroll
-  for (int i = 0; i < A_VECS; ++i) {
-    const int v = tid + i * NT;
-    const int r = v / CPR, kv = v % CPR;
-    a_src[i] = A + (int64_t)min(m0 + r, M - 1) * K + kbeg + kv * 8;
-    a_lds[i] = r * LS + kv * 8;
+  for (int i = 0; i < LPA; ++i) {
+    const int q = (i * NW + wave) * 64 + lane;
+    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+    ga[i] = A + (int64_t)min(m0 + r, M - 1) * K + kbeg + c * 8;
   }
-  const bf16* b_src[B_VECS];
-  int b_lds[B_VECS];
 #pragma unroll
-  for (int i = 0; i < B_VECS; ++i) {
-    const int v = tid + i * NT;
-    const int r = v / CPR, kv = v % CPR;
-    int grow;
-    const bf16* mat = B;
-    if (DUAL) {
-      const bool up = r >= BN / 2;
-      mat = up ? B2 : B;
-      grow = n0 + (up ? r - BN / 2 : r);
-    } else {
-      grow = n0 + r;
-    }
-    b_src[i] = mat + (int64_t)min(grow, N - 1) * K + kbeg + kv * 8;
-    b_lds[i] = r * LS + kv * 8;
+  for (int i = 0; i < LPB; ++i) {
+    const int q = (i * NW + wave) * 64 + lane;
+    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+    gb[i] = B + (int64_t)min(n0 + r, N - 1) * K + kbeg + c * 8;
   }
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    unsigned char* base = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < LPA; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(ga[i] + kt * 64),
+                                       (lds_void_t*)(base + (i * NW + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < LPB; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(gb[i] + kt * 64),
+                                       (lds_void_t*)(base + BM * ROWB + (i * NW + wave) * 1024), 16, 0,
+                                       0);
+  };
 
-  // D register sets of prefetched tiles: the global loads of K-step k+D are in
-  // flight while step k computes, so D steps of MFMA work cover the load latency
-  constexpr int D = STAGES;
-  v4u ra[D][A_VECS], rb[D][B_VECS];
-#define EC_GLOAD(KT, XA, XB)                                                          \
-  do {                                                                                \
-    _Pragma("unroll") for (int i_ = 0; i_ < A_VECS; ++i_)                             \
-      XA[i_] = *reinterpret_cast<const v4u*>(a_src[i_] + (KT) * BKT);               \
-    _Pragma("unroll") for (int i_ = 0; i_ < B_VECS; ++i_)                             \
-      XB[i_] = *reinterpret_cast<const v4u*>(b_src[i_] + (KT) * BKT);               \
-  } while (0)
-#define EC_SSTORE(BUF, XA, XB)                                                        \
-  do {                                                                                \
-    bf16* a_ = sA + (BUF) * BM * LS;                                                  \
-    bf16* b_ = sB + (BUF) * BN * LS;                                                  \
-    _Pragma("unroll") for (int i_ = 0; i_ < A_VECS; ++i_)                             \
-      *reinterpret_cast<v4u*>(a_ + a_lds[i_]) = XA[i_];                             \
-    _Pragma("unroll") for (int i_ = 0; i_ < B_VECS; ++i_)                             \
-      *reinterpret_cast<v4u*>(b_ + b_lds[i_]) = XB[i_];                             \
-  } while (0)
-
-  int brow[TN];
+  // fragment addresses: A/B operand of lane = row lane%32 of the tile, K chunk
+  // 2*kk + lane/32; the swizzle term depends on the row's bits 1..3 only
+  const int lrow = lane % 32, hi = lane / 32;
+  const int sw16 = (((lrow >> 1) & 7) ^ hi) * 16;
+  const int a_row = (wm * WM + lrow) * ROWB;
+  const int b_row = BM * ROWB + (wn * WN + lrow) * ROWB;
+  int koff[4];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    if (PAIRED) {
-      const int jj = j % (TN / 2);
-      brow[j] = (j < TN / 2 ? 0 : BN / 2) + wn * (WN / 2) + 32 * jj;
-    } else {
-      brow[j] = wn * WN + 32 * j;
-    }
-  }
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = sw16 ^ (32 * kk);
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -206,142 +222,164 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int lrow = lane % 32, lk = 8 * (lane / 32);
-  auto compute = [&](int buf) __attribute__((always_inline)) {
-    const bf16* a = sA + buf * BM * LS;
-    const bf16* b = sB + buf * BN * LS;
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto rdfrag = [&](int stage, int kk, int slot) __attribute__((always_inline)) {
+    const unsigned char* base = smem + stage * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < BKT / 16; ++kk) {
-      bf16x8 fa[TM], fb[TN];
+    for (int i = 0; i < TM; ++i)
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(base + a_row + i * 32 * ROWB + koff[kk]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(a + (wm * WM + 32 * i + lrow) * LS + kk * 16 + lk);
+    for (int j = 0; j < TN; ++j)
+      fb[slot][j] = *reinterpret_cast<const bf16x8*>(base + b_row + j * 32 * ROWB + koff[kk]);
+  };
+  // MFMAs on fragment slot ms; the reads of (stage, kk) into slot rs go after RD_AT of them
+  auto slice = [&](int ms, int stage, int kk, int rs) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(b + (brow[j] + lrow) * LS + kk * 16 + lk);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < TM * TN; ++q) {
+      if (q == RD_AT) {
+        __builtin_amdgcn_sched_barrier(0);
+        rdfrag(stage, kk, rs);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int i = q / TN, j = q % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ms][i], fb[ms][j], acc[i][j], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
 #pragma unroll
-  for (int j = 0; j < D; ++j)
-    if (j < nk) EC_GLOAD(j, ra[j], rb[j]);
-  EC_SSTORE(0, ra[0], rb[0]);
-  if (D < nk) EC_GLOAD(D, ra[0], rb[0]);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += D) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int k = kt + j;
-      if (k < nk) {
-        compute(k & 1);
-        if (k + 1 < nk) {
-          EC_SSTORE((k + 1) & 1, ra[(j + 1) % D], rb[(j + 1) % D]);
-          if (k + 1 + D < nk) EC_GLOAD(k + 1 + D, ra[(j + 1) % D], rb[(j + 1) % D]);
-        }
-        __syncthreads();
-      }
+  for (int st = 0; st < AHEAD; ++st)
+    if (st < nk) issue(st, st);
+  if (nk >= AHEAD) wait_vmcnt<(AHEAD - 1) * LPT>(); else wait_vmcnt<0>();
+  lds_stage_barrier();
+  rdfrag(0, 0, 0);
+
+  for (int t = 0; t < nk; ++t) {
+    const int stage = t % NSTG;
+    slice(0, stage, 1, 1);
+    slice(1, stage, 2, 0);
+    slice(0, stage, 3, 1);
+    if (t + 1 < nk) {
+      if (!LATE) wait_lgkmcnt0();
+      // this lane's loads of step t+1 have landed once at most the later steps'
+      // (t+2 .. min(t+AHEAD-1, nk-1)) are outstanding
+      if (t + AHEAD - 1 < nk) wait_vmcnt<(AHEAD - 2) * LPT>(); else wait_vmcnt<0>();
+      lds_stage_barrier();
+      if (t + AHEAD < nk) issue(t + AHEAD, (t + AHEAD) % NSTG);
     }
+    // on the last step the read of stage (t+1) % NSTG stays inside LDS and is unused
+    slice(1, (t + 1) % NSTG, 0, 0);
   }
-#undef EC_GLOAD
-#undef EC_SSTORE
 
   // ---------------------------------------------------------------- epilogue
-  // acc[i][j][v]: row = m0 + wm*WM + 32i + 8(v/4) + 4(lane/32) + v%4, column lane%32 of tile j
-  const int rbase = m0 + wm * WM + 4 * (lane / 32);
+  // acc[i][j][v]: row m0 + wm*WM + 32i + 8(v/4) + 4(lane/32) + v%4, column
+  // n0 + wn*WN + 32j + lane%32 (a packed column for the paired epilogues)
+  const int rbase = m0 + wm * WM + 4 * hi;
   if (SPLIT) {
-    const int ncols = DUAL ? 2 * N : N;
-    float* dst = part + (int64_t)kz * M * ncols;
+    float* dst = part + (int64_t)kz * M * N;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        int col;
-        if (DUAL) {
-          const int jj = j % (TN / 2);
-          col = (j < TN / 2 ? 0 : N) + n0 + wn * (WN / 2) + 32 * jj + lrow;
-        } else {
-          col = n0 + brow[j] + lrow;
-        }
+        const int col = n0 + wn * WN + 32 * j + lrow;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = rbase + 32 * i + 8 * (v / 4) + (v % 4);
-          if (m < M) dst[(int64_t)m * ncols + col] = acc[i][j][v];
+          if (m < M && col < N) dst[(int64_t)m * N + col] = acc[i][j][v];
+        }
+      }
+    return;
+  }
+  if (EPI == EPI_QKV) {
+    // per column tile: this lane's output column, section and rotary index
+    const int d = epi.d_model, D = epi.head_dim, half = D / 2;
+    int hcol[TN], cidx[TN], sec[TN];
+    bool second[TN], colok[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int pc = n0 + wn * WN + 32 * j + lrow;
+      const int hb = pc - pc % D, p = pc - hb, u = p & 31;
+      cidx[j] = (p >> 5) * 16 + (u & 15);
+      second[j] = u >= 16;
+      sec[j] = hb / d;
+      hcol[j] = hb % d + cidx[j] + (second[j] ? half : 0);
+      colok[j] = pc < N;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = rbase + 32 * i + 8 * (v / 4) + (v % 4);
+        const int pos = m < M ? epi.rows[m] : -1;
+        const bool pos_ok = pos >= 0 && pos < epi.seq_len;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const float x = acc[i][j][v];
+          const float y = swap16(x);  // every lane takes part in the swizzle
+          if (m >= M || !colok[j]) continue;
+          float out = x;
+          if (sec[j] < 2 && pos_ok) {
+            const float cs = epi.rope_cos[(int64_t)pos * half + cidx[j]];
+            const float sn = epi.rope_sin[(int64_t)pos * half + cidx[j]];
+            // first half: x1 cos - x2 sin; second half: x1 sin + x2 cos (x1 = partner)
+            out = second[j] ? y * sn + x * cs : x * cs - y * sn;
+          }
+          if (sec[j] == 0) ((bf16*)epi.out)[(int64_t)m * d + hcol[j]] = (bf16)out;
+          else if (pos_ok)
+            ((bf16*)(sec[j] == 1 ? epi.k_cache : epi.v_cache))[(int64_t)pos * d + hcol[j]] = (bf16)out;
         }
       }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = rbase + 32 * i + 8 * (v / 4) + (v % 4);
-      if (m >= M) continue;
-      if (PAIRED) {
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WN + 32 * j + lrow;
 #pragma unroll
-        for (int j = 0; j < TN / 2; ++j) {
-          const float x1 = acc[i][j][v], x2 = acc[i][j + TN / 2][v];
-          const int col = n0 + wn * (WN / 2) + 32 * j + lrow;
-          if (EPI == EPI_QKV) {
-            epi_qkv_pair<bf16>(epi, m, col, x1, x2);
-          } else {
-            epi_swiglu<bf16>(epi, m, col, x1, x2);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn * WN + 32 * j + lrow;
-          if (col < N) epi_single<bf16>(epi, m, col, acc[i][j][v]);
+      for (int v = 0; v < 16; ++v) {
+        const int m = rbase + 32 * i + 8 * (v / 4) + (v % 4);
+        const float x = acc[i][j][v];
+        if (EPI == EPI_SWIGLU) {
+          const float y = swap16(x);  // every lane takes part in the swizzle
+          if (m < M && col < N && (lrow & 16) == 0) epi_swiglu<bf16>(epi, m, (col >> 5) * 16 + (col & 15), x, y);
+        } else if (m < M && col < N) {
+          epi_single<bf16>(epi, m, col, x);
         }
       }
     }
-  }
 }
 
 // -------------------------------------------------------------------- split-K reduction
-// One thread per output unit; sums the S partials in order, then the epilogue.
-template <typename T>
+// Partials part[S][M][N] over the packed columns of the bf16 kernel. One thread per
+// output unit sums the S partials in order (deterministic), then the epilogue:
+// QKV and SwiGLU units are the (pc, pc + 16) pairs of each 32-column group.
 __global__ void __launch_bounds__(kThreads)
-splitk_epilogue_kernel(const float* __restrict__ part, int S, int M, int N, int kind,
-                       EpiArgs epi) {
+splitk_epilogue_kernel(const float* __restrict__ part, int S, int M, int N, int kind, EpiArgs epi) {
   const int64_t t = blockIdx.x * (int64_t)kThreads + threadIdx.x;
-  if (kind == EPI_QKV) {
-    // units: (m, pair) with pair over [0, 3d/2): head-major, c < D/2
-    const int half = epi.head_dim / 2;
-    const int64_t units_per_row = N / 2;
-    if (t >= (int64_t)M * units_per_row) return;
-    const int m = (int)(t / units_per_row);
-    const int u = (int)(t % units_per_row);
-    const int head = u / half, c = u % half;
-    const int col = head * epi.head_dim + c;
+  if (kind == EPI_QKV || kind == EPI_SWIGLU) {
+    const int64_t upr = N / 2;
+    if (t >= (int64_t)M * upr) return;
+    const int m = (int)(t / upr), u = (int)(t % upr);
+    const int pc = (u >> 4) * 32 + (u & 15);
     float x1 = 0.f, x2 = 0.f;
     for (int s = 0; s < S; ++s) {
       const float* p = part + ((int64_t)s * M + m) * N;
-      x1 += p[col];
-      x2 += p[col + half];
+      x1 += p[pc];
+      x2 += p[pc + 16];
     }
-    epi_qkv_pair<T>(epi, m, col, x1, x2);
-  } else if (kind == EPI_SWIGLU) {
-    if (t >= (int64_t)M * N) return;
-    const int m = (int)(t / N), col = (int)(t % N);
-    float g = 0.f, u = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float* p = part + ((int64_t)s * M + m) * (2 * N);
-      g += p[col];
-      u += p[N + col];
+    if (kind == EPI_SWIGLU) {
+      epi_swiglu<bf16>(epi, m, u, x1, x2);
+    } else {
+      const int hb = pc - pc % epi.head_dim, pp = pc - hb;
+      epi_qkv_pair<bf16>(epi, m, hb + (pp >> 5) * 16 + (pp & 15), x1, x2);
     }
-    epi_swiglu<T>(epi, m, col, g, u);
   } else {
     if (t >= (int64_t)M * N) return;
     const int m = (int)(t / N), col = (int)(t % N);
     float x = 0.f;
     for (int s = 0; s < S; ++s) x += part[((int64_t)s * M + m) * N + col];
-    epi_single<T>(epi, m, col, x);
+    epi_single<bf16>(epi, m, col, x);
   }
 }
 
@@ -390,71 +428,125 @@ gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
   }
 }
 
-// -------------------------------------------------------------------- host-side planning
-struct Plan {
-  int BM, BN, S, k_chunk, MT, NT;
-  bool skinny;  // M <= 64: 64-row tiles
-};
+// -------------------------------------------------------------------- weight packing
+// dst row pr <- src row of the packed layouts described above (one workgroup per row)
+__global__ void __launch_bounds__(kThreads)
+pack_rows_kernel(const unsigned char* __restrict__ a, const unsigned char* __restrict__ b,
+                 unsigned char* __restrict__ dst, int rows, int row_bytes, int mode, int head_dim) {
+  const int pr = blockIdx.x;
+  if (pr >= rows) return;
+  const unsigned char* src;
+  const int g = (pr & 31) >> 4, l = pr & 15, grp = pr >> 5;
+  if (mode == 0) {  // rotary: within each head
+    const int hb = pr - pr % head_dim, p = pr - hb;
+    const int c = (p >> 5) * 16 + l + (g ? head_dim / 2 : 0);
+    src = a + (int64_t)(hb + c) * row_bytes;
+  } else {          // gate / up interleave
+    src = (g ? b : a) + (int64_t)(grp * 16 + l) * row_bytes;
+  }
+  unsigned char* out = dst + (int64_t)pr * row_bytes;
+  if (row_bytes % 16 == 0) {
+    for (int i = threadIdx.x; i < row_bytes / 16; i += kThreads)
+      reinterpret_cast<v4u*>(out)[i] = reinterpret_cast<const v4u*>(src)[i];
+  } else {
+    for (int i = threadIdx.x; i < row_bytes; i += kThreads) out[i] = src[i];
+  }
+}
 
+// -------------------------------------------------------------------- host-side planning
 constexpr int kCUs = 256;
 
-// Tile choice, measured on MI355X for the projection shapes of the 2k / 4k models:
-// 128x128 workgroup tiles with 8 or 16 wavefronts (two or four per SIMD hide the LDS
-// and global latency); 64x128 tiles when M <= 64 (LM head over the candidates, skinny
-// skip steps). K is split only when the tiles cannot give every CU one workgroup.
-Plan plan_bf16(int M, int N, int K, int kind) {
-  Plan p{};
-  const bool dual = kind == EPI_SWIGLU;
-  p.skinny = M <= 64 && kind != EPI_QKV && kind != EPI_SWIGLU;
-  p.BM = p.skinny ? 64 : 128;
-  p.BN = 128;
-  const int nout = dual ? p.BN / 2 : p.BN;
-  p.MT = (M + p.BM - 1) / p.BM;
-  p.NT = (N + nout - 1) / nout;
-  const int tiles = p.MT * p.NT;
-  int S = 1;
+enum TileCfg { T256x192, T256x128, T128x128, T64x128, kNumTileCfg };
+struct TileInfo {
+  int BM, BN;
+  double eff;  // sustained MFMA rate relative to 4 TFLOP/s per CU, measured on MI355X
+};
+constexpr TileInfo kTile[kNumTileCfg] = {
+    {256, 192, 1.03}, {256, 128, 0.99}, {128, 128, 0.88}, {64, 128, 0.70}};
+
+struct Plan {
+  TileCfg cfg;
+  int S, k_chunk, MT, NT;
+};
+
+// Tile choice by a cost model fitted to MI355X measurements of the projection
+// shapes: time = waves x per-tile time, waves = ceil(tiles * S / 256), per-tile
+// time = 2 BM BN (K / S) / (eff x 4 TFLOP/s), plus, for split K, the partials'
+// round trip through HBM and one more launch. Larger tiles carry more MFMA work
+// per staged byte; smaller ones fill the 256 CUs at skinny M (skip steps, the LM
+// head over the candidates). K is split only when a configuration's tiles cover
+// fewer than half the CUs.
+Plan plan_bf16(int M, int N, int K) {
+  Plan best{};
+  double best_us = 1e300;
   const int nk = K / BK;
-  while (tiles * S < kCUs && S < 8 && nk % (2 * S) == 0 && nk / (2 * S) >= 8) S *= 2;
-  p.S = S;
-  p.k_chunk = K / S;
-  return p;
+  for (int c = 0; c < kNumTileCfg; ++c) {
+    const TileInfo& t = kTile[c];
+    if (M <= 64 && c != T64x128) continue;
+    if (M <= 128 && (c == T256x192 || c == T256x128)) continue;
+    const int MT = (M + t.BM - 1) / t.BM, NT = (N + t.BN - 1) / t.BN;
+    const int64_t tiles = (int64_t)MT * NT;
+    int S = 1;
+    if (tiles < kCUs / 2)
+      while (tiles * S * 2 <= kCUs && S < 8 && nk % (2 * S) == 0 && nk / (2 * S) >= 8) S *= 2;
+    const int64_t waves = (tiles * S + kCUs - 1) / kCUs;
+    double us = (double)waves * 2.0 * t.BM * t.BN * (double)(K / S) / (t.eff * 4e6);
+    if (S > 1) us += (double)S * M * N * 8.0 / 5e6 + 3.0;
+    if (us < best_us) {
+      best_us = us;
+      best.cfg = (TileCfg)c;
+      best.MT = MT;
+      best.NT = NT;
+      best.S = S;
+      best.k_chunk = K / S;
+    }
+  }
+  return best;
 }
 
-template <int BM, int BN, int WM, int WN, int BKT, int STAGES, int EPI, bool DUAL>
-ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, const bf16* B2, int M, int N,
-                      int K, const EpiArgs& epi, float* part, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, int NSTG, bool LATE, int EPI>
+ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, int M, int N, int K,
+                      const EpiArgs& epi, float* part, hipStream_t s) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  const size_t lds = (size_t)2 * (BM + BN) * (BKT + 8) * sizeof(bf16);
+  constexpr size_t lds = (size_t)NSTG * (BM + BN) * 128;
+  static_assert(lds <= 160 * 1024, "LDS budget");
   const int grid = p.MT * p.NT * p.S;
-  if (p.S > 1) {
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, BKT, STAGES, EPI, DUAL, true>;
+  auto run = [&](auto kern) -> ec_status {
     static bool attr = false;
     if (!attr) {
       EC_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
       attr = true;
     }
-    kern<<<grid, NT, lds, s>>>(A, B, B2, M, N, K, p.k_chunk, p.S, epi, part);
-  } else {
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, BKT, STAGES, EPI, DUAL, false>;
-    static bool attr = false;
-    if (!attr) {
-      EC_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-      attr = true;
-    }
-    kern<<<grid, NT, lds, s>>>(A, B, B2, M, N, K, p.k_chunk, p.S, epi, part);
-  }
-  EC_CHECK_LAUNCH("gemm_bf16_kernel");
-  return EC_OK;
+    kern<<<grid, NT, lds, s>>>(A, B, M, N, K, p.k_chunk, p.S, epi, part);
+    EC_CHECK_LAUNCH("gemm_bf16_kernel");
+    return EC_OK;
+  };
+  if (p.S > 1) return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, true>);
+  return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, false>);
 }
+
+template <int EPI>
+ec_status launch_cfg(const Plan& p, const bf16* A, const bf16* B, int M, int N, int K,
+                     const EpiArgs& epi, float* part, hipStream_t s) {
+  switch (p.cfg) {
+    case T256x192: return launch_bf16<256, 192, 64, 96, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
+    case T256x128: return launch_bf16<256, 128, 64, 64, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
+    case T128x128: return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+    default: return launch_bf16<64, 128, 32, 32, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+  }
+}
+
+// B rows of the bf16 kernel: the packed gate/up matrix has 2F rows for F outputs
+int b_rows(int N, int kind) { return kind == EPI_SWIGLU ? 2 * N : N; }
 
 }  // namespace
 
 size_t gemm_splitk_ws_bytes(int M, int N, int K, int kind, bool is_bf16) {
   if (!is_bf16 || M <= 0) return 0;
-  Plan p = plan_bf16(M, N, K, kind);
+  const int NB = b_rows(N, kind);
+  Plan p = plan_bf16(M, NB, K);
   if (p.S <= 1) return 0;
-  const size_t ncols = kind == EPI_SWIGLU ? 2 * (size_t)N : (size_t)N;
-  return (size_t)p.S * M * ncols * sizeof(float);
+  return (size_t)p.S * M * NB * sizeof(float);
 }
 
 ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M, int N, int K,
@@ -470,12 +562,13 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
     return EC_OK;
   }
   EC_REQUIRE(K % BK == 0, EC_ERR_UNSUPPORTED, "gemm: K=%d not a multiple of %d", K, BK);
-  Plan p = plan_bf16(M, N, K, kind);
   if (kind == EPI_QKV)
-    EC_REQUIRE(epi.head_dim == 128 && N % 128 == 0, EC_ERR_UNSUPPORTED,
-               "gemm: bf16 QKV needs head_dim 128");
+    EC_REQUIRE(epi.head_dim % 32 == 0 && N % epi.head_dim == 0, EC_ERR_UNSUPPORTED,
+               "gemm: packed QKV needs head_dim %% 32 == 0");
   if (kind == EPI_SWIGLU)
-    EC_REQUIRE(N % 128 == 0, EC_ERR_UNSUPPORTED, "gemm: bf16 SwiGLU needs F %% 128 == 0");
+    EC_REQUIRE(N % 16 == 0, EC_ERR_UNSUPPORTED, "gemm: packed SwiGLU needs F %% 16 == 0");
+  const int NB = b_rows(N, kind);
+  Plan p = plan_bf16(M, NB, K);
   float* part = nullptr;
   if (p.S > 1) {
     const size_t need = gemm_splitk_ws_bytes(M, N, K, kind, true);
@@ -485,32 +578,36 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
   }
   const bf16* a = (const bf16*)A;
   const bf16* b = (const bf16*)B;
-  const bf16* b2 = (const bf16*)B2;
   ec_status st;
   switch (kind) {
-    case EPI_QKV:
-      st = launch_bf16<128, 128, 32, 64, 64, 3, EPI_QKV, false>(p, a, b, b2, M, N, K, epi, part, s);
-      break;
-    case EPI_SWIGLU:
-      st = launch_bf16<128, 128, 32, 64, 64, 2, EPI_SWIGLU, true>(p, a, b, b2, M, N, K, epi, part, s);
-      break;
-    case EPI_RESID:
-      st = p.skinny
-               ? launch_bf16<64, 128, 32, 32, 64, 3, EPI_RESID, false>(p, a, b, b2, M, N, K, epi, part, s)
-               : launch_bf16<128, 128, 32, 32, 64, 2, EPI_RESID, false>(p, a, b, b2, M, N, K, epi, part, s);
-      break;
-    default:
-      st = p.skinny
-               ? launch_bf16<64, 128, 32, 32, 64, 3, EPI_STORE, false>(p, a, b, b2, M, N, K, epi, part, s)
-               : launch_bf16<128, 128, 32, 64, 64, 3, EPI_STORE, false>(p, a, b, b2, M, N, K, epi, part, s);
-      break;
+    case EPI_QKV: st = launch_cfg<EPI_QKV>(p, a, b, M, NB, K, epi, part, s); break;
+    case EPI_SWIGLU: st = launch_cfg<EPI_SWIGLU>(p, a, b, M, NB, K, epi, part, s); break;
+    case EPI_RESID: st = launch_cfg<EPI_RESID>(p, a, b, M, NB, K, epi, part, s); break;
+    default: st = launch_cfg<EPI_STORE>(p, a, b, M, NB, K, epi, part, s); break;
   }
   if (st != EC_OK) return st;
   if (p.S > 1) {
-    const int64_t units = (kind == EPI_QKV) ? (int64_t)M * (N / 2) : (int64_t)M * N;
+    const int64_t units = (kind == EPI_QKV || kind == EPI_SWIGLU) ? (int64_t)M * (NB / 2) : (int64_t)M * NB;
     const int blocks = (int)((units + kThreads - 1) / kThreads);
-    splitk_epilogue_kernel<bf16><<<blocks, kThreads, 0, s>>>(part, p.S, M, N, kind, epi);
+    splitk_epilogue_kernel<<<blocks, kThreads, 0, s>>>(part, p.S, M, NB, kind, epi);
     EC_CHECK_LAUNCH("splitk_epilogue_kernel");
+  }
+  return EC_OK;
+}
+
+ec_status pack_weights(int elem_bytes, int d, int head_dim, int F, const void* wqkv,
+                       const void* w_gate, const void* w_up, void* wqkv_packed,
+                       void* gateup_packed, hipStream_t s) {
+  const int row_bytes = d * elem_bytes;
+  if (wqkv_packed) {
+    pack_rows_kernel<<<3 * d, kThreads, 0, s>>>((const unsigned char*)wqkv, nullptr,
+                                                 (unsigned char*)wqkv_packed, 3 * d, row_bytes, 0, head_dim);
+    EC_CHECK_LAUNCH("pack_rows_kernel");
+  }
+  if (gateup_packed) {
+    pack_rows_kernel<<<2 * F, kThreads, 0, s>>>((const unsigned char*)w_gate, (const unsigned char*)w_up,
+                                                 (unsigned char*)gateup_packed, 2 * F, row_bytes, 1, head_dim);
+    EC_CHECK_LAUNCH("pack_rows_kernel");
   }
   return EC_OK;
 }

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define EC_VERSION 10000            /* 1.0.0 */
+#define EC_VERSION 10100            /* 1.1.0 */
 #define EC_MAX_TOKENS_PER_STEP 64   /* upper bound on tokens decoded per step */
 #define EC_MAX_LAYERS 256
 
@@ -133,13 +133,25 @@ ec_status ec_partial_attn(const void* q, const void* k_cache, const void* v_cach
  * RMSNorm, SwiGLU MLP (silu(gate) * up, then down) + residual; final RMSNorm
  * and an untied LM head. Logits of position p come from row p.
  * ---------------------------------------------------------------------- */
+/* Weight layout of the QKV and gate/up matrices.
+ * EC_LAYOUT_PLAIN  (fp32 models): wqkv [3d, d] with rows [0,d) q, [d,2d) k,
+ *   [2d,3d) v in natural order; w_gate and w_up [F, d].
+ * EC_LAYOUT_PACKED (bf16 models): the layout the MFMA kernels read, built from
+ *   the plain one by ec_pack_weights. wqkv keeps [3d, d] but inside each head's
+ *   head_dim rows, group g of 32 rows holds rows 16g .. 16g+15 followed by their
+ *   rotary partners head_dim/2 + 16g .. head_dim/2 + 16g + 15. w_gate points at
+ *   a [2F, d] matrix whose group g of 32 rows holds gate rows 16g .. 16g+15
+ *   followed by up rows 16g .. 16g+15; w_up is unused (may be NULL).
+ * The math is unchanged: the packed matrices hold the same rows, reordered. */
+typedef enum ec_weight_layout { EC_LAYOUT_PLAIN = 0, EC_LAYOUT_PACKED = 1 } ec_weight_layout;
+
 typedef struct ec_layer_weights {
   const void* attn_norm; /* [d] */
-  const void* wqkv;      /* [3d, d]: rows [0,d) q, [d,2d) k, [2d,3d) v */
+  const void* wqkv;      /* [3d, d]: q | k | v rows (packed order for EC_LAYOUT_PACKED) */
   const void* wo;        /* [d, d] */
   const void* mlp_norm;  /* [d] */
-  const void* w_gate;    /* [F, d] */
-  const void* w_up;      /* [F, d] */
+  const void* w_gate;    /* PLAIN: [F, d] gate; PACKED: [2F, d] gate/up interleave */
+  const void* w_up;      /* PLAIN: [F, d] up; PACKED: unused */
   const void* w_down;    /* [d, F] */
 } ec_layer_weights;
 
@@ -155,7 +167,18 @@ typedef struct ec_model_desc {
   const float* rope_cos;           /* [rope_max_pos, head_dim/2] fp32, from ec_rope_table */
   const float* rope_sin;           /* same shape */
   int32_t rope_max_pos;            /* >= seq_len */
+  int32_t weight_layout;           /* ec_weight_layout: PACKED for bf16, PLAIN for fp32 */
 } ec_model_desc;
+
+/* ec_pack_weights -- build the EC_LAYOUT_PACKED matrices of one layer from the
+ * plain ones (device to device, out of place, enqueued on `stream`).
+ * wqkv [3d, d] -> wqkv_packed [3d, d]; w_gate, w_up [F, d] -> gateup_packed
+ * [2F, d]. Either output may be NULL to skip it (its inputs are then ignored).
+ * Needs head_dim % 32 == 0 and d % head_dim == 0 for wqkv, F % 16 == 0 for gate/up.
+ * Errors: EC_ERR_DTYPE, EC_ERR_ARG (null input of a requested output, bad sizes). */
+ec_status ec_pack_weights(ec_dtype dtype, int32_t d_model, int32_t head_dim, int32_t ffn_dim,
+                          const void* wqkv, const void* w_gate, const void* w_up,
+                          void* wqkv_packed, void* gateup_packed, void* stream);
 
 typedef struct ec_cache_desc {
   uint32_t struct_size;

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_error_string(lib):
-    assert lib.ec_version() == 10000
+    assert lib.ec_version() == 10100
     assert isinstance(lib.ec_last_error(), bytes)
 
 
@@ -60,6 +60,7 @@ def _model_desc(dtype=_lib.EC_BF16, d=4096, H=32, Dh=128, F=12288, V=126464, n_l
     m.embed = m.final_norm = m.lm_head = m.rope_cos = m.rope_sin = 0x1000
     m.layers = C.cast(lw, C.POINTER(_lib.ec_layer_weights))
     m.rope_max_pos = 4096
+    m.weight_layout = _lib.EC_LAYOUT_PACKED if dtype == _lib.EC_BF16 else _lib.EC_LAYOUT_PLAIN
     return m, lw
 
 
@@ -89,6 +90,11 @@ def test_unsupported_shapes_and_bad_params_are_rejected(lib):
     assert lib.ec_step_workspace_size(C.byref(m2), C.byref(bad)) == 0
     bad = _params(tau=math.nan)
     assert lib.ec_step_workspace_size(C.byref(m2), C.byref(bad)) == 0
+    # bf16 models must come in the packed weight layout
+    m3, _keep3 = _model_desc()
+    m3.weight_layout = _lib.EC_LAYOUT_PLAIN
+    assert lib.ec_step_workspace_size(C.byref(m3), C.byref(_params())) == 0
+    assert b"weight_layout" in lib.ec_last_error()
 
 
 def test_argument_errors_return_before_any_gpu_work(lib):
@@ -105,6 +111,12 @@ def test_argument_errors_return_before_any_gpu_work(lib):
     m, _keep = _model_desc()
     assert lib.ec_forward(C.byref(m), None, None, None, 0, None, 0, None, None, None, 0, None) == E.EC_ERR_ARG
     assert lib.ec_rope_table(None, None, 16, 128, 10000.0, None) == E.EC_ERR_ARG
+    # packing: bad dtype, missing inputs, sizes the layout cannot take
+    assert lib.ec_pack_weights(5, 256, 128, 512, None, None, None, None, None, None) == E.EC_ERR_DTYPE
+    assert lib.ec_pack_weights(E.EC_BF16, 256, 128, 512, None, None, None, 0x1000, None, None) == E.EC_ERR_ARG
+    assert lib.ec_pack_weights(E.EC_BF16, 256, 48, 512, 0x1000, None, None, 0x1000, None, None) == E.EC_ERR_ARG
+    assert lib.ec_pack_weights(E.EC_BF16, 256, 128, 520, None, 0x1000, 0x1000, None, 0x1000, None) == E.EC_ERR_ARG
+    assert lib.ec_pack_weights(E.EC_BF16, 256, 128, 512, None, None, None, None, None, None) == E.EC_OK
     st = _lib.ec_state()
     st.struct_size = C.sizeof(_lib.ec_state)
     assert lib.ec_state_reset(C.byref(st), C.byref(_params()), None) == E.EC_ERR_ARG

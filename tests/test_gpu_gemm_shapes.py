@@ -1,0 +1,74 @@
+"""GPU parity of the bf16 MFMA GEMM paths at the 8B layer width, through ec_forward.
+
+One layer with d=4096, 32 heads of 128, SwiGLU width 12288 (the 8B-shaped
+model's projection shapes) and a small vocabulary, so the oracle forward
+stays fast. The row counts pick every tile configuration the GEMMs use:
+1024 rows (a refresh: 256x192 tiles for q|k|v and gate/up, 128x128 for the
+output and down projections), 300 rows (128x128, split K), 40 rows (64-row
+tiles, split K) and 17 rows (32-row tiles, split K). Bars as in the other
+forward tests: 2e-2 relative for hidden states, logits and cached K/V, argmax
+exact where the logit margin clears the gate.
+
+Also: ec_pack_weights moves exactly the rows its layout definition names.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.gpu_util import bf16_tensor
+from tests.test_gpu_forward import _compare, _setup
+
+pytestmark = pytest.mark.gpu
+
+WIDE = synth.ModelShape("wide", "bf16", 1, 4096, 32, 128, 12288, 1024)
+
+
+@pytest.mark.parametrize("n_rows", [1024, 300, 144, 40, 17])
+def test_forward_at_8b_layer_width(n_rows):
+    L = 1024
+    w, omm, dm, cache, oc = _setup(WIDE, L, seed=11, stale=n_rows < L)
+    rng = np.random.default_rng(12)
+    tokens = rng.integers(0, WIDE.vocab - 1, L).astype(np.int32)
+    rows = np.arange(L) if n_rows == L else np.sort(rng.choice(L, n_rows, replace=False))
+    out = rows[np.sort(rng.choice(len(rows), min(len(rows), 32), replace=False))]
+    _compare(WIDE, omm, dm, cache, oc, tokens, rows, out)
+
+
+def _packed_qkv_order(d, D):
+    """Row order of the packed q|k|v matrix: inside each head, group g of 32 rows is
+    first-half rows 16g..16g+15 then their rotary partners D/2 + 16g .. D/2 + 16g + 15."""
+    order = []
+    for hb in range(0, 3 * d, D):
+        for g in range(D // 32):
+            order += [hb + 16 * g + i for i in range(16)]
+            order += [hb + D // 2 + 16 * g + i for i in range(16)]
+    return np.array(order)
+
+
+@pytest.mark.parametrize("d,D,F,dtype", [(256, 128, 512, "bf16"), (4096, 128, 12288, "bf16"),
+                                         (256, 64, 1024, "f32")])
+def test_pack_weights_layout(d, D, F, dtype):
+    from entropy_guided_kv_amd import api
+    rng = np.random.default_rng(d + F)
+    mk = lambda r: rng.standard_normal((r, d)).astype(np.float32)
+    wqkv, wg, wu = mk(3 * d), mk(F), mk(F)
+    if dtype == "bf16":
+        dev = lambda a: bf16_tensor(synth.f32_to_bf16_bits(a))
+        host = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a))
+    else:
+        dev = lambda a: torch.from_numpy(a).cuda()
+        host = lambda a: a
+    shape = synth.ModelShape("p", dtype, 1, d, d // D, D, F, 16)
+    qp, gu = api.pack_weights(shape, dev(wqkv), dev(wg), dev(wu))
+    torch.cuda.synchronize()
+    got_q = qp.float().cpu().numpy()
+    got_gu = gu.float().cpu().numpy()
+    np.testing.assert_array_equal(got_q, host(wqkv)[_packed_qkv_order(d, D)])
+    exp_gu = np.empty((2 * F, d), np.float32)
+    for g in range(F // 16):
+        exp_gu[32 * g: 32 * g + 16] = host(wg)[16 * g: 16 * g + 16]
+        exp_gu[32 * g + 16: 32 * g + 32] = host(wu)[16 * g: 16 * g + 16]
+    np.testing.assert_array_equal(got_gu, exp_gu)
+    # a permutation: every plain row appears exactly once
+    assert sorted(_packed_qkv_order(d, D).tolist()) == list(range(3 * d))
