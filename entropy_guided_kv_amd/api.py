@@ -50,11 +50,12 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 # ---------------------------------------------------------------------- kernels
 def ec_entropy_max(logits: torch.Tensor, sel: Optional[torch.Tensor] = None, stream=None,
-                   workspace: Optional[torch.Tensor] = None):
+                   workspace: Optional[torch.Tensor] = None, out=None):
     """Per-row softmax entropy (nats), argmax, max-probability and E = max entropy over sel.
 
     logits: [rows, V] (row stride may exceed V), float32 or bfloat16, on the GPU.
-    Returns (entropy f32[rows], argmax i32[rows], maxprob f32[rows], emax f32[1]).
+    Returns (entropy f32[rows], argmax i32[rows], maxprob f32[rows], emax f32[1]); ``out``
+    may pass those four tensors in to be filled instead of allocated.
     """
     lib = load()
     _need_cuda(logits, sel)
@@ -62,10 +63,16 @@ def ec_entropy_max(logits: torch.Tensor, sel: Optional[torch.Tensor] = None, str
         raise ValueError("logits must be 2-D with unit column stride")
     rows, V = logits.shape
     dev = logits.device
-    H = torch.empty(rows, dtype=torch.float32, device=dev)
-    a = torch.empty(rows, dtype=torch.int32, device=dev)
-    c = torch.empty(rows, dtype=torch.float32, device=dev)
-    e = torch.empty(1, dtype=torch.float32, device=dev)
+    if out is not None:
+        H, a, c, e = out
+        if (H.numel() < rows or a.numel() < rows or c.numel() < rows or e.numel() < 1
+                or (H.dtype, a.dtype, c.dtype, e.dtype) != (torch.float32, torch.int32, torch.float32, torch.float32)):
+            raise ValueError("out: need float32[rows], int32[rows], float32[rows], float32[1]")
+    else:
+        H = torch.empty(rows, dtype=torch.float32, device=dev)
+        a = torch.empty(rows, dtype=torch.int32, device=dev)
+        c = torch.empty(rows, dtype=torch.float32, device=dev)
+        e = torch.empty(1, dtype=torch.float32, device=dev)
     if sel is not None:
         sel = sel.to(torch.int32).contiguous()
     ws_bytes = lib.ec_entropy_max_workspace_size(rows, V)

@@ -397,8 +397,9 @@ ec_status ec_entropy_max(const void* logits, ec_dtype dtype, int32_t rows, int32
     EC_REQUIRE(workspace && workspace_bytes >= need, EC_ERR_WORKSPACE,
                "ec_entropy_max: workspace %zu < %zu bytes", workspace_bytes, need);
   }
+  TScope t(EC_T_ENTROPY, (hipStream_t)stream, 0.0, (double)rows * vocab * esize(dtype));
   return ec::entropy(dtype, logits, rows, vocab, row_stride, sel, n_sel, entropy, argmax, maxprob, emax,
-                 workspace, workspace_bytes, (hipStream_t)stream);
+                     workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 ec_status ec_cache_scatter(void* k_cache, void* v_cache, int64_t seq_len, int32_t width,

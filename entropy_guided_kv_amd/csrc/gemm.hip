@@ -122,11 +122,6 @@ __device__ __forceinline__ void lds_stage_barrier() {
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-// value of lane ^ 16 (ds_swizzle bit mode, xor mask 0x10 within 32-lane groups)
-__device__ __forceinline__ float swap16(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
-}
-
 // C tile BM x BN from A[M, K] (row stride K) and B[N, K] (row stride K), bf16 in,
 // fp32 accumulate on v_mfma_f32_32x32x16_bf16. Wavefront tile WM x WN.
 //
@@ -272,82 +267,86 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   }
 
   // ---------------------------------------------------------------- epilogue
-  // acc[i][j][v]: row m0 + wm*WM + 32i + 8(v/4) + 4(lane/32) + v%4, column
-  // n0 + wn*WN + 32j + lane%32 (a packed column for the paired epilogues)
-  const int rbase = m0 + wm * WM + 4 * hi;
-  if (SPLIT) {
-    float* dst = part + (int64_t)kz * M * N;
+  // The accumulators go through LDS (each wavefront stages its own 32 x WN fp32
+  // slab, one 32-row MFMA slab at a time) so that every output is written as a
+  // row-contiguous 4-column vector: bf16 x4 stores for q / K / V / logits /
+  // SwiGLU, fp32 x4 read-modify-write for the residual, x4 partials for split K.
+  // A paired column's partner (packed column ^ 16) is read from the same slab.
+  wait_lgkmcnt0();
+  lds_stage_barrier();  // every wavefront is done with the staging buffers
+  constexpr int ES = WN + 4;                 // slab row stride (floats)
+  constexpr int C4 = WN / 4;                 // 4-column units per slab row
+  static_assert(NW * 32 * ES * 4 <= NSTG * STAGE, "epilogue slab exceeds the LDS tile buffers");
+  float* slab = reinterpret_cast<float*>(smem) + wave * 32 * ES;
+  const int d = epi.d_model, D = epi.head_dim, half = D / 2;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = n0 + wn * WN + 32 * j + lrow;
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = rbase + 32 * i + 8 * (v / 4) + (v % 4);
-          if (m < M && col < N) dst[(int64_t)m * N + col] = acc[i][j][v];
-        }
+      for (int v = 0; v < 16; ++v) slab[(8 * (v / 4) + 4 * hi + (v % 4)) * ES + 32 * j + lrow] = acc[i][j][v];
+    const int mrow = m0 + wm * WM + 32 * i;  // first output row of this slab
+    if (EPI == EPI_SWIGLU && !SPLIT) {
+      // units: (row, 4 gate columns); the up partner is 16 columns on
+      constexpr int UG = C4 / 2;
+#pragma unroll
+      for (int u = lane; u < 32 * UG; u += 64) {
+        const int r = u / UG, k = u % UG;
+        const int c = (k / 4) * 32 + (k % 4) * 4;
+        const int m = mrow + r, pc = n0 + wn * WN + c;
+        if (m >= M || pc >= N) continue;
+        const f32x4 g = *reinterpret_cast<const f32x4*>(slab + r * ES + c);
+        const f32x4 up = *reinterpret_cast<const f32x4*>(slab + r * ES + c + 16);
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)(silu(g[e]) * up[e]);
+        const int f = (pc >> 5) * 16 + (pc & 15);
+        *reinterpret_cast<bf16x4*>((bf16*)epi.out + (int64_t)m * epi.ldo + f) = o;
       }
-    return;
-  }
-  if (EPI == EPI_QKV) {
-    // per column tile: this lane's output column, section and rotary index
-    const int d = epi.d_model, D = epi.head_dim, half = D / 2;
-    int hcol[TN], cidx[TN], sec[TN];
-    bool second[TN], colok[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int pc = n0 + wn * WN + 32 * j + lrow;
-      const int hb = pc - pc % D, p = pc - hb, u = p & 31;
-      cidx[j] = (p >> 5) * 16 + (u & 15);
-      second[j] = u >= 16;
-      sec[j] = hb / d;
-      hcol[j] = hb % d + cidx[j] + (second[j] ? half : 0);
-      colok[j] = pc < N;
+      continue;
     }
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int u = lane; u < 32 * C4; u += 64) {
+      const int r = u / C4, c = (u % C4) * 4;
+      const int m = mrow + r, pc = n0 + wn * WN + c;
+      if (m >= M || pc >= N) continue;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(slab + r * ES + c);
+      if (SPLIT) {
+        *reinterpret_cast<f32x4*>(part + ((int64_t)kz * M + m) * N + pc) = x;
+      } else if (EPI == EPI_RESID) {
+        f32x4* hp = reinterpret_cast<f32x4*>(epi.resid + (int64_t)m * epi.ldo + pc);
+        *hp = *hp + x;
+      } else if (EPI == EPI_STORE) {
+        bf16x4 o;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = rbase + 32 * i + 8 * (v / 4) + (v % 4);
-        const int pos = m < M ? epi.rows[m] : -1;
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)x[e];
+        *reinterpret_cast<bf16x4*>((bf16*)epi.out + (int64_t)m * epi.ldo + pc) = o;
+      } else {  // EPI_QKV
+        const f32x4 y = *reinterpret_cast<const f32x4*>(slab + r * ES + (c ^ 16));
+        const int hb = pc - pc % D, p = pc - hb, pu = p & 31;
+        const bool second = pu >= 16;
+        const int rc = (p >> 5) * 16 + (pu & 15);  // rotary index of the first column
+        const int sec = hb / d;
+        const int hcol = hb % d + rc + (second ? half : 0);
+        const int pos = epi.rows[m];
         const bool pos_ok = pos >= 0 && pos < epi.seq_len;
+        f32x4 out = x;
+        if (sec < 2 && pos_ok) {
+          const f32x4 cs = *reinterpret_cast<const f32x4*>(epi.rope_cos + (int64_t)pos * half + rc);
+          const f32x4 sn = *reinterpret_cast<const f32x4*>(epi.rope_sin + (int64_t)pos * half + rc);
+          // first half: x1 cos - x2 sin; second half: x1 sin + x2 cos (x1 = partner)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const float x = acc[i][j][v];
-          const float y = swap16(x);  // every lane takes part in the swizzle
-          if (m >= M || !colok[j]) continue;
-          float out = x;
-          if (sec[j] < 2 && pos_ok) {
-            const float cs = epi.rope_cos[(int64_t)pos * half + cidx[j]];
-            const float sn = epi.rope_sin[(int64_t)pos * half + cidx[j]];
-            // first half: x1 cos - x2 sin; second half: x1 sin + x2 cos (x1 = partner)
-            out = second[j] ? y * sn + x * cs : x * cs - y * sn;
-          }
-          if (sec[j] == 0) ((bf16*)epi.out)[(int64_t)m * d + hcol[j]] = (bf16)out;
-          else if (pos_ok)
-            ((bf16*)(sec[j] == 1 ? epi.k_cache : epi.v_cache))[(int64_t)pos * d + hcol[j]] = (bf16)out;
+          for (int e = 0; e < 4; ++e) out[e] = second ? y[e] * sn[e] + x[e] * cs[e] : x[e] * cs[e] - y[e] * sn[e];
         }
-      }
-    return;
-  }
+        bf16x4 o;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WN + 32 * j + lrow;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = rbase + 32 * i + 8 * (v / 4) + (v % 4);
-        const float x = acc[i][j][v];
-        if (EPI == EPI_SWIGLU) {
-          const float y = swap16(x);  // every lane takes part in the swizzle
-          if (m < M && col < N && (lrow & 16) == 0) epi_swiglu<bf16>(epi, m, (col >> 5) * 16 + (col & 15), x, y);
-        } else if (m < M && col < N) {
-          epi_single<bf16>(epi, m, col, x);
-        }
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)out[e];
+        if (sec == 0) *reinterpret_cast<bf16x4*>((bf16*)epi.out + (int64_t)m * d + hcol) = o;
+        else if (pos_ok)
+          *reinterpret_cast<bf16x4*>((bf16*)(sec == 1 ? epi.k_cache : epi.v_cache) + (int64_t)pos * d + hcol) = o;
       }
     }
+  }
 }
 
 // -------------------------------------------------------------------- split-K reduction
