@@ -192,9 +192,18 @@ size_t carve_fwd(const ec_model_desc* m, int max_rows, int max_out, int L, void*
 }
 
 // The forward over `rows` (see ec_forward). All pointers validated by the caller.
+// Entropy outputs of a forward whose LM head reduces its logits on the fly (bf16).
+struct FusedEnt {
+  EntPart* parts;  // [n_out, column tiles of the LM head]
+  float* H;
+  int32_t* amax;
+  float* conf;
+};
+
 ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int32_t* tokens,
                       const int32_t* rows, int n_rows, const int32_t* out_idx, int n_out,
-                      void* logits, float* hidden, const FwdWs& w, hipStream_t s) {
+                      void* logits, float* hidden, const FwdWs& w, hipStream_t s,
+                      const FusedEnt* fe = nullptr) {
   const ec_dtype dt = m->dtype;
   const int d = m->d_model, F = m->ffn_dim, V = m->vocab, H = m->n_heads, Dh = m->head_dim;
   const int L = c->seq_len;
@@ -268,13 +277,26 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
     EC_CHECK_HIP(hipMemcpyAsync(hidden, w.h, (size_t)n_rows * d * sizeof(float),
                                 hipMemcpyDeviceToDevice, s));
   if (n_out > 0) {
-    TScope t(EC_T_LMHEAD, s, 2 * NO * VV * dd, (VV * dd + NO * dd + NO * VV) * es + NO * dd * 4);
+    TScope t(EC_T_LMHEAD, s, 2 * NO * VV * dd, (VV * dd + NO * dd + (fe ? 0.0 : NO * VV)) * es + NO * dd * 4);
     EC_TRY(rmsnorm(dt, w.h, n_rows, out_idx, n_out, d, m->final_norm, m->rms_eps, w.xn, s));
     EpiArgs o{};
-    o.kind = EPI_STORE;
-    o.out = logits;
-    o.ldo = V;
-    EC_TRY(gemm(dt, w.xn, m->lm_head, nullptr, n_out, V, d, o, w.splitk, w.splitk_bytes, s));
+    if (fe) {
+      // LM head with the entropy / argmax / confidence reduction in its epilogue: one
+      // partial state per (row, column tile) instead of a logits tensor
+      o.kind = EPI_ENTROPY;
+      o.parts = fe->parts;
+      EC_TRY(gemm(dt, w.xn, m->lm_head, nullptr, n_out, V, d, o, w.splitk, w.splitk_bytes, s));
+    } else {
+      o.kind = EPI_STORE;
+      o.out = logits;
+      o.ldo = V;
+      EC_TRY(gemm(dt, w.xn, m->lm_head, nullptr, n_out, V, d, o, w.splitk, w.splitk_bytes, s));
+    }
+  }
+  if (fe && n_out > 0) {
+    TScope t(EC_T_ENTROPY, s, 0.0, NO * (VV / 128.0) * sizeof(EntPart));
+    EC_TRY(entropy_merge(fe->parts, n_out, gemm_col_tiles(n_out, V, d, EPI_ENTROPY), fe->H, fe->amax,
+                         fe->conf, nullptr, 0, nullptr, s));
   }
 #undef EC_TRY
   return EC_OK;
@@ -305,7 +327,8 @@ size_t carve_step(const ec_model_desc* m, const ec_params* p, void* base, size_t
   x.H = c.take<float>(O);
   x.amax = c.take<int32_t>(O);
   x.conf = c.take<float>(O);
-  x.ent_bytes = entropy_ws_bytes(O, m->vocab);
+  x.ent_bytes = std::max(entropy_ws_bytes(O, m->vocab),
+                         (size_t)O * ((m->vocab + 127) / 128) * sizeof(EntPart));
   x.ent_ws = c.take<char>(x.ent_bytes + 1);
   if (w) *w = x;
   return c.off + 256;
@@ -534,15 +557,21 @@ ec_status ec_step(const ec_model_desc* model, const ec_cache_desc* cache, ec_sta
   // candidate indices into rows: positions themselves on a full step
   const int32_t* cidx = state->plan + (full ? lay.C0 : lay.I0);
 
-  st = run_forward(model, cache, state->tokens, rows, n_rows, cidx, n_cand, w.logits, nullptr,
-                   w.fwd, s);
-  if (st != EC_OK) return st;
-  {
+  if (model->dtype == EC_BF16) {
+    // the LM head reduces the candidates' logits in its epilogue (no logits tensor)
+    const FusedEnt fe{(EntPart*)w.ent_ws, w.H, w.amax, w.conf};
+    st = run_forward(model, cache, state->tokens, rows, n_rows, cidx, n_cand, nullptr, nullptr, w.fwd, s,
+                     &fe);
+    if (st != EC_OK) return st;
+  } else {
+    st = run_forward(model, cache, state->tokens, rows, n_rows, cidx, n_cand, w.logits, nullptr,
+                     w.fwd, s);
+    if (st != EC_OK) return st;
     TScope t(EC_T_ENTROPY, s, 0.0, (double)n_cand * model->vocab * esize(model->dtype));
     st = entropy(model->dtype, w.logits, n_cand, model->vocab, model->vocab, nullptr, 0, w.H,
                  w.amax, w.conf, nullptr, w.ent_ws, w.ent_bytes, s);
+    if (st != EC_OK) return st;
   }
-  if (st != EC_OK) return st;
   {
     TScope t(EC_T_SELECT, s, 0.0, 0.0);
     st = select_decode(w.H, w.amax, w.conf, n_cand, state->tokens, state->masked, state->plan,

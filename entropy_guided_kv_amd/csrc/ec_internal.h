@@ -56,7 +56,16 @@ struct Carver {
 
 // ---------------------------------------------------------------- GEMM
 // C[M,N] = A[M,K] . B[N,K]^T with fused epilogues.
-enum EpiKind { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
+enum EpiKind { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_ENTROPY = 4 };
+
+// Partial softmax state of one slice of a row: m = max, z = sum e^(x-m),
+// s = sum (x-m) e^(x-m) (natural units), idx = first index of m.
+struct EntPart {
+  float m, z, s;
+  int idx;
+  int nan;
+  int pad[3];
+};
 
 struct EpiArgs {
   int kind;
@@ -71,9 +80,15 @@ struct EpiArgs {
   const float* rope_sin;
   int d_model, head_dim;
   int seq_len;        // QKV: rows[m] outside [0, seq_len) are not written
+  // ENTROPY: no logits are stored; parts[m * ntiles + tile] gets the partial state
+  // of row m over the tile's columns (logits rounded to bf16 first)
+  EntPart* parts;
+  int ntiles;
 };
 
 size_t gemm_splitk_ws_bytes(int M, int N, int K, int kind, bool bf16);
+// column tiles of the bf16 GEMM's plan for M x N x K (the EPI_ENTROPY parts per row)
+int gemm_col_tiles(int M, int N, int K, int kind);
 // f32: plain weights (QKV [3d, K]; SwiGLU B = gate [N, K], B2 = up [N, K]).
 // bf16: packed weights (QKV rotary-interleaved [3d, K]; SwiGLU B = [2N, K] gate/up
 // interleave, B2 unused). N is the number of output columns.
@@ -90,6 +105,9 @@ ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, 
 
 // ---------------------------------------------------------------- entropy
 size_t entropy_ws_bytes(int rows, int vocab);
+// merge parts[rows][splits] in order into entropy / argmax / confidence, and E over sel
+ec_status entropy_merge(const EntPart* parts, int rows, int splits, float* H, int32_t* amax, float* c,
+                        const int32_t* sel, int n_sel, float* emax, hipStream_t s);
 ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t stride,
                   const int32_t* sel, int n_sel, float* H, int32_t* amax, float* c, float* emax,
                   void* ws, size_t ws_bytes, hipStream_t s);

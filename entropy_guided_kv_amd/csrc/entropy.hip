@@ -36,12 +36,7 @@ constexpr float kNegInf = -INFINITY;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-struct Part {
-  float m, z, s;  // s in natural units: sum (x - m) e^(x - m)
-  int idx;
-  int nan;
-  int pad[3];
-};
+typedef EntPart Part;  // s in natural units: sum (x - m) e^(x - m)
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
@@ -63,14 +58,6 @@ template <> struct Vec<float> {
     for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(u[k]);
   }
 };
-
-// (value, index) max with the lower index on ties
-__device__ __forceinline__ void vmax(float& v, int& i, float v2, int i2) {
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
-}
 
 // ---- wavefront reductions with DPP (no LDS round trip). After the six steps
 // lane 63 holds the result over all 64 lanes; readlane broadcasts it.
@@ -192,45 +179,71 @@ entropy_slice_kernel(const T* __restrict__ logits, int V, int64_t stride, int ch
   }
 }
 
-// Kernel 2, one wavefront per row: merge the row's slices (lane l takes slices l, l+64, ...).
+// a <- merge(a, b) of two partial states: m = max, z and s rescaled to it,
+// argmax = larger value, lower index on ties
+__device__ __forceinline__ void part_merge(Part& a, const Part& b) {
+  const float mm = fmaxf(a.m, b.m);
+  if (b.m > a.m || (b.m == a.m && b.idx < a.idx)) a.idx = b.idx;
+  a.nan |= b.nan;
+  if (mm == kNegInf) return;  // both empty: z = s = 0
+  float z = 0.f, s = 0.f;
+  if (a.m != kNegInf) {
+    const float d = a.m - mm, f = __expf(d);
+    z += a.z * f;
+    s += (a.s + d * a.z) * f;
+  }
+  if (b.m != kNegInf) {
+    const float d = b.m - mm, f = __expf(d);
+    z += b.z * f;
+    s += (b.s + d * b.z) * f;
+  }
+  a.m = mm;
+  a.z = z;
+  a.s = s;
+}
+
+// Kernel 2, one wavefront per row: one pass over the row's partial states. Lane l
+// merges states l, l+64, ... in ascending order (loads batched four deep), then the
+// 64 lane states combine along a fixed butterfly, so the result is reproducible.
+constexpr int kMergeBatch = 4;
 __global__ void __launch_bounds__(64)
 entropy_merge_kernel(const Part* __restrict__ parts, int splits, float* __restrict__ H,
                      int32_t* __restrict__ amax, float* __restrict__ conf) {
   const int row = blockIdx.x, lane = threadIdx.x;
   const Part* pr = parts + (int64_t)row * splits;
-  float mv = kNegInf;
-  int mi = 0x7fffffff, nan = 0;
-  for (int s = lane; s < splits; s += 64) {
-    vmax(mv, mi, pr[s].m, pr[s].idx);
-    nan |= pr[s].nan;
+  Part acc{kNegInf, 0.f, 0.f, 0x7fffffff, 0, {0, 0, 0}};
+  for (int s0 = 0; s0 < splits; s0 += 64 * kMergeBatch) {
+    Part p[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int q = s0 + lane + 64 * u;
+      if (q < splits) p[u] = pr[q];
+      else p[u] = Part{kNegInf, 0.f, 0.f, 0x7fffffff, 0, {0, 0, 0}};
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) part_merge(acc, p[u]);
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float v2 = __shfl_xor(mv, o);
-    const int i2 = __shfl_xor(mi, o);
-    vmax(mv, mi, v2, i2);
-    nan |= __shfl_xor(nan, o);
-  }
-  float z = 0.f, s = 0.f;
-  if (mv != kNegInf) {
-    for (int q = lane; q < splits; q += 64) {
-      const Part p = pr[q];
-      if (p.m == kNegInf) continue;
-      const float d = p.m - mv, f = __expf(d);
-      z += p.z * f;
-      s += (p.s + d * p.z) * f;
+  for (int o = 1; o < 64; o <<= 1) {
+    Part b;
+    b.m = __shfl_xor(acc.m, o);
+    b.z = __shfl_xor(acc.z, o);
+    b.s = __shfl_xor(acc.s, o);
+    b.idx = __shfl_xor(acc.idx, o);
+    b.nan = __shfl_xor(acc.nan, o);
+    if (lane & o) {  // the lower lanes' state first, on every lane alike
+      Part lo = b;
+      part_merge(lo, acc);
+      acc = lo;
+    } else {
+      part_merge(acc, b);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    z += __shfl_xor(z, o);
-    s += __shfl_xor(s, o);
-  }
   if (lane == 0) {
-    const bool bad = nan || mv == kNegInf;
-    H[row] = bad ? NAN : __logf(z) - s / z;
-    conf[row] = bad ? NAN : 1.0f / z;
-    amax[row] = mi == 0x7fffffff ? 0 : mi;
+    const bool bad = acc.nan || acc.m == kNegInf;
+    H[row] = bad ? NAN : __logf(acc.z) - acc.s / acc.z;
+    conf[row] = bad ? NAN : 1.0f / acc.z;
+    amax[row] = acc.idx == 0x7fffffff ? 0 : acc.idx;
   }
 }
 
@@ -303,6 +316,11 @@ ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t 
       entropy_slice_kernel<float, false, kU><<<grid, 256, 0, s>>>((const float*)logits, vocab, stride, chunk, splits, parts);
   }
   EC_CHECK_LAUNCH("entropy_slice_kernel");
+  return entropy_merge(parts, rows, splits, H, amax, c, sel, n_sel, emax, s);
+}
+
+ec_status entropy_merge(const EntPart* parts, int rows, int splits, float* H, int32_t* amax, float* c,
+                        const int32_t* sel, int n_sel, float* emax, hipStream_t s) {
   entropy_merge_kernel<<<rows, 64, 0, s>>>(parts, splits, H, amax, c);
   EC_CHECK_LAUNCH("entropy_merge_kernel");
   if (emax) {

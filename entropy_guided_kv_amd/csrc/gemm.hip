@@ -43,6 +43,32 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // -------------------------------------------------------------------- epilogue helpers
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// a <- merge(a, b) of partial softmax states, a covering the lower columns:
+// m = max, z and s rescaled to it; argmax = larger value, lower index on ties
+__device__ __forceinline__ void part_merge(EntPart& a, const EntPart& b) {
+  const float mm = fmaxf(a.m, b.m);
+  if (b.m > a.m || (b.m == a.m && b.idx < a.idx)) a.idx = b.idx;
+  if (mm == -INFINITY) return;  // both empty: z = s = 0
+  float z = 0.f, s = 0.f;
+  if (a.m != -INFINITY) {
+    const float dd = a.m - mm, f = __expf(dd);
+    z += a.z * f;
+    s += (a.s + dd * a.z) * f;
+  }
+  if (b.m != -INFINITY) {
+    const float dd = b.m - mm, f = __expf(dd);
+    z += b.z * f;
+    s += (b.s + dd * b.z) * f;
+  }
+  a.m = mm;
+  a.z = z;
+  a.s = s;
+  a.nan |= b.nan;
+}
+
 // Rotary pair (x1, x2) at columns (col, col + D/2) of the [3d] q|k|v output, col in
 // the first half of its head. WHICH bit 0 writes the rotated first element, bit 1
 // the second (q to the compact buffer, k and v to the cache row of position rows[m]).
@@ -276,7 +302,9 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   lds_stage_barrier();  // every wavefront is done with the staging buffers
   constexpr int ES = WN + 4;                 // slab row stride (floats)
   constexpr int C4 = WN / 4;                 // 4-column units per slab row
-  static_assert(NW * 32 * ES * 4 <= NSTG * STAGE, "epilogue slab exceeds the LDS tile buffers");
+  constexpr int PL_BYTES = EPI == EPI_ENTROPY ? BM * WAVES_N * (int)sizeof(EntPart) : 0;
+  static_assert(NW * 32 * ES * 4 + PL_BYTES <= NSTG * STAGE, "epilogue staging exceeds the LDS tile buffers");
+  static_assert(EPI != EPI_ENTROPY || !SPLIT, "the entropy epilogue needs whole K");
   float* slab = reinterpret_cast<float*>(smem) + wave * 32 * ES;
   const int d = epi.d_model, D = epi.head_dim, half = D / 2;
 #pragma unroll
@@ -286,6 +314,43 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
 #pragma unroll
       for (int v = 0; v < 16; ++v) slab[(8 * (v / 4) + 4 * hi + (v % 4)) * ES + 32 * j + lrow] = acc[i][j][v];
     const int mrow = m0 + wm * WM + 32 * i;  // first output row of this slab
+    if (EPI == EPI_ENTROPY) {
+      // partial softmax state of each slab row over this wavefront's WN columns, on
+      // the logits rounded to bf16 (the values a stored logits tensor would hold):
+      // lanes l and l + 32 take the lower / upper WN/2 columns of row l % 32
+      constexpr int CW = WN / 2;
+      const int r = lane & 31, cb = (lane >> 5) * CW;
+      const int colb = n0 + wn * WN + cb;
+      float mx = -INFINITY, z = 0.f, s2 = 0.f;
+      int ix = 0x7fffffff;
+#pragma unroll
+      for (int c = 0; c < CW; ++c) {
+        const float x = colb + c < N ? (float)(bf16)slab[r * ES + cb + c] : -INFINITY;
+        if (x > mx) {  // NaN never wins; the first index of the max stays
+          mx = x;
+          ix = colb + c;
+        }
+      }
+      if (mx != -INFINITY) {
+        const float mb = mx * kLog2e;
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+          const float x = colb + c < N ? (float)(bf16)slab[r * ES + cb + c] : -INFINITY;
+          const float t = fmaf(x, kLog2e, -mb);
+          const float e = __builtin_amdgcn_exp2f(t);  // a NaN logit makes z NaN
+          z += e;
+          s2 = fmaf(fmaxf(t, -1000.f), e, s2);     // -inf logit: -1000 * 0 = 0
+        }
+      }
+      EntPart a{mx, z, s2 * kLn2, ix, 0, {0, 0, 0}};
+      EntPart b{__shfl_xor(a.m, 32), __shfl_xor(a.z, 32), __shfl_xor(a.s, 32), __shfl_xor(a.idx, 32), 0,
+                {0, 0, 0}};
+      if (lane < 32) {
+        part_merge(a, b);
+        reinterpret_cast<EntPart*>(smem + NW * 32 * ES * 4)[(wm * WM + 32 * i + r) * WAVES_N + wn] = a;
+      }
+      continue;
+    }
     if (EPI == EPI_SWIGLU && !SPLIT) {
       // units: (row, 4 gate columns); the up partner is 16 columns on
       constexpr int UG = C4 / 2;
@@ -345,6 +410,18 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
         else if (pos_ok)
           *reinterpret_cast<bf16x4*>((bf16*)(sec == 1 ? epi.k_cache : epi.v_cache) + (int64_t)pos * d + hcol) = o;
       }
+    }
+  }
+  if (EPI == EPI_ENTROPY) {
+    // one state per (row, column tile): the wavefronts' states merged in column order
+    lds_stage_barrier();
+    const EntPart* pl = reinterpret_cast<const EntPart*>(smem + NW * 32 * ES * 4);
+    for (int r = tid; r < BM; r += NT) {
+      if (m0 + r >= M) continue;
+      EntPart a = pl[r * WAVES_N];
+#pragma unroll
+      for (int w = 1; w < WAVES_N; ++w) part_merge(a, pl[r * WAVES_N + w]);
+      epi.parts[(int64_t)(m0 + r) * epi.ntiles + nt] = a;
     }
   }
 }
@@ -475,18 +552,21 @@ struct Plan {
 // per staged byte; smaller ones fill the 256 CUs at skinny M (skip steps, the LM
 // head over the candidates). K is split only when a configuration's tiles cover
 // fewer than half the CUs.
-Plan plan_bf16(int M, int N, int K) {
+Plan plan_bf16(int M, int N, int K, int kind) {
   Plan best{};
   double best_us = 1e300;
   const int nk = K / BK;
+  // the fused entropy epilogue needs whole K and stages one state per row and
+  // wavefront column next to the slabs: 128x128 and 64x128 tiles only
+  const bool ent = kind == EPI_ENTROPY;
   for (int c = 0; c < kNumTileCfg; ++c) {
     const TileInfo& t = kTile[c];
     if (M <= 64 && c != T64x128) continue;
-    if (M <= 128 && (c == T256x192 || c == T256x128)) continue;
+    if ((M <= 128 || ent) && (c == T256x192 || c == T256x128)) continue;
     const int MT = (M + t.BM - 1) / t.BM, NT = (N + t.BN - 1) / t.BN;
     const int64_t tiles = (int64_t)MT * NT;
     int S = 1;
-    if (tiles < kCUs / 2)
+    if (tiles < kCUs / 2 && !ent)
       while (tiles * S * 2 <= kCUs && S < 8 && nk % (2 * S) == 0 && nk / (2 * S) >= 8) S *= 2;
     const int64_t waves = (tiles * S + kCUs - 1) / kCUs;
     double us = (double)waves * 2.0 * t.BM * t.BN * (double)(K / S) / (t.eff * 4e6);
@@ -520,18 +600,25 @@ ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, int M, int N,
     EC_CHECK_LAUNCH("gemm_bf16_kernel");
     return EC_OK;
   };
-  if (p.S > 1) return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, true>);
+  if constexpr (EPI != EPI_ENTROPY) {
+    if (p.S > 1) return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, true>);
+  }
   return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, false>);
 }
 
 template <int EPI>
 ec_status launch_cfg(const Plan& p, const bf16* A, const bf16* B, int M, int N, int K,
                      const EpiArgs& epi, float* part, hipStream_t s) {
-  switch (p.cfg) {
-    case T256x192: return launch_bf16<256, 192, 64, 96, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
-    case T256x128: return launch_bf16<256, 128, 64, 64, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
-    case T128x128: return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
-    default: return launch_bf16<64, 128, 32, 32, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+  if constexpr (EPI == EPI_ENTROPY) {
+    if (p.cfg == T128x128) return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+    return launch_bf16<64, 128, 32, 32, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+  } else {
+    switch (p.cfg) {
+      case T256x192: return launch_bf16<256, 192, 64, 96, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
+      case T256x128: return launch_bf16<256, 128, 64, 64, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
+      case T128x128: return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+      default: return launch_bf16<64, 128, 32, 32, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+    }
   }
 }
 
@@ -540,10 +627,15 @@ int b_rows(int N, int kind) { return kind == EPI_SWIGLU ? 2 * N : N; }
 
 }  // namespace
 
+int gemm_col_tiles(int M, int N, int K, int kind) {
+  if (M <= 0) return 0;
+  return plan_bf16(M, b_rows(N, kind), K, kind).NT;
+}
+
 size_t gemm_splitk_ws_bytes(int M, int N, int K, int kind, bool is_bf16) {
   if (!is_bf16 || M <= 0) return 0;
   const int NB = b_rows(N, kind);
-  Plan p = plan_bf16(M, NB, K);
+  Plan p = plan_bf16(M, NB, K, kind);
   if (p.S <= 1) return 0;
   return (size_t)p.S * M * NB * sizeof(float);
 }
@@ -553,6 +645,7 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
   if (M == 0) return EC_OK;
   const int kind = epi.kind;
   if (dt == EC_F32) {
+    EC_REQUIRE(kind != EPI_ENTROPY, EC_ERR_UNSUPPORTED, "gemm: the fused entropy epilogue is bf16 only");
     const int64_t units = (kind == EPI_QKV) ? (int64_t)M * (N / 2) : (int64_t)M * N;
     const int blocks = (int)((units + kThreads - 1) / kThreads);
     gemm_f32_kernel<<<blocks, kThreads, 0, s>>>((const float*)A, (const float*)B,
@@ -567,7 +660,12 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
   if (kind == EPI_SWIGLU)
     EC_REQUIRE(N % 16 == 0, EC_ERR_UNSUPPORTED, "gemm: packed SwiGLU needs F %% 16 == 0");
   const int NB = b_rows(N, kind);
-  Plan p = plan_bf16(M, NB, K);
+  Plan p = plan_bf16(M, NB, K, kind);
+  EpiArgs e = epi;
+  if (kind == EPI_ENTROPY) {
+    EC_REQUIRE(epi.parts != nullptr, EC_ERR_ARG, "gemm: entropy epilogue without a parts buffer");
+    e.ntiles = p.NT;
+  }
   float* part = nullptr;
   if (p.S > 1) {
     const size_t need = gemm_splitk_ws_bytes(M, N, K, kind, true);
@@ -579,10 +677,11 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
   const bf16* b = (const bf16*)B;
   ec_status st;
   switch (kind) {
-    case EPI_QKV: st = launch_cfg<EPI_QKV>(p, a, b, M, NB, K, epi, part, s); break;
-    case EPI_SWIGLU: st = launch_cfg<EPI_SWIGLU>(p, a, b, M, NB, K, epi, part, s); break;
-    case EPI_RESID: st = launch_cfg<EPI_RESID>(p, a, b, M, NB, K, epi, part, s); break;
-    default: st = launch_cfg<EPI_STORE>(p, a, b, M, NB, K, epi, part, s); break;
+    case EPI_QKV: st = launch_cfg<EPI_QKV>(p, a, b, M, NB, K, e, part, s); break;
+    case EPI_SWIGLU: st = launch_cfg<EPI_SWIGLU>(p, a, b, M, NB, K, e, part, s); break;
+    case EPI_RESID: st = launch_cfg<EPI_RESID>(p, a, b, M, NB, K, e, part, s); break;
+    case EPI_ENTROPY: st = launch_cfg<EPI_ENTROPY>(p, a, b, M, NB, K, e, part, s); break;
+    default: st = launch_cfg<EPI_STORE>(p, a, b, M, NB, K, e, part, s); break;
   }
   if (st != EC_OK) return st;
   if (p.S > 1) {

@@ -150,3 +150,34 @@ def test_determinism_two_runs_bit_identical():
     assert res[0][0] == res[1][0]
     assert torch.equal(res[0][1], res[1][1])
     assert all(torch.equal(a, b) for a, b in zip(res[0][2], res[1][2]))
+
+
+@pytest.mark.parametrize("n_cand_rows", ["small"])
+def test_fused_lm_head_entropy_matches_stored_logits(n_cand_rows):
+    """bf16 ec_step reduces the LM head's logits in the GEMM epilogue (no logits tensor).
+    Its first step must match ec_forward's stored logits reduced by ec_entropy_max: same
+    picked positions and ids, entropy within 1e-5 nats, confidence within 1e-5 relative."""
+    from entropy_guided_kv_amd import api
+    cfg = synth.CONFIGS["small"]
+    w = synth.make_model(cfg.model, n_layers=2)
+    dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+    prompt = synth.make_prompt(cfg)
+    dec = _decoder(dm, cfg, math.inf)
+    dec.reset(torch.from_numpy(prompt))
+    tokens0 = dec.tokens.clone()
+    o = dec.step()
+    assert o.refreshed
+    L, P, B = cfg.seq_len, cfg.prompt_len, cfg.block_len
+    cand = np.arange(P, min(P + B, L))
+    cache = api.KVCache(dm, L)
+    allr = torch.arange(L, dtype=torch.int32, device="cuda")
+    logits, _ = api.ec_forward(dm, cache, tokens0, allr, torch.from_numpy(cand.astype(np.int32)).cuda())
+    H, a, c, _ = api.ec_entropy_max(logits)
+    torch.cuda.synchronize()
+    H, a, c = H.cpu().numpy(), a.cpu().numpy(), c.cpu().numpy()
+    order = sorted(range(len(cand)), key=lambda i: (-c[i], cand[i]))[: cfg.tokens_per_step]
+    picked = sorted(order, key=lambda i: cand[i])
+    assert o.positions == [int(cand[i]) for i in picked]
+    assert o.ids == [int(a[i]) for i in picked]
+    np.testing.assert_allclose(o.entropy, H[picked], rtol=0, atol=1e-5)
+    np.testing.assert_allclose(o.maxprob, c[picked], rtol=1e-5, atol=0)
