@@ -106,7 +106,8 @@ def upload_model(cfg, keep_layers: int, device="cuda"):
                 log(f"[bench] weights: {i + 1}/{m.n_layers} layers on device ({time.time() - t0:.1f}s)")
     fn = synth.make_final_norm(m)
     host["final_norm"] = fn
-    dm = api.DeviceModel(m, d_emb, layers, to_dev(fn), d_head, rope_max_pos=cfg.seq_len, device=device)
+    rope_max = max(cfg.seq_len, synth.CONFIGS["long"].seq_len)  # the long-context batch reuses the model
+    dm = api.DeviceModel(m, d_emb, layers, to_dev(fn), d_head, rope_max_pos=rope_max, device=device)
     torch.cuda.synchronize()
     return dm, host
 
@@ -142,6 +143,65 @@ def timed_steps(dec, prompt, K):
     ev1.record()
     torch.cuda.synchronize()
     return outs, time.perf_counter() - t0, ev0.elapsed_time(ev1)
+
+
+def batch_step_work(m, L: int, rows, cands):
+    """(flops, bytes) of one batched step: per-sequence work summed, weights read once."""
+    f = b = 0.0
+    w_bytes = 2.0 * (m.n_layers * (4 * m.d_model ** 2 + 3 * m.d_model * m.ffn_dim) + m.vocab * m.d_model)
+    for r, c in zip(rows, cands):
+        fi, bi = step_work(m, L, r, c)
+        f += fi
+        b += bi - w_bytes
+    return f, b + w_bytes
+
+
+def long_batch_bench(dm, steps: int, warmup: int = 2):
+    """The long-context workload: 4 sequences of 3584 prompt + 512 masked positions,
+    k = 32, stepped together by ec_step_batch (one forward over all their rows per step).
+    tau = 1.0 as configured (every step refreshes with random weights), then tau = +inf
+    (one refresh per sequence, then skip steps)."""
+    import torch
+    import synth
+    from entropy_guided_kv_amd import api
+    cfg = synth.CONFIGS["long"]
+    m = cfg.model
+    prompts = [torch.from_numpy(synth.make_prompt(cfg, seq=i)) for i in range(cfg.batch)]
+    bd = api.BatchDecoder(dm, cfg.batch, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step,
+                          cfg.block_len, cfg.k_recent, 1.0)
+    res = {"workload": f"{cfg.batch} sequences x (L={cfg.seq_len} = {cfg.prompt_len} prompt + "
+                       f"{cfg.n_masked} masked), k={cfg.k_recent}, 1 token/step, blocks of {cfg.block_len}",
+           "workspace_MiB": bd.workspace.numel() / 2 ** 20}
+    for tau in (1.0, math.inf):
+        bd.set_tau(tau)
+        bd.reset(prompts)
+        n_warm = warmup if tau == 1.0 else 1  # at +inf the first (refresh) step is the warmup
+        for _ in range(n_warm):
+            bd.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        outs = [bd.step() for _ in range(steps)]
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        roof = 0.0
+        ntok = nref = nseq = 0
+        for st in outs:
+            live = [o for o in st if o is not None]
+            f, b = batch_step_work(m, cfg.seq_len, [o.rows for o in live], [o.n_cand for o in live])
+            roof += t_roof(f, b)
+            ntok += sum(len(o.positions) for o in live)
+            nref += sum(o.refreshed for o in live)
+            nseq += len(live)
+        res[f"tau={tau}"] = {"steps": steps, "steps_per_s": steps / wall,
+                             "gen_tokens_per_s": ntok / wall, "ms_per_step": wall * 1e3 / steps,
+                             "refresh_rate": nref / max(nseq, 1),
+                             "mean_rows_per_seq": sum(o.rows for st in outs for o in st if o) / max(nseq, 1),
+                             "roofline_frac": roof / wall}
+        log(f"[bench] long batch-4 tau={tau}: {steps / wall:.2f} steps/s, {ntok / wall:.1f} tokens/s, "
+            f"roofline {roof / wall:.3f}")
+    del bd
+    torch.cuda.empty_cache()
+    return res
 
 
 def kernel_breakdown(dec, prompt, n_refresh=4, n_skip=8):
@@ -267,6 +327,9 @@ def main():
     ap.add_argument("--no-entropy", action="store_true", help="skip the 64x126464 entropy kernel run")
     ap.add_argument("--entropy-only", action="store_true",
                     help="only the 64x126464 entropy kernel run (no model)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context batch-of-4 workload (ec_step_batch)")
+    ap.add_argument("--long-steps", type=int, default=8, help="timed steps of the long-context batch")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -353,6 +416,10 @@ def main():
     if not args.no_breakdown:
         roofline, kernels = breakdown_report(dec, prompt, args.breakdown == "both")
 
+    long_res = None
+    if not args.no_long:
+        long_res = long_batch_bench(dm, args.long_steps)
+
     ent = None
     if not args.no_entropy:
         ent = _entropy_kernel_bench()
@@ -365,7 +432,7 @@ def main():
         cpu = cpu_baseline(cfg, host, prompt_np, args.cpu_layers)
         log(f"[bench] CPU oracle: {cpu['value']:.4f} steps/s on {cpu['cores']} threads")
     emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, sweep, roofline, kernels,
-         ent, cpu)
+         ent, cpu, long_res)
 
 
 def breakdown_report(dec, prompt, with_skip=True):
@@ -408,7 +475,7 @@ def breakdown_report(dec, prompt, with_skip=True):
 
 
 def emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, sweep, roofline,
-         kernels, ent, cpu):
+         kernels, ent, cpu, long_res=None):
     res = {
         "metric": METRIC,
         "value": steps_s,
@@ -434,6 +501,7 @@ def emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, swe
         "roofline": roofline,
         "kernels": kernels,
         "entropy_kernel_64x126464": ent,
+        "long_context_batch4": long_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

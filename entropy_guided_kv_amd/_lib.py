@@ -11,6 +11,7 @@ EC_OK, EC_ERR_ARG, EC_ERR_DTYPE, EC_ERR_WORKSPACE, EC_ERR_HIP, EC_ERR_NAN, EC_ER
 EC_F32, EC_BF16 = 0, 1
 EC_LAYOUT_PLAIN, EC_LAYOUT_PACKED = 0, 1
 EC_MAX_TOKENS_PER_STEP = 64
+EC_MAX_SEQ = 16
 
 STATUS_NAMES = {
     0: "EC_OK", 1: "EC_ERR_ARG", 2: "EC_ERR_DTYPE", 3: "EC_ERR_WORKSPACE", 4: "EC_ERR_HIP",
@@ -22,7 +23,7 @@ EXPORTS = (
     "ec_partial_attn_workspace_size", "ec_partial_attn", "ec_rope_table",
     "ec_forward_workspace_size", "ec_forward", "ec_state_plan_words", "ec_state_reset",
     "ec_step_workspace_size", "ec_step", "ec_timing_enable", "ec_timing_read", "ec_last_error",
-    "ec_version", "ec_pack_weights",
+    "ec_version", "ec_pack_weights", "ec_step_batch_workspace_size", "ec_step_batch",
 )
 
 EC_T_KINDS = 10
@@ -121,6 +122,10 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ec_last_error": (C.c_char_p, []),
         "ec_version": (C.c_int, []),
         "ec_pack_weights": (C.c_int, [C.c_int, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "ec_step_batch_workspace_size": (sz, [C.POINTER(ec_model_desc), i32, C.POINTER(ec_params)]),
+        "ec_step_batch": (C.c_int, [C.POINTER(ec_model_desc), i32, C.POINTER(ec_cache_desc),
+                                    C.POINTER(ec_state), C.POINTER(ec_params), vp, sz, vp,
+                                    C.POINTER(ec_step_out)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -325,6 +325,86 @@ class Decoder:
         return outs
 
 
+class BatchDecoder:
+    """Several independent sequences of one model stepped together by ec_step_batch:
+    one forward over all their rows per step, each sequence deciding refresh or skip
+    from its own E."""
+
+    def __init__(self, model: DeviceModel, n_seq: int, seq_len: int, prompt_len: int,
+                 tokens_per_step: int, block_len: int, k_recent: int, tau: float):
+        lib = load()
+        if not 1 <= n_seq <= _lib.EC_MAX_SEQ:
+            raise ValueError(f"n_seq must be in [1, {_lib.EC_MAX_SEQ}]")
+        self.model, self.n_seq = model, n_seq
+        dev = model.device
+        p = _lib.ec_params()
+        p.struct_size = C.sizeof(_lib.ec_params)
+        p.tau = float(tau)
+        p.k_recent, p.tokens_per_step, p.block_len = k_recent, tokens_per_step, block_len
+        p.prompt_len, p.seq_len, p.mask_id = prompt_len, seq_len, model.shape.mask_id
+        self.params = p
+        self.caches = [KVCache(model, seq_len) for _ in range(n_seq)]
+        words = lib.ec_state_plan_words(seq_len, k_recent)
+        self.tokens = [torch.zeros(seq_len, dtype=torch.int32, device=dev) for _ in range(n_seq)]
+        self.masked = [torch.zeros(seq_len, dtype=torch.uint8, device=dev) for _ in range(n_seq)]
+        self.plans = [torch.zeros(words, dtype=torch.int32, device=dev) for _ in range(n_seq)]
+        self._cd = (_lib.ec_cache_desc * n_seq)(*[c.desc for c in self.caches])
+        self.states = (_lib.ec_state * n_seq)()
+        self._outs = (_lib.ec_step_out * n_seq)()
+        for i in range(n_seq):
+            st = self.states[i]
+            st.struct_size = C.sizeof(_lib.ec_state)
+            st.tokens, st.masked, st.plan = (self.tokens[i].data_ptr(), self.masked[i].data_ptr(),
+                                             self.plans[i].data_ptr())
+            self._outs[i].struct_size = C.sizeof(_lib.ec_step_out)
+        need = lib.ec_step_batch_workspace_size(C.byref(model.desc), n_seq, C.byref(p))
+        if need == 0:
+            check(_lib.EC_ERR_ARG, "ec_step_batch_workspace_size")
+        self.workspace = _workspace(need, dev)
+
+    def set_tau(self, tau: float) -> None:
+        self.params.tau = float(tau)
+
+    def reset(self, prompts: Sequence[torch.Tensor], stream=None) -> None:
+        """Load each sequence's prompt (the first prompt_len ids of prompts[i])."""
+        P = self.params.prompt_len
+        for i in range(self.n_seq):
+            self.tokens[i][:P].copy_(prompts[i][:P].to(device=self.tokens[i].device, dtype=torch.int32))
+            check(load().ec_state_reset(C.byref(self.states[i]), C.byref(self.params), _stream(stream)),
+                  "ec_state_reset")
+
+    @property
+    def done(self) -> bool:
+        return all(self.states[i].n_masked <= 0 for i in range(self.n_seq))
+
+    def step(self, stream=None) -> List[Optional[StepOut]]:
+        """One batched step; None for sequences that had nothing left to decode."""
+        lib = load()
+        active = [self.states[i].n_masked > 0 for i in range(self.n_seq)]
+        rc = lib.ec_step_batch(C.byref(self.model.desc), self.n_seq, self._cd, self.states,
+                               C.byref(self.params), _ptr(self.workspace), self.workspace.numel(),
+                               _stream(stream), self._outs)
+        if rc not in (_lib.EC_OK, _lib.EC_ERR_NAN):
+            check(rc, "ec_step_batch")
+        res = []
+        for i in range(self.n_seq):
+            if not active[i]:
+                res.append(None)
+                continue
+            o = self._outs[i]
+            n = o.n_decoded
+            res.append(StepOut(o.status, bool(o.refreshed), o.rows, o.n_cand, bool(o.refresh_next), o.emax,
+                               list(o.positions[:n]), list(o.ids[:n]), list(o.entropy[:n]),
+                               list(o.maxprob[:n])))
+        return res
+
+    def run(self, max_steps: Optional[int] = None, stream=None) -> List[List[Optional[StepOut]]]:
+        outs = []
+        while not self.done and (max_steps is None or len(outs) < max_steps):
+            outs.append(self.step(stream))
+        return outs
+
+
 # ---------------------------------------------------------------------- measurement aid
 def ec_timing_enable(on: bool) -> None:
     check(load().ec_timing_enable(1 if on else 0), "ec_timing_enable")

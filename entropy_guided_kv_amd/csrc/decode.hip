@@ -17,6 +17,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace ec {
 
 namespace {
@@ -225,6 +227,27 @@ ec_status plan_reset(int32_t* tokens, uint8_t* masked, int32_t* plan, const ec_p
   reset_kernel<<<1, kThreads, 0, s>>>(tokens, masked, plan, p.seq_len, p.prompt_len, p.block_len,
                                       p.k_recent, p.mask_id, res);
   EC_CHECK_LAUNCH("reset_kernel");
+  return EC_OK;
+}
+
+__global__ void __launch_bounds__(kThreads)
+batch_gather_kernel(BatchSegs b, int32_t* __restrict__ rows_all, int32_t* __restrict__ row_seq,
+                    int32_t* __restrict__ out_all) {
+  const BatchSeg g = b.seg[blockIdx.y];
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < g.n_rows; i += gridDim.x * kThreads) {
+    rows_all[g.row_off + i] = g.rows[i];
+    row_seq[g.row_off + i] = g.seq;
+  }
+  for (int j = blockIdx.x * kThreads + threadIdx.x; j < g.n_cand; j += gridDim.x * kThreads)
+    out_all[g.cand_off + j] = g.row_off + g.cidx[j];
+}
+
+ec_status batch_gather(const BatchSegs& b, int max_rows, int32_t* rows_all, int32_t* row_seq,
+                       int32_t* out_all, hipStream_t s) {
+  if (b.n == 0) return EC_OK;
+  dim3 grid((unsigned)std::max(1, std::min((max_rows + kThreads - 1) / kThreads, 64)), (unsigned)b.n);
+  batch_gather_kernel<<<grid, kThreads, 0, s>>>(b, rows_all, row_seq, out_all);
+  EC_CHECK_LAUNCH("batch_gather_kernel");
   return EC_OK;
 }
 

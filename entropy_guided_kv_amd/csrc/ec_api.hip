@@ -192,6 +192,18 @@ size_t carve_fwd(const ec_model_desc* m, int max_rows, int max_out, int L, void*
 }
 
 // The forward over `rows` (see ec_forward). All pointers validated by the caller.
+// Rows of several sequences in one forward (ec_step_batch): sequence s owns rows
+// [row_off[s], row_off[s+1]) of the concatenated row list.
+struct BatchRows {
+  int n_seq;
+  const int32_t* row_seq;          // device [rows]: sequence of each row
+  const int32_t* const* tok_tab;   // device [n_seq]: token array of each sequence
+  void* const* k_tab;              // device [n_layers * n_seq]: K cache of (layer, sequence)
+  void* const* v_tab;
+  const int* row_off;              // host [n_seq + 1]
+  const ec_cache_desc* caches;     // host [n_seq]
+};
+
 // Entropy outputs of a forward whose LM head reduces its logits on the fly (bf16).
 struct FusedEnt {
   EntPart* parts;  // [n_out, column tiles of the LM head]
@@ -203,7 +215,7 @@ struct FusedEnt {
 ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int32_t* tokens,
                       const int32_t* rows, int n_rows, const int32_t* out_idx, int n_out,
                       void* logits, float* hidden, const FwdWs& w, hipStream_t s,
-                      const FusedEnt* fe = nullptr) {
+                      const FusedEnt* fe = nullptr, const BatchRows* b = nullptr) {
   const ec_dtype dt = m->dtype;
   const int d = m->d_model, F = m->ffn_dim, V = m->vocab, H = m->n_heads, Dh = m->head_dim;
   const int L = c->seq_len;
@@ -219,7 +231,8 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
   if (n_rows > 0) {
     {
       TScope t(EC_T_EMBED, s, 0.0, M * dd * (es + 4));
-      EC_TRY(embed(dt, m->embed, V, tokens, L, rows, n_rows, d, w.h, s));
+      EC_TRY(embed(dt, m->embed, V, tokens, L, rows, n_rows, d, w.h, s, b ? b->tok_tab : nullptr,
+                   b ? b->row_seq : nullptr));
     }
     for (int l = 0; l < m->n_layers; ++l) {
       const ec_layer_weights& lw = m->layers[l];
@@ -231,8 +244,14 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
       e.kind = EPI_QKV;
       e.out = w.q;
       e.ldo = d;
-      e.k_cache = c->k[l];
-      e.v_cache = c->v[l];
+      if (b) {
+        e.row_seq = b->row_seq;
+        e.k_tab = b->k_tab + (size_t)l * b->n_seq;
+        e.v_tab = b->v_tab + (size_t)l * b->n_seq;
+      } else {
+        e.k_cache = c->k[l];
+        e.v_cache = c->v[l];
+      }
       e.rows = rows;
       e.rope_cos = m->rope_cos;
       e.rope_sin = m->rope_sin;
@@ -245,7 +264,19 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
       }
       {
         TScope t(EC_T_ATTN, s, 4 * M * Lq * dd, (2 * Lq * dd + 2 * M * dd) * es);
-        EC_TRY(attn(dt, w.q, c->k[l], c->v[l], n_rows, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
+        if (b) {
+          // each sequence's rows attend to that sequence's cache (stream order keeps the
+          // split partials of consecutive launches apart)
+          for (int q = 0; q < b->n_seq; ++q) {
+            const int r0 = b->row_off[q], nr = b->row_off[q + 1] - r0;
+            if (nr == 0) continue;
+            const size_t off = (size_t)r0 * d * esize(dt);
+            EC_TRY(attn(dt, (const char*)w.q + off, b->caches[q].k[l], b->caches[q].v[l], nr, L, H, Dh,
+                        scale, (char*)w.o + off, w.attn, w.attn_bytes, s));
+          }
+        } else {
+          EC_TRY(attn(dt, w.q, c->k[l], c->v[l], n_rows, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
+        }
       }
       EpiArgs r{};
       r.kind = EPI_RESID;
@@ -330,6 +361,74 @@ size_t carve_step(const ec_model_desc* m, const ec_params* p, void* base, size_t
   x.ent_bytes = std::max(entropy_ws_bytes(O, m->vocab),
                          (size_t)O * ((m->vocab + 127) / 128) * sizeof(EntPart));
   x.ent_ws = c.take<char>(x.ent_bytes + 1);
+  if (w) *w = x;
+  return c.off + 256;
+}
+
+// Apply a step's device result to the state and the host record; false if E is NaN.
+bool finish_step(const StepResult& h, const ec_params& p, bool full, int n_rows, int n_cand, ec_state* state,
+                 ec_step_out* out) {
+  const bool nan = h.has_nan != 0;
+  const bool refresh = nan || (h.emax > p.tau);
+  out->status = nan ? EC_ERR_NAN : EC_OK;
+  out->refreshed = full ? 1 : 0;
+  out->rows = n_rows;
+  out->n_cand = n_cand;
+  out->n_decoded = h.n_picked;
+  out->refresh_next = refresh ? 1 : 0;
+  out->emax = h.emax;
+  for (int i = 0; i < h.n_picked && i < EC_MAX_TOKENS_PER_STEP; ++i) {
+    out->positions[i] = h.pos[i];
+    out->ids[i] = h.ids[i];
+    out->entropy[i] = h.ent[i];
+    out->maxprob[i] = h.conf[i];
+  }
+  state->t += 1;
+  state->refresh_next = refresh ? 1 : 0;
+  state->n_masked = h.n_masked;
+  state->n_decoded += h.n_picked;
+  state->next_rows = h.next_rows;
+  state->next_cand = h.next_cand;
+  return !nan;
+}
+
+// ec_step_batch workspace: the forward over every sequence's rows, candidates of all
+// sequences, the concatenated row / candidate lists and the device pointer tables
+struct BatchWs {
+  FwdWs fwd;
+  void* logits;  // fp32 models only
+  float* H;
+  int32_t* amax;
+  float* conf;
+  void* ent_ws;
+  size_t ent_bytes;
+  int32_t* rows_all;
+  int32_t* row_seq;
+  int32_t* out_all;
+  const int32_t** tok_tab;
+  void** k_tab;
+  void** v_tab;
+};
+
+size_t carve_batch(const ec_model_desc* m, int n_seq, const ec_params* p, void* base, size_t cap, BatchWs* w) {
+  const int L = p->seq_len, O = max_cand(p);
+  const int MR = n_seq * L, MO = n_seq * O;
+  BatchWs x;
+  const size_t fwd = carve_fwd(m, MR, MO, L, base, cap, &x.fwd);
+  Carver c(base, cap);
+  c.off = fwd;
+  x.logits = c.take<char>(m->dtype == EC_F32 ? (size_t)MO * m->vocab * 4 : 1);
+  x.H = c.take<float>(MO);
+  x.amax = c.take<int32_t>(MO);
+  x.conf = c.take<float>(MO);
+  x.ent_bytes = std::max(entropy_ws_bytes(MO, m->vocab), (size_t)MO * ((m->vocab + 127) / 128) * sizeof(EntPart));
+  x.ent_ws = c.take<char>(x.ent_bytes + 1);
+  x.rows_all = c.take<int32_t>(MR);
+  x.row_seq = c.take<int32_t>(MR);
+  x.out_all = c.take<int32_t>(MO);
+  x.tok_tab = c.take<const int32_t*>(n_seq);
+  x.k_tab = c.take<void*>((size_t)m->n_layers * n_seq);
+  x.v_tab = c.take<void*>((size_t)m->n_layers * n_seq);
   if (w) *w = x;
   return c.off + 256;
 }
@@ -582,30 +681,132 @@ ec_status ec_step(const ec_model_desc* model, const ec_cache_desc* cache, ec_sta
   EC_CHECK_HIP(hipMemcpyAsync(&h, res, sizeof(StepResult), hipMemcpyDeviceToHost, s));
   EC_CHECK_HIP(hipStreamSynchronize(s));
   if (g_tm.on) timing_collect();
-
-  const bool nan = h.has_nan != 0;
-  const bool refresh = nan || (h.emax > params->tau);
-  out->status = nan ? EC_ERR_NAN : EC_OK;
-  out->refreshed = full ? 1 : 0;
-  out->rows = n_rows;
-  out->n_cand = n_cand;
-  out->n_decoded = h.n_picked;
-  out->refresh_next = refresh ? 1 : 0;
-  out->emax = h.emax;
-  for (int i = 0; i < h.n_picked && i < EC_MAX_TOKENS_PER_STEP; ++i) {
-    out->positions[i] = h.pos[i];
-    out->ids[i] = h.ids[i];
-    out->entropy[i] = h.ent[i];
-    out->maxprob[i] = h.conf[i];
-  }
-  state->t += 1;
-  state->refresh_next = refresh ? 1 : 0;
-  state->n_masked = h.n_masked;
-  state->n_decoded += h.n_picked;
-  state->next_rows = h.next_rows;
-  state->next_cand = h.next_cand;
-  if (nan) {
+  if (!finish_step(h, *params, full, n_rows, n_cand, state, out)) {
     set_error("ec_step: E is NaN at step %d; next step refreshes", state->t - 1);
+    return EC_ERR_NAN;
+  }
+  return EC_OK;
+}
+
+size_t ec_step_batch_workspace_size(const ec_model_desc* model, int32_t n_seq, const ec_params* params) {
+  if (check_model(model) != EC_OK || check_params(params, model, nullptr) != EC_OK) return 0;
+  if (n_seq < 1 || n_seq > EC_MAX_SEQ) return 0;
+  return carve_batch(model, n_seq, params, nullptr, 0, nullptr);
+}
+
+ec_status ec_step_batch(const ec_model_desc* model, int32_t n_seq, const ec_cache_desc* caches,
+                        ec_state* states, const ec_params* params, void* workspace,
+                        size_t workspace_bytes, void* stream, ec_step_out* outs) {
+  ec_status st = check_model(model);
+  if (st != EC_OK) return st;
+  EC_REQUIRE(n_seq >= 1 && n_seq <= EC_MAX_SEQ, EC_ERR_ARG, "ec_step_batch: n_seq %d not in [1, %d]",
+             n_seq, EC_MAX_SEQ);
+  EC_REQUIRE(caches && states && outs, EC_ERR_ARG, "ec_step_batch: null caches, states or outs");
+  st = check_params(params, model, &caches[0]);
+  if (st != EC_OK) return st;
+  for (int q = 0; q < n_seq; ++q) {
+    st = check_cache(&caches[q], model);
+    if (st != EC_OK) return st;
+    EC_REQUIRE(caches[q].seq_len == params->seq_len, EC_ERR_ARG, "ec_step_batch: cache %d seq_len differs", q);
+    const ec_state& sq = states[q];
+    EC_REQUIRE(sq.struct_size >= sizeof(ec_state) && sq.tokens && sq.masked && sq.plan, EC_ERR_ARG,
+               "ec_step_batch: bad state %d", q);
+    EC_REQUIRE(outs[q].struct_size >= sizeof(ec_step_out), EC_ERR_ARG, "ec_step_batch: bad out %d", q);
+  }
+  const size_t need = carve_batch(model, n_seq, params, nullptr, 0, nullptr);
+  EC_REQUIRE(workspace && workspace_bytes >= need, EC_ERR_WORKSPACE,
+             "ec_step_batch: workspace %zu < %zu bytes", workspace_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  for (int q = 0; q < n_seq; ++q) {
+    const uint32_t osz = outs[q].struct_size;
+    memset(&outs[q], 0, sizeof(ec_step_out));
+    outs[q].struct_size = osz;
+  }
+  BatchWs w;
+  carve_batch(model, n_seq, params, workspace, workspace_bytes, &w);
+  const PlanLayout lay(params->seq_len, params->k_recent);
+  const int L = params->seq_len, nl = model->n_layers;
+
+  // this step's rows and candidates of every sequence, concatenated in sequence order
+  BatchSegs segs{};
+  int row_off[EC_MAX_SEQ + 1], cand_off[EC_MAX_SEQ + 1];
+  bool full[EC_MAX_SEQ] = {};
+  int nrows[EC_MAX_SEQ] = {}, ncand[EC_MAX_SEQ] = {};
+  int M = 0, C = 0;
+  for (int q = 0; q < n_seq; ++q) {
+    row_off[q] = M;
+    cand_off[q] = C;
+    const ec_state& sq = states[q];
+    if (sq.n_masked <= 0) continue;
+    full[q] = sq.t == 0 || sq.refresh_next;
+    nrows[q] = full[q] ? L : sq.next_rows;
+    ncand[q] = sq.next_cand;
+    segs.seg[segs.n++] = BatchSeg{sq.plan + (full[q] ? lay.J0 : lay.R0), sq.plan + (full[q] ? lay.C0 : lay.I0),
+                                  nrows[q], M, ncand[q], C, q};
+    M += nrows[q];
+    C += ncand[q];
+  }
+  row_off[n_seq] = M;
+  cand_off[n_seq] = C;
+  if (segs.n == 0) return EC_OK;
+
+  // device tables of token arrays and of every (layer, sequence) cache; the host
+  // vectors outlive the copies (the stream is synchronised before returning)
+  std::vector<const int32_t*> tok(n_seq);
+  std::vector<void*> kt((size_t)nl * n_seq), vt((size_t)nl * n_seq);
+  for (int q = 0; q < n_seq; ++q) {
+    tok[q] = states[q].tokens;
+    for (int l = 0; l < nl; ++l) {
+      kt[(size_t)l * n_seq + q] = caches[q].k[l];
+      vt[(size_t)l * n_seq + q] = caches[q].v[l];
+    }
+  }
+  EC_CHECK_HIP(hipMemcpyAsync(w.tok_tab, tok.data(), tok.size() * sizeof(void*), hipMemcpyHostToDevice, s));
+  EC_CHECK_HIP(hipMemcpyAsync(w.k_tab, kt.data(), kt.size() * sizeof(void*), hipMemcpyHostToDevice, s));
+  EC_CHECK_HIP(hipMemcpyAsync(w.v_tab, vt.data(), vt.size() * sizeof(void*), hipMemcpyHostToDevice, s));
+  st = batch_gather(segs, L, w.rows_all, w.row_seq, w.out_all, s);
+  if (st != EC_OK) return st;
+
+  const BatchRows b{n_seq, w.row_seq, w.tok_tab, w.k_tab, w.v_tab, row_off, caches};
+  if (model->dtype == EC_BF16) {
+    const FusedEnt fe{(EntPart*)w.ent_ws, w.H, w.amax, w.conf};
+    st = run_forward(model, &caches[0], nullptr, w.rows_all, M, w.out_all, C, nullptr, nullptr, w.fwd, s,
+                     &fe, &b);
+    if (st != EC_OK) return st;
+  } else {
+    st = run_forward(model, &caches[0], nullptr, w.rows_all, M, w.out_all, C, w.logits, nullptr, w.fwd, s,
+                     nullptr, &b);
+    if (st != EC_OK) return st;
+    TScope t(EC_T_ENTROPY, s, 0.0, (double)C * model->vocab * esize(model->dtype));
+    st = entropy(model->dtype, w.logits, C, model->vocab, model->vocab, nullptr, 0, w.H, w.amax, w.conf,
+                 nullptr, w.ent_ws, w.ent_bytes, s);
+    if (st != EC_OK) return st;
+  }
+  StepResult hres[EC_MAX_SEQ];
+  {
+    TScope t(EC_T_SELECT, s, 0.0, 0.0);
+    for (int i = 0; i < segs.n; ++i) {
+      const int q = segs.seg[i].seq;
+      StepResult* res = (StepResult*)(states[q].plan + lay.RES);
+      st = select_decode(w.H + cand_off[q], w.amax + cand_off[q], w.conf + cand_off[q], ncand[q],
+                         states[q].tokens, states[q].masked, states[q].plan, *params, res, s);
+      if (st != EC_OK) return st;
+    }
+  }
+  for (int i = 0; i < segs.n; ++i) {
+    const int q = segs.seg[i].seq;
+    EC_CHECK_HIP(hipMemcpyAsync(&hres[i], states[q].plan + lay.RES, sizeof(StepResult),
+                                hipMemcpyDeviceToHost, s));
+  }
+  EC_CHECK_HIP(hipStreamSynchronize(s));
+  if (g_tm.on) timing_collect();
+  int bad = -1;
+  for (int i = 0; i < segs.n; ++i) {
+    const int q = segs.seg[i].seq;
+    if (!finish_step(hres[i], *params, full[q], nrows[q], ncand[q], &states[q], &outs[q]) && bad < 0) bad = q;
+  }
+  if (bad >= 0) {
+    set_error("ec_step_batch: E of sequence %d is NaN; its next step refreshes", bad);
     return EC_ERR_NAN;
   }
   return EC_OK;

@@ -84,7 +84,20 @@ struct EpiArgs {
   // of row m over the tile's columns (logits rounded to bf16 first)
   EntPart* parts;
   int ntiles;
+  // QKV over rows of several sequences: row m writes its K / V row into the cache of
+  // sequence row_seq[m] (k_tab / v_tab hold this layer's cache of each sequence);
+  // row_seq == nullptr: every row uses k_cache / v_cache
+  const int32_t* row_seq;
+  void* const* k_tab;
+  void* const* v_tab;
 };
+
+// K / V destination of row m for the QKV epilogues
+template <typename T>
+__device__ __forceinline__ T* kv_dst(const EpiArgs& e, int m, bool v) {
+  if (e.row_seq) return (T*)(v ? e.v_tab : e.k_tab)[e.row_seq[m]];
+  return (T*)(v ? e.v_cache : e.k_cache);
+}
 
 size_t gemm_splitk_ws_bytes(int M, int N, int K, int kind, bool bf16);
 // column tiles of the bf16 GEMM's plan for M x N x K (the EPI_ENTROPY parts per row)
@@ -113,12 +126,29 @@ ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t 
                   void* ws, size_t ws_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------- elementwise
+// h[i] = table[tokens[rows[i]]]; with row_seq, the token array of row i is tok_tab[row_seq[i]]
 ec_status embed(ec_dtype dt, const void* table, int vocab, const int32_t* tokens, int L,
-                const int32_t* rows, int n, int d, float* h, hipStream_t s);
+                const int32_t* rows, int n, int d, float* h, hipStream_t s,
+                const int32_t* const* tok_tab = nullptr, const int32_t* row_seq = nullptr);
 ec_status rmsnorm(ec_dtype dt, const float* h, int n_src, const int32_t* idx, int n, int d,
                   const void* gain, float eps, void* out, hipStream_t s);
 ec_status scatter(ec_dtype dt, void* kc, void* vc, int64_t L, int width, const void* kr,
                   const void* vr, const int32_t* idx, int n, hipStream_t s);
+
+// ---------------------------------------------------------------- batch of sequences
+// per-sequence segments of the concatenated row / candidate lists of ec_step_batch
+struct BatchSeg {
+  const int32_t* rows;  // positions recomputed (device, in the sequence's plan)
+  const int32_t* cidx;  // candidate indices into rows (device)
+  int n_rows, row_off, n_cand, cand_off, seq;
+};
+struct BatchSegs {
+  BatchSeg seg[EC_MAX_SEQ];
+  int n;
+};
+// rows_all[row_off + i] = rows[i], row_seq[...] = seq; out_all[cand_off + j] = row_off + cidx[j]
+ec_status batch_gather(const BatchSegs& b, int max_rows, int32_t* rows_all, int32_t* row_seq,
+                       int32_t* out_all, hipStream_t s);
 
 // ---------------------------------------------------------------- decode / plan
 // plan buffer layout (int32 words), L = seq_len, k = k_recent (ring size max(k,1)):

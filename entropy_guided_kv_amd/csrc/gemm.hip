@@ -90,8 +90,7 @@ __device__ __forceinline__ void epi_qkv_pair(const EpiArgs& e, int m, int col, f
   }
   T* dst;
   if (sec == 0) dst = (T*)e.out + (int64_t)m * d;
-  else if (sec == 1) dst = (T*)e.k_cache + (int64_t)pos * d;
-  else dst = (T*)e.v_cache + (int64_t)pos * d;
+  else dst = kv_dst<T>(e, m, sec == 2) + (int64_t)pos * d;
   if (which & 1) dst[hc] = from_f<T>(y1);
   if (which & 2) dst[hc + half] = from_f<T>(y2);
 }
@@ -408,7 +407,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
         for (int e = 0; e < 4; ++e) o[e] = (bf16)out[e];
         if (sec == 0) *reinterpret_cast<bf16x4*>((bf16*)epi.out + (int64_t)m * d + hcol) = o;
         else if (pos_ok)
-          *reinterpret_cast<bf16x4*>((bf16*)(sec == 1 ? epi.k_cache : epi.v_cache) + (int64_t)pos * d + hcol) = o;
+          *reinterpret_cast<bf16x4*>(kv_dst<bf16>(epi, m, sec == 2) + (int64_t)pos * d + hcol) = o;
       }
     }
   }

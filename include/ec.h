@@ -44,6 +44,7 @@ extern "C" {
 #define EC_VERSION 10100            /* 1.1.0 */
 #define EC_MAX_TOKENS_PER_STEP 64   /* upper bound on tokens decoded per step */
 #define EC_MAX_LAYERS 256
+#define EC_MAX_SEQ 16               /* upper bound on sequences per ec_step_batch call */
 
 typedef enum ec_status {
   EC_OK = 0,
@@ -290,6 +291,26 @@ size_t ec_step_workspace_size(const ec_model_desc* model, const ec_params* param
 ec_status ec_step(const ec_model_desc* model, const ec_cache_desc* cache, ec_state* state,
                   const ec_params* params, void* workspace, size_t workspace_bytes,
                   void* stream, ec_step_out* out);
+
+/* ec_step_batch -- one denoising step of n_seq independent sequences of the same
+ * model with the same params (every field but the state and cache is shared),
+ * decided per sequence exactly as ec_step decides it: sequence s refreshes when
+ * its own t == 0 or its refresh_next is set, otherwise it recomputes its own
+ * recompute set, and it reads its own E. All sequences' rows go through one
+ * forward (one launch per GEMM over the concatenated rows, so every weight is
+ * read once per step for the whole batch; attention runs per sequence against
+ * that sequence's cache); one LM head over all candidates with the entropy
+ * reduction fused for bf16; selection per sequence.
+ * (EntropyCache explainer, Arabic technical summary, section 2, with the
+ * decision taken per sequence; the batching itself is not on the pages.)
+ * caches, states, outs: HOST arrays of n_seq entries (1 <= n_seq <= EC_MAX_SEQ);
+ * a sequence with no masked position left is not stepped (its out has
+ * n_decoded = 0). Synchronises `stream` once. Returns EC_ERR_NAN if any
+ * sequence's E is NaN (that sequence's out->status says which). */
+size_t ec_step_batch_workspace_size(const ec_model_desc* model, int32_t n_seq, const ec_params* params);
+ec_status ec_step_batch(const ec_model_desc* model, int32_t n_seq, const ec_cache_desc* caches,
+                        ec_state* states, const ec_params* params, void* workspace,
+                        size_t workspace_bytes, void* stream, ec_step_out* outs);
 
 /* ------------------------------------------------------------------------
  * Measurement aid: per-kernel-group timing with HIP events.

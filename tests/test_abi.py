@@ -120,3 +120,12 @@ def test_argument_errors_return_before_any_gpu_work(lib):
     st = _lib.ec_state()
     st.struct_size = C.sizeof(_lib.ec_state)
     assert lib.ec_state_reset(C.byref(st), C.byref(_params()), None) == E.EC_ERR_ARG
+    # batched step: sequence count and null arrays are rejected before any GPU work
+    assert lib.ec_step_batch(C.byref(m), 0, None, None, C.byref(_params()), None, 0, None, None) == E.EC_ERR_ARG
+    assert lib.ec_step_batch(C.byref(m), E.EC_MAX_SEQ + 1, None, None, C.byref(_params()), None, 0, None,
+                             None) == E.EC_ERR_ARG
+    assert lib.ec_step_batch(C.byref(m), 2, None, None, C.byref(_params()), None, 0, None, None) == E.EC_ERR_ARG
+    assert lib.ec_step_batch_workspace_size(C.byref(m), 0, C.byref(_params())) == 0
+    ws1 = lib.ec_step_batch_workspace_size(C.byref(m), 1, C.byref(_params()))
+    ws4 = lib.ec_step_batch_workspace_size(C.byref(m), 4, C.byref(_params()))
+    assert ws1 > 0 and ws4 > 3 * ws1 // 2

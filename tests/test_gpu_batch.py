@@ -1,0 +1,123 @@
+"""GPU parity: ec_step_batch (several sequences in one forward per step).
+
+Each sequence must follow exactly the trajectory ec_step gives it alone, and the
+oracle's loop run on that sequence alone (EntropyCache explainer, Arabic
+technical summary section 2: the decision is taken per sequence from its own
+E). Bars as for ec_step: path, |R|, candidates, decoded positions and ids
+identical wherever the margin gate clears; E within 1e-3 nats (fp32 models) or
+2e-2 (bf16) of the oracle. Against ec_step alone, fp32 runs are bit-identical
+(the fp32 kernels reduce every output in a fixed order whatever the row count).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import loop as ol
+from oracle import model as om
+from tests.test_gpu_step import PEAKED_SCALE, PEAKED_TAU, _gate_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def _prompts(cfg, n):
+    base = synth.make_prompt(cfg)
+    out = [base]
+    for i in range(1, n):
+        p = base.copy()
+        rng = np.random.default_rng(100 + i)
+        p[: cfg.prompt_len] = rng.integers(0, cfg.model.vocab - 1, cfg.prompt_len)
+        out.append(p)
+    return out
+
+
+def _batch_run(dm, cfg, tau, prompts, max_steps=None):
+    from entropy_guided_kv_amd import api
+    bd = api.BatchDecoder(dm, len(prompts), cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step,
+                          cfg.block_len, cfg.k_recent, tau)
+    bd.reset([torch.from_numpy(p) for p in prompts])
+    steps = bd.run(max_steps=max_steps)
+    return bd, [[st[i] for st in steps] for i in range(len(prompts))]
+
+
+def _check_vs_oracle(outs, recs, cfg, tau, e_tol):
+    compared = 0
+    for o, r in zip(outs, recs):
+        assert o is not None
+        assert o.refreshed == r.refreshed, f"step {r.t}: path differs"
+        assert o.rows == len(r.rows) and o.n_cand == len(r.cand)
+        same = o.positions == [int(p) for p in r.picked] and o.ids == [int(i) for i in r.ids]
+        if not same:
+            assert not _gate_ok(r, cfg.tokens_per_step, cfg.model.dtype), f"step {r.t}: decoded differs"
+            break
+        assert abs(o.emax - r.emax) <= e_tol, f"step {r.t}: E {o.emax} vs {r.emax}"
+        if abs(float(np.float32(r.emax)) - tau) > e_tol:
+            assert o.refresh_next == r.refresh_next
+        compared += 1
+    return compared
+
+
+def test_batch_tiny_peaked_matches_oracle_and_single():
+    """Three fp32 sequences, refresh and skip steps mixed within and across sequences."""
+    from entropy_guided_kv_amd import api
+    cfg = synth.CONFIGS["tiny"]
+    w = synth.make_model(cfg.model, lm_head_scale=PEAKED_SCALE)
+    dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+    prompts = _prompts(cfg, 3)
+    bd, seq_outs = _batch_run(dm, cfg, PEAKED_TAU, prompts)
+    mixed_step = False
+    for t in range(len(seq_outs[0])):
+        flags = {seq_outs[i][t].refreshed for i in range(3)}
+        mixed_step |= len(flags) == 2
+    assert mixed_step, "no step mixed refresh and skip sequences"
+    for i, p in enumerate(prompts):
+        recs, _, _ = ol.run_entropycache(om.OracleModel(w), cfg, p, PEAKED_TAU)
+        assert len(seq_outs[i]) == len(recs)
+        assert _check_vs_oracle(seq_outs[i], recs, cfg, PEAKED_TAU, 1e-3) == len(recs)
+        # the same sequence stepped alone by ec_step: bit-identical
+        dec = api.Decoder(dm, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len,
+                          cfg.k_recent, PEAKED_TAU)
+        dec.reset(torch.from_numpy(p))
+        single = dec.run()
+        assert [(o.refreshed, o.positions, o.ids, o.emax) for o in single] == \
+               [(o.refreshed, o.positions, o.ids, o.emax) for o in seq_outs[i]]
+        assert torch.equal(dec.tokens, bd.tokens[i])
+        for a, b in zip(dec.cache.k + dec.cache.v, bd.caches[i].k + bd.caches[i].v):
+            assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("tau", [1.0, math.inf])
+def test_batch_small_bf16_first_steps(tau):
+    """Two bf16 sequences of the small config (refresh-only at tau 1, skips at tau inf)."""
+    from entropy_guided_kv_amd import api
+    cfg = synth.CONFIGS["small"]
+    w = synth.make_model(cfg.model)
+    dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+    prompts = _prompts(cfg, 2)
+    steps = 3 if tau == 1.0 else 5
+    _, seq_outs = _batch_run(dm, cfg, tau, prompts, max_steps=steps)
+    for i, p in enumerate(prompts):
+        recs, _, _ = ol.run_entropycache(om.OracleModel(w), cfg, p, tau, max_steps=steps)
+        # the configs' flat logits leave near ties at the selection cut: the comparison
+        # runs up to the first gated divergence (as for ec_step alone)
+        _check_vs_oracle(seq_outs[i], recs, cfg, tau, 2e-2)
+        assert seq_outs[i][0].refreshed and abs(seq_outs[i][0].emax - recs[0].emax) <= 2e-2
+
+
+def test_batch_sixteen_sequences_tiny():
+    """The largest batch: 16 fp32 sequences equal their single-sequence runs."""
+    from entropy_guided_kv_amd import api
+    cfg = synth.CONFIGS["tiny"]
+    w = synth.make_model(cfg.model, lm_head_scale=PEAKED_SCALE)
+    dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+    prompts = _prompts(cfg, 16)
+    _, seq_outs = _batch_run(dm, cfg, PEAKED_TAU, prompts, max_steps=6)
+    for i in (0, 7, 15):
+        dec = api.Decoder(dm, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len,
+                          cfg.k_recent, PEAKED_TAU)
+        dec.reset(torch.from_numpy(prompts[i]))
+        single = dec.run(max_steps=6)
+        assert [(o.refreshed, o.positions, o.ids, o.emax) for o in single] == \
+               [(o.refreshed, o.positions, o.ids, o.emax) for o in seq_outs[i]]
