@@ -204,6 +204,43 @@ def long_batch_bench(dm, steps: int, warmup: int = 2):
     return res
 
 
+def drift_probe_bench(dec, prompt, steps: int):
+    """ec_step_probe on the headline workload: the probe's cost per step, and E of step t
+    against the mean (over layers) V drift that step t+1 measures on the rows it recomputes
+    (every row on a refresh step: the pages' step-to-step KV drift)."""
+    import numpy as np
+    import torch
+    nl = len(dec.model.layers)
+    drift = torch.zeros(4 * nl, dtype=torch.float32, device="cuda")
+    res = {}
+    for probe in (False, True):
+        dec.reset(prompt)
+        dec.step(drift=drift if probe else None)  # first step: cache never written (NaN drift)
+        torch.cuda.synchronize()
+        es, dv, dk = [], [], []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            if dec.done:
+                break
+            o = dec.step(drift=drift if probe else None)
+            if probe:
+                d = drift.cpu().numpy().reshape(nl, 4)
+                dk.append(float(np.nanmean(d[:, 0])))
+                dv.append(float(np.nanmean(d[:, 2])))
+            es.append(o.emax)
+        torch.cuda.synchronize()
+        res["probe" if probe else "plain"] = (time.perf_counter() - t0) / max(len(es), 1)
+    e = np.array(es[:-1])
+    v = np.array(dv[1:])
+    out = {"steps": len(es), "ms_per_step_plain": res["plain"] * 1e3, "ms_per_step_probe": res["probe"] * 1e3,
+           "probe_overhead_ms": (res["probe"] - res["plain"]) * 1e3,
+           "mean_V_drift": float(np.mean(dv)) if dv else None, "mean_K_drift": float(np.mean(dk)) if dk else None,
+           "corr_E_t_vs_V_drift_t1": float(np.corrcoef(e, v)[0, 1]) if len(e) > 2 and np.std(e) > 0 else None}
+    log(f"[bench] KV-drift probe: +{out['probe_overhead_ms']:.2f} ms/step, mean V drift {out['mean_V_drift']}, "
+        f"corr(E_t, V drift t+1) {out['corr_E_t_vs_V_drift_t1']}")
+    return out
+
+
 def kernel_breakdown(dec, prompt, n_refresh=4, n_skip=8):
     """Per-kernel-group event timing for refresh steps and for skip steps."""
     import math as _m
@@ -327,6 +364,7 @@ def main():
     ap.add_argument("--no-entropy", action="store_true", help="skip the 64x126464 entropy kernel run")
     ap.add_argument("--entropy-only", action="store_true",
                     help="only the 64x126464 entropy kernel run (no model)")
+    ap.add_argument("--no-drift", action="store_true", help="skip the KV-drift probe run")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context batch-of-4 workload (ec_step_batch)")
     ap.add_argument("--long-steps", type=int, default=8, help="timed steps of the long-context batch")
@@ -411,10 +449,31 @@ def main():
                 f"refresh {sweep[str(tv)]['refresh_rate']:.3f}")
         dec.set_tau(tau)
 
+    # sliding-window decoding (candidates from a window at the lowest masked position)
+    window = {}
+    if not args.no_sweep:
+        wdec = api.Decoder(dm, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len,
+                           cfg.k_recent, tau, window=True)
+        for tv in (1.0, math.inf):
+            wdec.set_tau(tv)
+            o2, w2, _ = run_trajectory(wdec, prompt)
+            f_roof = sum(t_roof(*step_work(m, cfg.seq_len, o.rows, o.n_cand)) for o in o2)
+            window[str(tv)] = {"steps": len(o2), "steps_per_s": len(o2) / w2,
+                               "gen_tokens_per_s": sum(len(o.positions) for o in o2) / w2,
+                               "refresh_rate": sum(o.refreshed for o in o2) / len(o2),
+                               "mean_rows": sum(o.rows for o in o2) / len(o2), "roofline_frac": f_roof / w2}
+            log(f"[bench] sliding window tau={tv}: {window[str(tv)]['steps_per_s']:.2f} steps/s")
+        del wdec
+        sweep["sliding_window"] = window
+
     # per-kernel event timing (refresh steps and skip steps)
     roofline, kernels = None, {}
     if not args.no_breakdown:
         roofline, kernels = breakdown_report(dec, prompt, args.breakdown == "both")
+
+    drift_res = None
+    if not args.no_drift:
+        drift_res = drift_probe_bench(dec, prompt, 32)
 
     long_res = None
     if not args.no_long:
@@ -432,7 +491,7 @@ def main():
         cpu = cpu_baseline(cfg, host, prompt_np, args.cpu_layers)
         log(f"[bench] CPU oracle: {cpu['value']:.4f} steps/s on {cpu['cores']} threads")
     emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, sweep, roofline, kernels,
-         ent, cpu, long_res)
+         ent, cpu, long_res, drift_res)
 
 
 def breakdown_report(dec, prompt, with_skip=True):
@@ -475,7 +534,7 @@ def breakdown_report(dec, prompt, with_skip=True):
 
 
 def emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, sweep, roofline,
-         kernels, ent, cpu, long_res=None):
+         kernels, ent, cpu, long_res=None, drift_res=None):
     res = {
         "metric": METRIC,
         "value": steps_s,
@@ -502,6 +561,7 @@ def emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, swe
         "kernels": kernels,
         "entropy_kernel_64x126464": ent,
         "long_context_batch4": long_res,
+        "kv_drift_probe": drift_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(PKG, "libec.so")
 EC_OK, EC_ERR_ARG, EC_ERR_DTYPE, EC_ERR_WORKSPACE, EC_ERR_HIP, EC_ERR_NAN, EC_ERR_UNSUPPORTED = range(7)
 EC_F32, EC_BF16 = 0, 1
 EC_LAYOUT_PLAIN, EC_LAYOUT_PACKED = 0, 1
+EC_CAND_BLOCKS, EC_CAND_WINDOW = 0, 1
 EC_MAX_TOKENS_PER_STEP = 64
 EC_MAX_SEQ = 16
 
@@ -23,7 +24,7 @@ EXPORTS = (
     "ec_partial_attn_workspace_size", "ec_partial_attn", "ec_rope_table",
     "ec_forward_workspace_size", "ec_forward", "ec_state_plan_words", "ec_state_reset",
     "ec_step_workspace_size", "ec_step", "ec_timing_enable", "ec_timing_read", "ec_last_error",
-    "ec_version", "ec_pack_weights", "ec_step_batch_workspace_size", "ec_step_batch",
+    "ec_version", "ec_pack_weights", "ec_step_batch_workspace_size", "ec_step_batch", "ec_step_probe",
 )
 
 EC_T_KINDS = 10
@@ -57,7 +58,8 @@ class ec_cache_desc(C.Structure):
 class ec_params(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("tau", C.c_float), ("k_recent", C.c_int32),
                 ("tokens_per_step", C.c_int32), ("block_len", C.c_int32),
-                ("prompt_len", C.c_int32), ("seq_len", C.c_int32), ("mask_id", C.c_int32)]
+                ("prompt_len", C.c_int32), ("seq_len", C.c_int32), ("mask_id", C.c_int32),
+                ("candidates", C.c_int32)]
 
 
 class ec_state(C.Structure):
@@ -122,6 +124,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ec_last_error": (C.c_char_p, []),
         "ec_version": (C.c_int, []),
         "ec_pack_weights": (C.c_int, [C.c_int, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "ec_step_probe": (C.c_int, [C.POINTER(ec_model_desc), C.POINTER(ec_cache_desc), C.POINTER(ec_state),
+                                    C.POINTER(ec_params), vp, sz, vp, C.POINTER(ec_step_out), vp]),
         "ec_step_batch_workspace_size": (sz, [C.POINTER(ec_model_desc), i32, C.POINTER(ec_params)]),
         "ec_step_batch": (C.c_int, [C.POINTER(ec_model_desc), i32, C.POINTER(ec_cache_desc),
                                     C.POINTER(ec_state), C.POINTER(ec_params), vp, sz, vp,

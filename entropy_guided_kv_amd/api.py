@@ -267,7 +267,8 @@ class Decoder:
     """One sequence's EntropyCache decoding state, driven by ec_step."""
 
     def __init__(self, model: DeviceModel, seq_len: int, prompt_len: int, tokens_per_step: int,
-                 block_len: int, k_recent: int, tau: float, cache: Optional[KVCache] = None):
+                 block_len: int, k_recent: int, tau: float, cache: Optional[KVCache] = None,
+                 window: bool = False):
         lib = load()
         self.model = model
         dev = model.device
@@ -276,6 +277,7 @@ class Decoder:
         p.tau = float(tau)
         p.k_recent, p.tokens_per_step, p.block_len = k_recent, tokens_per_step, block_len
         p.prompt_len, p.seq_len, p.mask_id = prompt_len, seq_len, model.shape.mask_id
+        p.candidates = _lib.EC_CAND_WINDOW if window else _lib.EC_CAND_BLOCKS
         self.params = p
         self.cache = cache if cache is not None else KVCache(model, seq_len)
         self.tokens = torch.zeros(seq_len, dtype=torch.int32, device=dev)
@@ -306,13 +308,29 @@ class Decoder:
     def done(self) -> bool:
         return self.state.n_masked <= 0
 
-    def step(self, stream=None) -> StepOut:
+    def next_rows(self):
+        """Positions the next step recomputes if it is a skip step (R in the plan buffer:
+        int32 words from 8 + max(k, 1), state.next_rows of them, ascending)."""
+        r0 = 8 + max(self.params.k_recent, 1)
+        return self.plan[r0: r0 + self.state.next_rows].cpu().numpy()
+
+    def step(self, stream=None, drift: Optional[torch.Tensor] = None) -> StepOut:
+        """One ec_step; with ``drift`` (float32[4 * n_layers] on the GPU) ec_step_probe,
+        which also fills per layer the mean / max cosine distance of the recomputed K and V
+        rows from their cached values."""
         lib = load()
-        rc = lib.ec_step(C.byref(self.model.desc), C.byref(self.cache.desc), C.byref(self.state),
-                         C.byref(self.params), _ptr(self.workspace), self.workspace.numel(),
-                         _stream(stream), C.byref(self._out))
+        if drift is not None:
+            if drift.dtype != torch.float32 or drift.numel() < 4 * len(self.model.layers) or not drift.is_cuda:
+                raise ValueError("drift: need float32[4 * n_layers] on the GPU")
+            rc = lib.ec_step_probe(C.byref(self.model.desc), C.byref(self.cache.desc), C.byref(self.state),
+                                   C.byref(self.params), _ptr(self.workspace), self.workspace.numel(),
+                                   _stream(stream), C.byref(self._out), _ptr(drift))
+        else:
+            rc = lib.ec_step(C.byref(self.model.desc), C.byref(self.cache.desc), C.byref(self.state),
+                             C.byref(self.params), _ptr(self.workspace), self.workspace.numel(),
+                             _stream(stream), C.byref(self._out))
         if rc not in (_lib.EC_OK, _lib.EC_ERR_NAN):
-            check(rc, "ec_step")
+            check(rc, "ec_step_probe" if drift is not None else "ec_step")
         o = self._out
         n = o.n_decoded
         return StepOut(o.status, bool(o.refreshed), o.rows, o.n_cand, bool(o.refresh_next), o.emax,
@@ -331,7 +349,7 @@ class BatchDecoder:
     from its own E."""
 
     def __init__(self, model: DeviceModel, n_seq: int, seq_len: int, prompt_len: int,
-                 tokens_per_step: int, block_len: int, k_recent: int, tau: float):
+                 tokens_per_step: int, block_len: int, k_recent: int, tau: float, window: bool = False):
         lib = load()
         if not 1 <= n_seq <= _lib.EC_MAX_SEQ:
             raise ValueError(f"n_seq must be in [1, {_lib.EC_MAX_SEQ}]")
@@ -342,6 +360,7 @@ class BatchDecoder:
         p.tau = float(tau)
         p.k_recent, p.tokens_per_step, p.block_len = k_recent, tokens_per_step, block_len
         p.prompt_len, p.seq_len, p.mask_id = prompt_len, seq_len, model.shape.mask_id
+        p.candidates = _lib.EC_CAND_WINDOW if window else _lib.EC_CAND_BLOCKS
         self.params = p
         self.caches = [KVCache(model, seq_len) for _ in range(n_seq)]
         words = lib.ec_state_plan_words(seq_len, k_recent)

@@ -11,7 +11,8 @@
 //   - takes E = max entropy over the decoded rows (the decision signal);
 //   - builds the next step's lists: R = still-masked positions + ring
 //     (ascending), the candidates (masked positions of the lowest block that
-//     still has a mask) and each candidate's index in R.
+//     still has a mask; or, in sliding-window mode, the masked positions of the
+//     B positions from the lowest masked one) and each candidate's index in R.
 // It then writes a small result record that the host copies back once.
 #include "ec_internal.h"
 
@@ -66,7 +67,7 @@ __device__ int block_min(int v, int* sh) {
 }
 
 // Build R, candidates and candidate indices from masked[] and the ring.
-__device__ void build_plan(const uint8_t* masked, int32_t* plan, int L, int P, int B, int k,
+__device__ void build_plan(const uint8_t* masked, int32_t* plan, int L, int P, int B, int k, int window,
                            StepResult* res) {
   __shared__ uint32_t ringbits[kMaxL / 32];
   __shared__ int sh[kWaves + 1];
@@ -102,12 +103,12 @@ __device__ void build_plan(const uint8_t* masked, int32_t* plan, int L, int P, i
     const int inr = (ringbits[p / 32] >> (p % 32)) & 1;
     if (m | inr) R[off++] = p;
   }
-  // candidates: masked positions of the lowest open block
+  // candidates: masked positions of the lowest open block [P + bB, P + (b+1)B), or
+  // of the window [first, first + B) that starts at the lowest masked position
   const int first = block_min(mmin, sh);
   int clo = L, chi = L;
   if (first < L) {
-    const int b = (first - P) / B;
-    clo = P + b * B;
+    clo = window ? first : P + ((first - P) / B) * B;
     chi = min(L, clo + B);
   }
   int ccnt = 0;
@@ -141,7 +142,7 @@ __device__ void build_plan(const uint8_t* masked, int32_t* plan, int L, int P, i
 }
 
 __global__ void __launch_bounds__(kThreads)
-reset_kernel(int32_t* tokens, uint8_t* masked, int32_t* plan, int L, int P, int B, int k,
+reset_kernel(int32_t* tokens, uint8_t* masked, int32_t* plan, int L, int P, int B, int k, int window,
              int mask_id, StepResult* res) {
   const PlanLayout lay(L, k);
   for (int p = threadIdx.x; p < L; p += kThreads) {
@@ -152,7 +153,7 @@ reset_kernel(int32_t* tokens, uint8_t* masked, int32_t* plan, int L, int P, int 
   if (threadIdx.x == 0) plan[0] = 0;
   for (int e = threadIdx.x; e < lay.K; e += kThreads) plan[8 + e] = -1;
   __syncthreads();
-  build_plan(masked, plan, L, P, B, k, res);
+  build_plan(masked, plan, L, P, B, k, window, res);
   if (threadIdx.x == 0) {
     res->n_picked = 0;
     res->has_nan = 0;
@@ -163,7 +164,7 @@ reset_kernel(int32_t* tokens, uint8_t* masked, int32_t* plan, int L, int P, int 
 __global__ void __launch_bounds__(kThreads)
 select_kernel(const float* __restrict__ H, const int32_t* __restrict__ amax,
               const float* __restrict__ conf, int n_cand, int32_t* tokens, uint8_t* masked,
-              int32_t* plan, int L, int P, int B, int k, int n, StepResult* res) {
+              int32_t* plan, int L, int P, int B, int k, int window, int n, StepResult* res) {
   const PlanLayout lay(L, k);
   __shared__ int by_rank[EC_MAX_TOKENS_PER_STEP];
   __shared__ float emax_sh[EC_MAX_TOKENS_PER_STEP];
@@ -216,7 +217,7 @@ select_kernel(const float* __restrict__ H, const int32_t* __restrict__ amax,
     plan[0] = count0 + npick;
   }
   __syncthreads();
-  build_plan(masked, plan, L, P, B, k, res);
+  build_plan(masked, plan, L, P, B, k, window, res);
 }
 
 }  // namespace
@@ -225,7 +226,7 @@ ec_status plan_reset(int32_t* tokens, uint8_t* masked, int32_t* plan, const ec_p
                      StepResult* res, hipStream_t s) {
   EC_REQUIRE(p.seq_len <= kMaxL, EC_ERR_UNSUPPORTED, "seq_len %d > %d", p.seq_len, kMaxL);
   reset_kernel<<<1, kThreads, 0, s>>>(tokens, masked, plan, p.seq_len, p.prompt_len, p.block_len,
-                                      p.k_recent, p.mask_id, res);
+                                      p.k_recent, p.candidates == EC_CAND_WINDOW, p.mask_id, res);
   EC_CHECK_LAUNCH("reset_kernel");
   return EC_OK;
 }
@@ -255,8 +256,8 @@ ec_status select_decode(const float* H, const int32_t* amax, const float* conf, 
                         int32_t* tokens, uint8_t* masked, int32_t* plan, const ec_params& p,
                         StepResult* res, hipStream_t s) {
   select_kernel<<<1, kThreads, 0, s>>>(H, amax, conf, n_cand, tokens, masked, plan, p.seq_len,
-                                       p.prompt_len, p.block_len, p.k_recent, p.tokens_per_step,
-                                       res);
+                                       p.prompt_len, p.block_len, p.k_recent,
+                                       p.candidates == EC_CAND_WINDOW, p.tokens_per_step, res);
   EC_CHECK_LAUNCH("select_kernel");
   return EC_OK;
 }

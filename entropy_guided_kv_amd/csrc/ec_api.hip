@@ -204,6 +204,14 @@ struct BatchRows {
   const ec_cache_desc* caches;     // host [n_seq]
 };
 
+// KV-drift probe buffers of a forward (ec_step_probe)
+struct DriftProbe {
+  void* old_k;   // [rows, d] cached K of the rows before the layer's QKV GEMM
+  void* old_v;
+  float* dist;   // [n_layers][2][rows] per-row cosine distances
+  float* out;    // device [4 * n_layers]
+};
+
 // Entropy outputs of a forward whose LM head reduces its logits on the fly (bf16).
 struct FusedEnt {
   EntPart* parts;  // [n_out, column tiles of the LM head]
@@ -215,7 +223,8 @@ struct FusedEnt {
 ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int32_t* tokens,
                       const int32_t* rows, int n_rows, const int32_t* out_idx, int n_out,
                       void* logits, float* hidden, const FwdWs& w, hipStream_t s,
-                      const FusedEnt* fe = nullptr, const BatchRows* b = nullptr) {
+                      const FusedEnt* fe = nullptr, const BatchRows* b = nullptr,
+                      const DriftProbe* probe = nullptr) {
   const ec_dtype dt = m->dtype;
   const int d = m->d_model, F = m->ffn_dim, V = m->vocab, H = m->n_heads, Dh = m->head_dim;
   const int L = c->seq_len;
@@ -258,10 +267,15 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
       e.d_model = d;
       e.head_dim = Dh;
       e.seq_len = L;
+      if (probe)
+        EC_TRY(drift_gather(dt, c->k[l], c->v[l], rows, n_rows, L, d, probe->old_k, probe->old_v, s));
       {
         TScope t(EC_T_QKV, s, 2 * M * 3 * dd * dd, (3 * dd * dd + M * dd + 3 * M * dd) * es);
         EC_TRY(gemm(dt, w.a, lw.wqkv, nullptr, n_rows, 3 * d, d, e, w.splitk, w.splitk_bytes, s));
       }
+      if (probe)
+        EC_TRY(drift_rows(dt, probe->old_k, probe->old_v, c->k[l], c->v[l], rows, n_rows, L, d,
+                          probe->dist + (size_t)l * 2 * n_rows, s));
       {
         TScope t(EC_T_ATTN, s, 4 * M * Lq * dd, (2 * Lq * dd + 2 * M * dd) * es);
         if (b) {
@@ -304,6 +318,7 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
       }
     }
   }
+  if (probe && n_rows > 0) EC_TRY(drift_reduce(probe->dist, m->n_layers, n_rows, 2 * (int64_t)n_rows, probe->out, s));
   if (hidden && n_rows > 0)
     EC_CHECK_HIP(hipMemcpyAsync(hidden, w.h, (size_t)n_rows * d * sizeof(float),
                                 hipMemcpyDeviceToDevice, s));
@@ -342,6 +357,9 @@ struct StepWs {
   float* conf;
   void* ent_ws;
   size_t ent_bytes;
+  void* old_k;   // KV-drift probe (ec_step_probe)
+  void* old_v;
+  float* dist;
 };
 
 int max_cand(const ec_params* p) {
@@ -361,6 +379,9 @@ size_t carve_step(const ec_model_desc* m, const ec_params* p, void* base, size_t
   x.ent_bytes = std::max(entropy_ws_bytes(O, m->vocab),
                          (size_t)O * ((m->vocab + 127) / 128) * sizeof(EntPart));
   x.ent_ws = c.take<char>(x.ent_bytes + 1);
+  x.old_k = c.take<char>((size_t)L * m->d_model * esize(m->dtype));
+  x.old_v = c.take<char>((size_t)L * m->d_model * esize(m->dtype));
+  x.dist = c.take<float>((size_t)m->n_layers * 2 * L);
   if (w) *w = x;
   return c.off + 256;
 }
@@ -442,6 +463,8 @@ ec_status check_params(const ec_params* p, const ec_model_desc* m, const ec_cach
   EC_REQUIRE(p->tokens_per_step >= 1 && p->tokens_per_step <= EC_MAX_TOKENS_PER_STEP, EC_ERR_ARG,
              "params: tokens_per_step must be in [1, %d]", EC_MAX_TOKENS_PER_STEP);
   EC_REQUIRE(!(p->tau != p->tau), EC_ERR_ARG, "params: tau is NaN");
+  EC_REQUIRE(p->candidates == EC_CAND_BLOCKS || p->candidates == EC_CAND_WINDOW, EC_ERR_ARG,
+             "params: candidates must be EC_CAND_BLOCKS or EC_CAND_WINDOW");
   if (m) EC_REQUIRE(p->mask_id >= 0 && p->mask_id < m->vocab, EC_ERR_ARG, "params: mask_id out of range");
   if (c) EC_REQUIRE(c->seq_len == p->seq_len, EC_ERR_ARG, "params: seq_len differs from cache");
   return EC_OK;
@@ -451,6 +474,75 @@ ec_status check_params(const ec_params* p, const ec_model_desc* m, const ec_cach
 }  // namespace ec
 
 using namespace ec;
+
+// One step of one sequence (ec_step, and with drift != NULL ec_step_probe).
+ec_status step_impl(const ec_model_desc* model, const ec_cache_desc* cache, ec_state* state,
+                    const ec_params* params, void* workspace, size_t workspace_bytes, void* stream,
+                    ec_step_out* out, float* drift) {
+  ec_status st = check_model(model);
+  if (st != EC_OK) return st;
+  st = check_cache(cache, model);
+  if (st != EC_OK) return st;
+  st = check_params(params, model, cache);
+  if (st != EC_OK) return st;
+  EC_REQUIRE(state && state->struct_size >= sizeof(ec_state) && state->tokens && state->masked &&
+                 state->plan,
+             EC_ERR_ARG, "ec_step: bad state");
+  EC_REQUIRE(out && out->struct_size >= sizeof(ec_step_out), EC_ERR_ARG, "ec_step: bad out");
+  const size_t need = carve_step(model, params, nullptr, 0, nullptr);
+  EC_REQUIRE(workspace && workspace_bytes >= need, EC_ERR_WORKSPACE,
+             "ec_step: workspace %zu < %zu bytes", workspace_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  const uint32_t osz = out->struct_size;
+  memset(out, 0, sizeof(ec_step_out));
+  out->struct_size = osz;
+  if (state->n_masked <= 0) return EC_OK;
+
+  StepWs w;
+  carve_step(model, params, workspace, workspace_bytes, &w);
+  const PlanLayout lay(params->seq_len, params->k_recent);
+  StepResult* res = (StepResult*)(state->plan + lay.RES);
+  const bool full = state->t == 0 || state->refresh_next;
+  const int L = params->seq_len;
+  const int n_rows = full ? L : state->next_rows;
+  const int n_cand = state->next_cand;
+  const int32_t* rows = state->plan + (full ? lay.J0 : lay.R0);
+  // candidate indices into rows: positions themselves on a full step
+  const int32_t* cidx = state->plan + (full ? lay.C0 : lay.I0);
+
+  const DriftProbe probe{w.old_k, w.old_v, w.dist, drift};
+  const DriftProbe* pr = drift ? &probe : nullptr;
+  if (model->dtype == EC_BF16) {
+    // the LM head reduces the candidates' logits in its epilogue (no logits tensor)
+    const FusedEnt fe{(EntPart*)w.ent_ws, w.H, w.amax, w.conf};
+    st = run_forward(model, cache, state->tokens, rows, n_rows, cidx, n_cand, nullptr, nullptr, w.fwd, s,
+                     &fe, nullptr, pr);
+    if (st != EC_OK) return st;
+  } else {
+    st = run_forward(model, cache, state->tokens, rows, n_rows, cidx, n_cand, w.logits, nullptr,
+                     w.fwd, s, nullptr, nullptr, pr);
+    if (st != EC_OK) return st;
+    TScope t(EC_T_ENTROPY, s, 0.0, (double)n_cand * model->vocab * esize(model->dtype));
+    st = entropy(model->dtype, w.logits, n_cand, model->vocab, model->vocab, nullptr, 0, w.H,
+                 w.amax, w.conf, nullptr, w.ent_ws, w.ent_bytes, s);
+    if (st != EC_OK) return st;
+  }
+  {
+    TScope t(EC_T_SELECT, s, 0.0, 0.0);
+    st = select_decode(w.H, w.amax, w.conf, n_cand, state->tokens, state->masked, state->plan,
+                       *params, res, s);
+  }
+  if (st != EC_OK) return st;
+  StepResult h;
+  EC_CHECK_HIP(hipMemcpyAsync(&h, res, sizeof(StepResult), hipMemcpyDeviceToHost, s));
+  EC_CHECK_HIP(hipStreamSynchronize(s));
+  if (g_tm.on) timing_collect();
+  if (!finish_step(h, *params, full, n_rows, n_cand, state, out)) {
+    set_error("ec_step: E is NaN at step %d; next step refreshes", state->t - 1);
+    return EC_ERR_NAN;
+  }
+  return EC_OK;
+}
 
 extern "C" {
 
@@ -625,68 +717,16 @@ ec_status ec_state_reset(ec_state* state, const ec_params* params, void* stream)
 ec_status ec_step(const ec_model_desc* model, const ec_cache_desc* cache, ec_state* state,
                   const ec_params* params, void* workspace, size_t workspace_bytes, void* stream,
                   ec_step_out* out) {
-  ec_status st = check_model(model);
-  if (st != EC_OK) return st;
-  st = check_cache(cache, model);
-  if (st != EC_OK) return st;
-  st = check_params(params, model, cache);
-  if (st != EC_OK) return st;
-  EC_REQUIRE(state && state->struct_size >= sizeof(ec_state) && state->tokens && state->masked &&
-                 state->plan,
-             EC_ERR_ARG, "ec_step: bad state");
-  EC_REQUIRE(out && out->struct_size >= sizeof(ec_step_out), EC_ERR_ARG, "ec_step: bad out");
-  const size_t need = carve_step(model, params, nullptr, 0, nullptr);
-  EC_REQUIRE(workspace && workspace_bytes >= need, EC_ERR_WORKSPACE,
-             "ec_step: workspace %zu < %zu bytes", workspace_bytes, need);
-  hipStream_t s = (hipStream_t)stream;
-  const uint32_t osz = out->struct_size;
-  memset(out, 0, sizeof(ec_step_out));
-  out->struct_size = osz;
-  if (state->n_masked <= 0) return EC_OK;
-
-  StepWs w;
-  carve_step(model, params, workspace, workspace_bytes, &w);
-  const PlanLayout lay(params->seq_len, params->k_recent);
-  StepResult* res = (StepResult*)(state->plan + lay.RES);
-  const bool full = state->t == 0 || state->refresh_next;
-  const int L = params->seq_len;
-  const int n_rows = full ? L : state->next_rows;
-  const int n_cand = state->next_cand;
-  const int32_t* rows = state->plan + (full ? lay.J0 : lay.R0);
-  // candidate indices into rows: positions themselves on a full step
-  const int32_t* cidx = state->plan + (full ? lay.C0 : lay.I0);
-
-  if (model->dtype == EC_BF16) {
-    // the LM head reduces the candidates' logits in its epilogue (no logits tensor)
-    const FusedEnt fe{(EntPart*)w.ent_ws, w.H, w.amax, w.conf};
-    st = run_forward(model, cache, state->tokens, rows, n_rows, cidx, n_cand, nullptr, nullptr, w.fwd, s,
-                     &fe);
-    if (st != EC_OK) return st;
-  } else {
-    st = run_forward(model, cache, state->tokens, rows, n_rows, cidx, n_cand, w.logits, nullptr,
-                     w.fwd, s);
-    if (st != EC_OK) return st;
-    TScope t(EC_T_ENTROPY, s, 0.0, (double)n_cand * model->vocab * esize(model->dtype));
-    st = entropy(model->dtype, w.logits, n_cand, model->vocab, model->vocab, nullptr, 0, w.H,
-                 w.amax, w.conf, nullptr, w.ent_ws, w.ent_bytes, s);
-    if (st != EC_OK) return st;
-  }
-  {
-    TScope t(EC_T_SELECT, s, 0.0, 0.0);
-    st = select_decode(w.H, w.amax, w.conf, n_cand, state->tokens, state->masked, state->plan,
-                       *params, res, s);
-  }
-  if (st != EC_OK) return st;
-  StepResult h;
-  EC_CHECK_HIP(hipMemcpyAsync(&h, res, sizeof(StepResult), hipMemcpyDeviceToHost, s));
-  EC_CHECK_HIP(hipStreamSynchronize(s));
-  if (g_tm.on) timing_collect();
-  if (!finish_step(h, *params, full, n_rows, n_cand, state, out)) {
-    set_error("ec_step: E is NaN at step %d; next step refreshes", state->t - 1);
-    return EC_ERR_NAN;
-  }
-  return EC_OK;
+  return step_impl(model, cache, state, params, workspace, workspace_bytes, stream, out, nullptr);
 }
+
+ec_status ec_step_probe(const ec_model_desc* model, const ec_cache_desc* cache, ec_state* state,
+                        const ec_params* params, void* workspace, size_t workspace_bytes, void* stream,
+                        ec_step_out* out, float* drift) {
+  EC_REQUIRE(drift, EC_ERR_ARG, "ec_step_probe: drift is NULL");
+  return step_impl(model, cache, state, params, workspace, workspace_bytes, stream, out, drift);
+}
+
 
 size_t ec_step_batch_workspace_size(const ec_model_desc* model, int32_t n_seq, const ec_params* params) {
   if (check_model(model) != EC_OK || check_params(params, model, nullptr) != EC_OK) return 0;

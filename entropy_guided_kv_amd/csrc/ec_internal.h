@@ -135,6 +135,16 @@ ec_status rmsnorm(ec_dtype dt, const float* h, int n_src, const int32_t* idx, in
 ec_status scatter(ec_dtype dt, void* kc, void* vc, int64_t L, int width, const void* kr,
                   const void* vr, const int32_t* idx, int n, hipStream_t s);
 
+// ---------------------------------------------------------------- KV-drift probe
+// old K / V rows of `rows` before a layer's QKV GEMM; per-row cosine distances after
+// it (dist[c * n + i], c = 0 K, 1 V); per layer mean / max over valid rows into
+// out[4 l + 2 c + {0, 1}] (dist of layer l at dist + l * layer_stride)
+ec_status drift_gather(ec_dtype dt, const void* kc, const void* vc, const int32_t* rows, int n, int L, int d,
+                       void* ok, void* ov, hipStream_t s);
+ec_status drift_rows(ec_dtype dt, const void* ok, const void* ov, const void* kc, const void* vc,
+                     const int32_t* rows, int n, int L, int d, float* dist, hipStream_t s);
+ec_status drift_reduce(const float* dist, int n_layers, int n, int64_t layer_stride, float* out, hipStream_t s);
+
 // ---------------------------------------------------------------- batch of sequences
 // per-sequence segments of the concatenated row / candidate lists of ec_step_batch
 struct BatchSeg {

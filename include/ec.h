@@ -219,6 +219,15 @@ ec_status ec_forward(const ec_model_desc* model, const ec_cache_desc* cache,
 /* ------------------------------------------------------------------------
  * Denoising state and ec_step.
  * ---------------------------------------------------------------------- */
+/* Candidates of a step (the pages note the entropy-guided skipping applies to
+ * different decoding strategies, sliding windows and blocks among them; EntropyCache
+ * explainer, Italian summary, section 5):
+ * EC_CAND_BLOCKS: the masked positions of the lowest block [P + bB, P + (b+1)B) that
+ *   still has a masked position (semi-autoregressive blocks of length B);
+ * EC_CAND_WINDOW: the masked positions among the B positions starting at the lowest
+ *   masked position (a window that slides as soon as its first position is decoded). */
+typedef enum ec_candidates { EC_CAND_BLOCKS = 0, EC_CAND_WINDOW = 1 } ec_candidates;
+
 typedef struct ec_params {
   uint32_t struct_size;
   float tau;               /* threshold in nats; E > tau -> refresh next step */
@@ -228,6 +237,7 @@ typedef struct ec_params {
   int32_t prompt_len;      /* P */
   int32_t seq_len;         /* L = P + masked positions */
   int32_t mask_id;         /* token id written at masked positions */
+  int32_t candidates;      /* ec_candidates: which masked positions may be decoded */
 } ec_params;
 
 typedef struct ec_state {
@@ -307,6 +317,22 @@ ec_status ec_step(const ec_model_desc* model, const ec_cache_desc* cache, ec_sta
  * a sequence with no masked position left is not stepped (its out has
  * n_decoded = 0). Synchronises `stream` once. Returns EC_ERR_NAN if any
  * sequence's E is NaN (that sequence's out->status says which). */
+/* ec_step_probe -- ec_step plus the KV-drift probe (the pages' drift measure: the
+ * cosine distance of cached vs freshly computed value vectors between consecutive
+ * steps, which they report tracks the previous step's E; EntropyCache explainer,
+ * Arabic technical summary, section 2, key observations). For every row the step
+ * recomputes (all L on a refresh) and every layer, dist = 1 - <old, new> / (|old| |new|)
+ * between the K (and the V) the cache held before the step and the one the step
+ * writes; drift (device float[4 * n_layers]) receives per layer l:
+ *   drift[4l] = mean K distance, drift[4l+1] = max K distance,
+ *   drift[4l+2] = mean V distance, drift[4l+3] = max V distance,
+ * over the rows whose old and new vectors are both non-zero (NaN if none: the
+ * first step of a zero-filled cache). Same workspace as ec_step (ec_step_workspace_size
+ * covers the probe's buffers); otherwise identical to ec_step. */
+ec_status ec_step_probe(const ec_model_desc* model, const ec_cache_desc* cache, ec_state* state,
+                        const ec_params* params, void* workspace, size_t workspace_bytes, void* stream,
+                        ec_step_out* out, float* drift);
+
 size_t ec_step_batch_workspace_size(const ec_model_desc* model, int32_t n_seq, const ec_params* params);
 ec_status ec_step_batch(const ec_model_desc* model, int32_t n_seq, const ec_cache_desc* caches,
                         ec_state* states, const ec_params* params, void* workspace,

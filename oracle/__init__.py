@@ -20,10 +20,12 @@ Modules:
               per-layer K/V cache (refresh = all rows, skip = partial rows).
   loop     -- the denoising loop: decode, entropy, threshold decision,
               recompute set of masked + k most recently decoded positions.
+  drift    -- the KV-drift measure (cosine distance of cached vs recomputed
+              K / V rows), the quantity the pages correlate with E.
 
 Parity pins: every function here is pinned by tests in tests/test_oracle_*.py
 against closed forms, library routines or brute force; the end-to-end
 trajectory has no worked example on the pages and is pinned only through the
 invariants of its parts (parity unpinned beyond those).
 """
-from . import entropy, model, loop  # noqa: F401
+from . import entropy, model, loop, drift  # noqa: F401

@@ -33,17 +33,24 @@ from typing import List, Optional
 
 import numpy as np
 
+from .drift import step_drift
 from .entropy import entropy_rows
 from .model import OracleModel, forward, new_cache
 
 
-def candidates(masked: np.ndarray, prompt_len: int, block_len: int) -> np.ndarray:
-    """Masked positions of the lowest block [P + bB, P + (b+1)B) that still has a mask."""
+def candidates(masked: np.ndarray, prompt_len: int, block_len: int, window: bool = False) -> np.ndarray:
+    """Masked positions of the lowest block [P + bB, P + (b+1)B) that still has a mask;
+    with ``window``, the masked positions among the B positions from the lowest masked one
+    (a sliding window, one of the decoding strategies the pages name: EntropyCache
+    explainer, Italian summary, section 5)."""
     pos = np.flatnonzero(masked)
     if pos.size == 0:
         return pos
-    b = (int(pos[0]) - prompt_len) // block_len
-    lo, hi = prompt_len + b * block_len, prompt_len + (b + 1) * block_len
+    if window:
+        lo = int(pos[0])
+    else:
+        lo = prompt_len + ((int(pos[0]) - prompt_len) // block_len) * block_len
+    hi = lo + block_len
     return pos[(pos >= lo) & (pos < hi)]
 
 
@@ -80,6 +87,7 @@ class StepRecord:
     emax: float               # E_{t+1} (float32 value)
     refresh_next: bool
     logits: Optional[np.ndarray] = None
+    drift: Optional[np.ndarray] = None  # [n_layers, 4] KV drift of the recomputed rows (probe)
 
 
 @dataclass
@@ -105,14 +113,16 @@ def _top2_margin(logits: np.ndarray) -> np.ndarray:
 
 
 def step(model: OracleModel, cfg, st: DecodeState, cache, tau: float,
-         keep_logits: bool = False) -> StepRecord:
-    """One denoising step; mutates ``st`` and ``cache``."""
+         keep_logits: bool = False, probe: bool = False) -> StepRecord:
+    """One denoising step; mutates ``st`` and ``cache``. With ``probe`` the record also
+    holds the KV drift of the recomputed rows (cache before vs after the forward)."""
     full = st.t == 0 or st.refresh_next
     if full:
         rows = np.arange(cfg.seq_len, dtype=np.int64)
     else:
         rows = recompute_set(st.masked, st.decode_log, cfg.k_recent)
-    cand = candidates(st.masked, cfg.prompt_len, cfg.block_len)
+    cand = candidates(st.masked, cfg.prompt_len, cfg.block_len, getattr(cfg, "window", False))
+    before = [[k.copy(), v.copy()] for k, v in cache] if probe else None
     out = forward(model, st.tokens, rows, cache, out_rows=cand)
     logits = out["logits"]
     h, a, c = entropy_rows(logits)
@@ -133,19 +143,20 @@ def step(model: OracleModel, cfg, st: DecodeState, cache, tau: float,
         emax = float(np.float32(hp.max()))
     st.refresh_next = bool(math.isnan(emax) or np.float32(emax) > np.float32(tau))
     rec = StepRecord(st.t, full, rows, cand, h, a, c, _top2_margin(logits), logits.max(axis=1),
-                     picked, ids, emax, st.refresh_next, logits if keep_logits else None)
+                     picked, ids, emax, st.refresh_next, logits if keep_logits else None,
+                     step_drift(before, cache, rows) if probe else None)
     st.t += 1
     return rec
 
 
 def run_entropycache(model: OracleModel, cfg, prompt: np.ndarray, tau: float,
-                     max_steps: Optional[int] = None, keep_logits: bool = False):
+                     max_steps: Optional[int] = None, keep_logits: bool = False, probe: bool = False):
     """Run the loop until no mask remains (or ``max_steps``). Returns (records, state, cache)."""
     st = init_state(cfg, prompt)
     cache = new_cache(model, cfg.seq_len)
     recs = []
     while st.masked.any() and (max_steps is None or st.t < max_steps):
-        recs.append(step(model, cfg, st, cache, tau, keep_logits))
+        recs.append(step(model, cfg, st, cache, tau, keep_logits, probe))
     return recs, st, cache
 
 

@@ -68,6 +68,7 @@ class DecodeConfig:
     taus: Tuple[float, ...]
     batch: int = 1
     seed: int = 0
+    window: bool = False  # candidates from a sliding window instead of fixed blocks
 
     @property
     def seq_len(self) -> int:

@@ -31,7 +31,7 @@ PEAKED_SCALE, PEAKED_TAU = 24.0, 2.15
 def _decoder(dm, cfg, tau):
     from entropy_guided_kv_amd import api
     dec = api.Decoder(dm, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len,
-                      cfg.k_recent, tau)
+                      cfg.k_recent, tau, window=cfg.window)
     return dec
 
 
@@ -181,3 +181,19 @@ def test_fused_lm_head_entropy_matches_stored_logits(n_cand_rows):
     assert o.ids == [int(a[i]) for i in picked]
     np.testing.assert_allclose(o.entropy, H[picked], rtol=0, atol=1e-5)
     np.testing.assert_allclose(o.maxprob, c[picked], rtol=1e-5, atol=0)
+
+
+@pytest.mark.parametrize("n,B", [(1, 8), (3, 5)])
+def test_tiny_sliding_window_trajectory(n, B):
+    """Sliding-window candidates (EC_CAND_WINDOW): the whole trajectory follows the oracle,
+    with refresh and skip steps mixed; it differs from block decoding."""
+    import dataclasses
+    base = synth.CONFIGS["tiny"]
+    cfg = dataclasses.replace(base, tokens_per_step=n, block_len=B, window=True)
+    w = synth.make_model(cfg.model, lm_head_scale=PEAKED_SCALE)
+    outs, recs = _compare_run(cfg, w, PEAKED_TAU)
+    flags = [o.refreshed for o in outs]
+    assert any(flags[1:]) and not all(flags[1:])
+    blk, _, _ = ol.run_entropycache(om.OracleModel(w), dataclasses.replace(cfg, window=False), synth.make_prompt(cfg),
+                                    PEAKED_TAU)
+    assert [list(r.picked) for r in blk] != [list(r.picked) for r in recs]

@@ -100,6 +100,34 @@ def test_select_matches_bruteforce(seed):
     np.testing.assert_array_equal(ol.select(cand, conf, n), _brute_select(cand, conf, n))
 
 
+def test_window_candidates_start_at_lowest_mask():
+    """Sliding window of B positions from the lowest masked position (not block-aligned)."""
+    masked = np.zeros(20, dtype=bool)
+    masked[[9, 12, 13, 17]] = True
+    np.testing.assert_array_equal(ol.candidates(masked, 4, 4, window=True), [9, 12])      # [9, 13)
+    np.testing.assert_array_equal(ol.candidates(masked, 4, 8, window=True), [9, 12, 13])  # [9, 17)
+    masked[9] = False
+    np.testing.assert_array_equal(ol.candidates(masked, 4, 4, window=True), [12, 13])     # [12, 16)
+    np.testing.assert_array_equal(ol.candidates(masked, 4, 6, window=True), [12, 13, 17])
+    assert ol.candidates(np.zeros(5, dtype=bool), 0, 2, window=True).size == 0
+
+
+def test_window_candidates_brute_force():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        L, P, B = int(rng.integers(2, 40)), 0, int(rng.integers(1, 9))
+        P = int(rng.integers(0, L))
+        masked = np.zeros(L, dtype=bool)
+        masked[P:] = rng.random(L - P) < 0.5
+        got = ol.candidates(masked, P, B, window=True)
+        pos = [p for p in range(L) if masked[p]]
+        want = [p for p in pos if pos and pos[0] <= p < pos[0] + B]
+        np.testing.assert_array_equal(got, want)
+        # the window always holds the lowest masked position; blocks hold it too
+        if pos:
+            assert got[0] == pos[0] and ol.candidates(masked, P, B)[0] == pos[0]
+
+
 def test_candidates_are_lowest_open_block():
     masked = np.zeros(20, dtype=bool)
     masked[[9, 12, 13, 17]] = True
