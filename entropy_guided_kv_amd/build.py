@@ -73,7 +73,9 @@ def build(verbose: bool = False, jobs: int = 0, debug: bool = False) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(compile_one, zip(srcs, objs)))
     tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # -z defs: every symbol the library references must resolve at link time (a kernel
+    # whose host stub the compiler dropped would otherwise surface only at load time)
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

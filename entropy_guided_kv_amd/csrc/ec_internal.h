@@ -95,8 +95,15 @@ struct EpiArgs {
 // K / V destination of row m for the QKV epilogues
 template <typename T>
 __device__ __forceinline__ T* kv_dst(const EpiArgs& e, int m, bool v) {
-  if (e.row_seq) return (T*)(v ? e.v_tab : e.k_tab)[e.row_seq[m]];
-  return (T*)(v ? e.v_cache : e.k_cache);
+  // selects between values held in registers (a select between the two fields'
+  // addresses would make the compiler spill them to a private array)
+  const uintptr_t kc = (uintptr_t)e.k_cache, vc = (uintptr_t)e.v_cache;
+  if (e.row_seq) {
+    const int q = e.row_seq[m];
+    const uintptr_t kt = (uintptr_t)e.k_tab[q], vt = (uintptr_t)e.v_tab[q];
+    return (T*)(v ? vt : kt);
+  }
+  return (T*)(v ? vc : kc);
 }
 
 size_t gemm_splitk_ws_bytes(int M, int N, int K, int kind, bool bf16);

@@ -10,7 +10,7 @@
 //   EPI_STORE  -- plain store (LM head logits).
 //
 // bf16 path: MFMA v_mfma_f32_32x32x16_bf16 (gfx950), both operands K-contiguous.
-// Global tiles are loaded straight into LDS (global_load_lds_dwordx4) in a
+// Global tiles are loaded straight into LDS (buffer_load_dwordx4 ... lds) in a
 // swizzled, unpadded layout; several K-steps are in flight while the MFMAs of
 // the current one run. The rotary and SwiGLU pairs come from packed weights
 // (ec_pack_weights) that place the two members of a pair 16 columns apart in
@@ -139,6 +139,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
+// buffer resource over [base, base + bytes) (raw buffer, no stride, gfx9 dword3)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from rsrc at voffset + soffset into LDS at lds + 16 * lane
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds, int voffset,
+                                                  int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voffset, soffset, 0, 0);
+}
+
 // workgroup barrier for LDS produced by direct-to-LDS loads: the waits are explicit
 // (the loads are tracked by vmcnt only), the fences keep the compiler from moving
 // LDS accesses across it
@@ -153,7 +163,8 @@ __device__ __forceinline__ void lds_stage_barrier() {
 // Staging: K advances 64 at a time; each stage of LDS holds BM + BN rows of 128
 // bytes, unpadded, with the 16-byte chunk c of row r stored at chunk c ^ ((r/2) % 8)
 // so that the 32 rows a fragment read touches fall in distinct banks. Global tiles
-// go straight to LDS with global_load_lds_dwordx4 (no staging registers): lane l
+// go straight to LDS with buffer_load_dwordx4 ... lds (no staging registers; the
+// buffer form, unlike the flat one, is tracked by vmcnt alone): lane l
 // of a load instruction fills bytes 16 l of the wavefront's 1 KB slice, and is
 // given the global address of the chunk that belongs there. NSTG stages rotate;
 // AHEAD of them are in flight. With LATE the stage refilled after the barrier of
@@ -163,7 +174,7 @@ __device__ __forceinline__ void lds_stage_barrier() {
 // Fragment reads of the next 16-wide K slice are issued in the middle of the
 // current slice's MFMAs; the first slice of K-step t+1 is read right after the
 // barrier that publishes it.
-template <int BM, int BN, int WM, int WN, int NSTG, bool LATE, int EPI, bool SPLIT>
+template <int BM, int BN, int WM, int WN, int NSTG, bool LATE, int EPI, bool SPLIT, int BKS = 64>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K,
                  int k_chunk, int splits, EpiArgs epi, float* __restrict__ part) {
@@ -171,13 +182,17 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   constexpr int NT = NW * 64;
   constexpr int WAVES_N = BN / WN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int ROWB = 128;                        // LDS bytes per tile row (64 bf16)
+  constexpr int CPR = BKS / 8;                     // 16-byte chunks per tile row
+  constexpr int ROWB = BKS * 2;                    // LDS bytes per tile row
+  constexpr int NS = BKS / 16;                     // 16-wide K slices per K-step
+  constexpr int SWS = CPR == 8 ? 1 : 2;            // chunk c of row r sits at c ^ ((r >> SWS) % CPR)
   constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr int LPA = BM * 8 / NT, LPB = BN * 8 / NT, LPT = LPA + LPB;
+  constexpr int LPA = BM * CPR / NT, LPB = BN * CPR / NT, LPT = LPA + LPB;
+  static_assert(BKS == 32 || BKS == 64, "K-step of 32 or 64");
   constexpr int AHEAD = LATE ? NSTG - 1 : NSTG;   // stages in flight
   constexpr int RD_AT = (TM * TN) / 2;             // fragment reads after this many MFMAs
   static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % WM == 0 && BN % WN == 0, "tile shape");
-  static_assert(LPA >= 1 && LPB >= 1 && LPA * NT == BM * 8 && LPB * NT == BN * 8, "load split");
+  static_assert(LPA >= 1 && LPB >= 1 && LPA * NT == BM * CPR && LPB * NT == BN * CPR, "load split");
   static_assert(AHEAD >= 2 && (AHEAD - 1) * LPT < 64, "pipeline depth");
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -189,50 +204,49 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   const int nt = rest / splits;
   const int m0 = mt * BM, n0 = nt * BN;
   const int kbeg = kz * k_chunk;
-  const int nk = k_chunk / 64;
+  const int nk = k_chunk / BKS;
 
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-  // per-lane global source of each direct-to-LDS load (rows past M / N clamp to the
-  // last row; their products land in rows / columns the epilogue skips)
-  const bf16* ga[LPA];
-  const bf16* gb[LPB];
+  // Direct-to-LDS loads through buffer resources (buffer_load_dwordx4 ... lds): the
+  // per-lane byte offset of each load is fixed, the K-step advances the scalar
+  // offset. Rows past M / N clamp to the last row (their products land in rows /
+  // columns the epilogue skips); the resource's extent bounds every access.
+  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(A, (int64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(B, (int64_t)N * K * 2);
+  int oa[LPA], ob[LPB];
 #pragma unroll
   for (int i = 0; i < LPA; ++i) {
     const int q = (i * NW + wave) * 64 + lane;
-    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
-    ga[i] = A + (int64_t)min(m0 + r, M - 1) * K + kbeg + c * 8;
+    const int r = q / CPR, c = (q % CPR) ^ ((r >> SWS) & (CPR - 1));
+    oa[i] = (int)(((int64_t)min(m0 + r, M - 1) * K + kbeg + c * 8) * 2);
   }
 #pragma unroll
   for (int i = 0; i < LPB; ++i) {
     const int q = (i * NW + wave) * 64 + lane;
-    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
-    gb[i] = B + (int64_t)min(n0 + r, N - 1) * K + kbeg + c * 8;
+    const int r = q / CPR, c = (q % CPR) ^ ((r >> SWS) & (CPR - 1));
+    ob[i] = (int)(((int64_t)min(n0 + r, N - 1) * K + kbeg + c * 8) * 2);
   }
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
     unsigned char* base = smem + stage * STAGE;
+    const int ks = kt * BKS * 2;
 #pragma unroll
-    for (int i = 0; i < LPA; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(ga[i] + kt * 64),
-                                       (lds_void_t*)(base + (i * NW + wave) * 1024), 16, 0, 0);
+    for (int i = 0; i < LPA; ++i) buffer_load_lds16(rA, base + (i * NW + wave) * 1024, oa[i], ks);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(gb[i] + kt * 64),
-                                       (lds_void_t*)(base + BM * ROWB + (i * NW + wave) * 1024), 16, 0,
-                                       0);
+    for (int i = 0; i < LPB; ++i) buffer_load_lds16(rB, base + BM * ROWB + (i * NW + wave) * 1024, ob[i], ks);
   };
 
   // fragment addresses: A/B operand of lane = row lane%32 of the tile, K chunk
-  // 2*kk + lane/32; the swizzle term depends on the row's bits 1..3 only
+  // 2*kk + lane/32; the swizzle term depends only on the row bits below 32
   const int lrow = lane % 32, hi = lane / 32;
-  const int sw16 = (((lrow >> 1) & 7) ^ hi) * 16;
+  const int swr = (lrow >> SWS) & (CPR - 1);
   const int a_row = (wm * WM + lrow) * ROWB;
   const int b_row = BM * ROWB + (wn * WN + lrow) * ROWB;
-  int koff[4];
+  int koff[NS];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) koff[kk] = sw16 ^ (32 * kk);
+  for (int kk = 0; kk < NS; ++kk) koff[kk] = ((2 * kk + hi) ^ swr) * 16;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -276,9 +290,8 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
 
   for (int t = 0; t < nk; ++t) {
     const int stage = t % NSTG;
-    slice(0, stage, 1, 1);
-    slice(1, stage, 2, 0);
-    slice(0, stage, 3, 1);
+#pragma unroll
+    for (int kk = 0; kk + 1 < NS; ++kk) slice(kk & 1, stage, kk + 1, (kk + 1) & 1);
     if (t + 1 < nk) {
       if (!LATE) wait_lgkmcnt0();
       // this lane's loads of step t+1 have landed once at most the later steps'
@@ -288,7 +301,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
       if (t + AHEAD < nk) issue(t + AHEAD, (t + AHEAD) % NSTG);
     }
     // on the last step the read of stage (t+1) % NSTG stays inside LDS and is unused
-    slice(1, (t + 1) % NSTG, 0, 0);
+    slice((NS - 1) & 1, (t + 1) % NSTG, 0, 0);
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -582,11 +595,11 @@ Plan plan_bf16(int M, int N, int K, int kind) {
   return best;
 }
 
-template <int BM, int BN, int WM, int WN, int NSTG, bool LATE, int EPI>
+template <int BM, int BN, int WM, int WN, int NSTG, bool LATE, int EPI, int BKS = 64>
 ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, int M, int N, int K,
                       const EpiArgs& epi, float* part, hipStream_t s) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  constexpr size_t lds = (size_t)NSTG * (BM + BN) * 128;
+  constexpr size_t lds = (size_t)NSTG * (BM + BN) * BKS * 2;
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int grid = p.MT * p.NT * p.S;
   auto run = [&](auto kern) -> ec_status {
@@ -600,9 +613,9 @@ ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, int M, int N,
     return EC_OK;
   };
   if constexpr (EPI != EPI_ENTROPY) {
-    if (p.S > 1) return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, true>);
+    if (p.S > 1) return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, true, BKS>);
   }
-  return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, false>);
+  return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, false, BKS>);
 }
 
 template <int EPI>

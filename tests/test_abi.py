@@ -33,6 +33,11 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(_lib.EXPORTS) <= set(names)
 
 
+def test_library_resolves_every_symbol_at_load():
+    # RTLD_NOW: an unresolved symbol (e.g. a kernel stub the compiler dropped) fails here
+    C.CDLL(_lib.LIB_PATH, mode=os.RTLD_NOW)
+
+
 def test_version_and_error_string(lib):
     assert lib.ec_version() == 10100
     assert isinstance(lib.ec_last_error(), bytes)
