@@ -23,7 +23,10 @@
 // when a row max exceeds it by 2^8, so most tiles skip the rescale. Q stays
 // in registers; K and V tiles of 64 keys are double-buffered in LDS, the next
 // tile's global loads in flight during the current tile's MFMAs, shared by the
-// 4 wavefronts (128 queries) of a workgroup. When heads x query tiles
+// 8 wavefronts of a workgroup: 4 groups of 32 queries (128 queries), the two
+// wavefronts of a group taking the lower and the upper 32 keys of every tile
+// (two wavefronts per SIMD: one's softmax and LDS reads overlap the other's
+// MFMAs) and combining their (m, l, o) through LDS at the end. When heads x query tiles
 // under-fill the 256 CUs, the key range is split over workgroups and a merge
 // kernel combines (m, l, o) exactly.
 #include "ec_internal.h"
@@ -34,7 +37,8 @@ namespace ec {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;      // merge and fp32 kernels
+constexpr int kAttnThreads = 512;  // MFMA kernel: 8 wavefronts
 constexpr int D = 128;       // head_dim of the MFMA kernel
 constexpr int BQ = 128;      // queries per workgroup (32 per wavefront)
 constexpr int BKV = 64;      // keys per LDS stage
@@ -48,20 +52,24 @@ typedef __attribute__((address_space(3))) bf16 lds_bf16;
 
 // grid: (query tiles, heads, splits)
 template <bool SPLIT>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kAttnThreads)
 attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                  const bf16* __restrict__ vc, int r, int L, int H, float scale_log2,
                  int kv_chunk, bf16* __restrict__ out, float* __restrict__ po,
                  float* __restrict__ pml) {
   // K and V tiles in natural [key][dim] layout, double-buffered
-  __shared__ __align__(16) bf16 sK[2][BKV * KS];
-  __shared__ __align__(16) bf16 sV[2][BKV * KS];
+  // one allocation: after the loop the whole of it holds the (m, l, o) hand-over
+  __shared__ __align__(16) bf16 skv[2][2][BKV * KS];
+  bf16 (*sK)[BKV * KS] = skv[0];
+  bf16 (*sV)[BKV * KS] = skv[1];
+  static_assert(4 * 64 * (D / 2 + 2) * sizeof(float) <= sizeof(skv), "hand-over exceeds the K/V tiles");
 
   const int qt = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int qw = wave % 4, kh = wave / 4;   // query group, key half of every tile
   const int lq = lane % 32, g = lane / 32;
   const int64_t HD = (int64_t)H * D;
-  const int qrow = qt * BQ + wave * 32 + lq;  // this lane's query (column of S^T)
+  const int qrow = qt * BQ + qw * 32 + lq;  // this lane's query (column of S^T)
   const bool qok = qrow < r;
 
   // Q fragments (B operand of S^T): Q[qrow][16kk + 8g .. +7]
@@ -83,14 +91,14 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   const int kv_hi = min(L, kv_lo + kv_chunk);
   const int ntiles = (kv_hi - kv_lo + BKV - 1) / BKV;
 
-  // staging: 64 keys x 16 vectors of 8 dims per tile, 4 vectors per thread for K and for V
-  constexpr int NV = BKV * (D / 8) / kThreads;
+  // staging: 64 keys x 16 vectors of 8 dims per tile, 2 vectors per thread for K and for V
+  constexpr int NV = BKV * (D / 8) / kAttnThreads;
   bf16x8 rk[NV], rv[NV];
   auto gload = [&](int t) __attribute__((always_inline)) {
     const int kv0 = kv_lo + t * BKV;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int v = tid + i * kThreads;
+      const int v = tid + i * kAttnThreads;
       const int key = min(kv0 + v / (D / 8), L - 1);  // rows past the end are masked below
       const int dv = (v % (D / 8)) * 8;
       rk[i] = *reinterpret_cast<const bf16x8*>(kc + (int64_t)key * HD + h * D + dv);
@@ -100,7 +108,7 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   auto sstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int v = tid + i * kThreads;
+      const int v = tid + i * kAttnThreads;
       const int off = (v / (D / 8)) * KS + (v % (D / 8)) * 8;
       *reinterpret_cast<bf16x8*>(&sK[buf][off]) = rk[i];
       *reinterpret_cast<bf16x8*>(&sV[buf][off]) = rv[i];
@@ -123,8 +131,8 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
     if (t + 1 < ntiles) gload(t + 1);
     const bf16* kt = sK[buf];
     const lds_bf16* vt = (const lds_bf16*)sV[buf];
-#pragma unroll
-    for (int sub = 0; sub < BKV / 32; ++sub) {
+    {
+      const int sub = kh;  // this wavefront's 32 keys of the tile
       // ---- S^T[32 keys, 32 queries] (raw dot products)
       f32x16 st;
 #pragma unroll
@@ -188,6 +196,31 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
     __syncthreads();
   }
 
+  // the upper-key wavefront of each query group hands (m, l, o) to the lower one through
+  // LDS (the K/V tiles are no longer read after the loop's last barrier)
+  {
+    float* xb = reinterpret_cast<float*>(&skv[0][0][0]) + (qw * 64 + lane) * (D / 2 + 2);
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xb[16 * i + v] = o[i][v];
+      xb[D / 2] = m_ref;
+      xb[D / 2 + 1] = l_run;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m2 = xb[D / 2], l2 = xb[D / 2 + 1];
+    const float mm = fmaxf(m_ref, m2);
+    const float a1 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
+    const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[i][v] = o[i][v] * a1 + xb[16 * i + v] * a2;
+    l_run = l_run * a1 + l2 * a2;
+    m_ref = mm;
+  }
   if (!qok) return;
   // o[i][v]: dim = 32i + 8(v/4) + 4g + v%4 of query qrow
   if (!SPLIT) {
@@ -324,7 +357,7 @@ ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, 
   const float sl = scale * kLog2e;
   dim3 grid(p.qtiles, H, p.splits);
   if (p.splits == 1) {
-    attn_bf16_kernel<false><<<grid, kThreads, 0, s>>>((const bf16*)q, (const bf16*)k,
+    attn_bf16_kernel<false><<<grid, kAttnThreads, 0, s>>>((const bf16*)q, (const bf16*)k,
                                                       (const bf16*)v, r, L, H, sl, p.chunk,
                                                       (bf16*)out, nullptr, nullptr);
     EC_CHECK_LAUNCH("attn_bf16_kernel");
@@ -334,7 +367,7 @@ ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, 
   EC_REQUIRE(ws && ws_bytes >= need, EC_ERR_WORKSPACE, "attn: workspace %zu < %zu", ws_bytes, need);
   float* po = (float*)ws;
   float* pml = po + (size_t)p.splits * r * H * Dh;
-  attn_bf16_kernel<true><<<grid, kThreads, 0, s>>>((const bf16*)q, (const bf16*)k, (const bf16*)v,
+  attn_bf16_kernel<true><<<grid, kAttnThreads, 0, s>>>((const bf16*)q, (const bf16*)k, (const bf16*)v,
                                                    r, L, H, sl, p.chunk, nullptr, po, pml);
   EC_CHECK_LAUNCH("attn_bf16_kernel");
   const int64_t n = (int64_t)r * H * Dh;

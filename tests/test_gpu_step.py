@@ -6,7 +6,9 @@ and ids, E_{t+1} and the next step's flag. Decoded ids and positions must be
 identical wherever the oracle's top-1/top-2 logit margin of the decoded rows
 exceeds 1e-2 (of max(1, |top-1|) for bf16 models, whose logits are stored
 with a step of 1/64 at |logit| >= 2) and the confidence gap at the selection
-cut exceeds 1e-2 (in log space); the first step that fails that gate ends the
+cut exceeds 1e-2 in log space (for bf16 models, of max(1, |top-1|) of the two
+rows at the cut: a rounding flip of a stored top-1 logit shifts that row's
+log-confidence by one bf16 step of the logit); the first step that fails that gate ends the
 comparison (the two trajectories may legitimately part there). E within 1e-3
 nats for fp32 models; for bf16 models E is checked against the oracle's
 entropy of the device's own logits (within 1e-3) by the forward tests, and
@@ -41,9 +43,15 @@ def _gate_ok(rec, n, dtype):
     ok = margin_gate(rec.top1, rec.margin) if dtype == "bf16" else rec.margin > 1e-2
     if not all(ok[i] for i in idx):
         return False
-    c = np.sort(np.log(rec.maxprob))[::-1]
-    if len(c) > n and abs(c[n - 1] - c[n]) <= 1e-2:
-        return False
+    order = np.argsort(-np.log(rec.maxprob), kind="stable")
+    if len(order) > n:
+        a, b = order[n - 1], order[n]
+        gap = abs(np.log(rec.maxprob[a]) - np.log(rec.maxprob[b]))
+        # a bf16 rounding flip of a row's top-1 logit moves its log-confidence by one
+        # bf16 step of that logit, so for bf16 the cut scales like the margin gate
+        scale = max(1.0, abs(float(rec.top1[a])), abs(float(rec.top1[b]))) if dtype == "bf16" else 1.0
+        if gap <= 1e-2 * scale:
+            return False
     return True
 
 
