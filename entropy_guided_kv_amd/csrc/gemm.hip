@@ -128,6 +128,7 @@ __device__ __forceinline__ int xcd_remap(int pid, int nblk) {
 // Any column tile that is a multiple of 32 then keeps every pair in one wavefront.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((address_space(1))) bf16x4 gbf16x4;
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
@@ -281,6 +282,27 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // QKV: each lane keeps the position and the K / V cache base of slab row lane % 32
+  // (one per 32-row MFMA slab), loaded before the main loop so that the epilogue's
+  // rotary-table loads do not wait behind them
+  int pre_pos[TM];
+  uintptr_t pre_k[TM], pre_v[TM];
+  if constexpr (EPI == EPI_QKV && !SPLIT) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = min(m0 + wm * WM + 32 * i + (lane & 31), M - 1);
+      pre_pos[i] = epi.rows[m];
+      if (epi.row_seq) {
+        const int q = epi.row_seq[m];
+        pre_k[i] = (uintptr_t)epi.k_tab[q];
+        pre_v[i] = (uintptr_t)epi.v_tab[q];
+      } else {
+        pre_k[i] = (uintptr_t)epi.k_cache;
+        pre_v[i] = (uintptr_t)epi.v_cache;
+      }
+    }
+  }
+
 #pragma unroll
   for (int st = 0; st < AHEAD; ++st)
     if (st < nk) issue(st, st);
@@ -364,10 +386,14 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
       continue;
     }
     if (EPI == EPI_SWIGLU && !SPLIT) {
-      // units: (row, 4 gate columns); the up partner is 16 columns on
+      // units: (row, 4 gate columns); the up partner is 16 columns on. The unit loops
+      // have a constant trip count (32 * WN / 8 and 32 * WN / 4 units, multiples of
+      // 64) so that they unroll and their global loads issue together.
       constexpr int UG = C4 / 2;
+      static_assert((32 * UG) % 64 == 0, "unit count");
 #pragma unroll
-      for (int u = lane; u < 32 * UG; u += 64) {
+      for (int it = 0; it < 32 * UG / 64; ++it) {
+        const int u = lane + 64 * it;
         const int r = u / UG, k = u % UG;
         const int c = (k / 4) * 32 + (k % 4) * 4;
         const int m = mrow + r, pc = n0 + wn * WN + c;
@@ -382,45 +408,97 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
       }
       continue;
     }
+    static_assert((32 * C4) % 64 == 0, "unit count");
+    if constexpr (EPI == EPI_QKV && !SPLIT) {
+      // units: (row, 4 first-half packed columns c) with their rotary partners at c + 16;
+      // a lane computes both halves of a pair, so one cos / sin load serves both. All
+      // table loads of the slab are issued before its first store (on this target stores
+      // and loads share one counter, so a store would otherwise make the next unit's
+      // loads wait for it).
+      constexpr int UP = C4 / 2;  // pairs per slab row
+      constexpr int NPI = 32 * UP / 64;
+      static_assert((32 * UP) % 64 == 0, "pair count");
+      f32x4 tcs[NPI], tsn[NPI];
 #pragma unroll
-    for (int u = lane; u < 32 * C4; u += 64) {
+      for (int it = 0; it < NPI; ++it) {
+        const int u = lane + 64 * it;
+        const int r = u / UP, k = u % UP;
+        const int pc = n0 + wn * WN + (k / 4) * 32 + (k % 4) * 4;
+        const int p = pc & (D - 1);  // D is a power of two
+        const int rc = (p >> 5) * 16 + (p & 15);
+        const int pos = __shfl(pre_pos[i], r);
+        const bool pos_ok = pos >= 0 && pos < epi.seq_len;
+        const int64_t tp = (int64_t)(pos_ok ? pos : 0) * half + rc;
+        tcs[it] = *reinterpret_cast<const f32x4*>(epi.rope_cos + tp);
+        tsn[it] = *reinterpret_cast<const f32x4*>(epi.rope_sin + tp);
+      }
+      const bool per_row_kv = epi.row_seq != nullptr;
+#pragma unroll
+      for (int it = 0; it < NPI; ++it) {
+        const int u = lane + 64 * it;
+        const int r = u / UP, k = u % UP;
+        const int c = (k / 4) * 32 + (k % 4) * 4;
+        const int m = mrow + r, pc = n0 + wn * WN + c;
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(slab + r * ES + c);
+        const f32x4 x2 = *reinterpret_cast<const f32x4*>(slab + r * ES + c + 16);
+        const int p = pc & (D - 1), hb = pc - p;
+        const int rc = (p >> 5) * 16 + (p & 15);
+        const int sec = (hb >= d) + (hb >= 2 * d);  // 0: q, 1: k, 2: v
+        const int hcol = hb - sec * d + rc;         // first-half column; its partner is + D/2
+        const int pos = __shfl(pre_pos[i], r);
+        const bool pos_ok = pos >= 0 && pos < epi.seq_len;
+        const bool rot = sec < 2 && pos_ok;
+        // first half: x1 cos - x2 sin; second half: x1 sin + x2 cos
+        bf16x4 o1, o2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = fmaf(x1[e], tcs[it][e], -x2[e] * tsn[it][e]);
+          const float b = fmaf(x1[e], tsn[it][e], x2[e] * tcs[it][e]);
+          o1[e] = (bf16)(rot ? a : x1[e]);
+          o2[e] = (bf16)(rot ? b : x2[e]);
+        }
+        uintptr_t kb = (uintptr_t)epi.k_cache, vb = (uintptr_t)epi.v_cache;
+        if (per_row_kv) {
+          kb = ((uintptr_t)(uint32_t)__shfl((int)(uint32_t)pre_k[i], r)) |
+               ((uintptr_t)(uint32_t)__shfl((int)(uint32_t)(pre_k[i] >> 32), r) << 32);
+          vb = ((uintptr_t)(uint32_t)__shfl((int)(uint32_t)pre_v[i], r)) |
+               ((uintptr_t)(uint32_t)__shfl((int)(uint32_t)(pre_v[i] >> 32), r) << 32);
+        }
+        if (m >= M || pc >= N) continue;
+        uintptr_t dst;
+        if (sec == 0) dst = (uintptr_t)((bf16*)epi.out + (int64_t)m * d + hcol);
+        else if (pos_ok) dst = (uintptr_t)((bf16*)(sec == 2 ? vb : kb) + (int64_t)pos * d + hcol);
+        else continue;
+        // the destination is device memory: global (not flat) stores, which neither wait
+        // on nor alias the LDS slab reads
+        gbf16x4* g = (gbf16x4*)dst;
+        g[0] = o1;
+        *(gbf16x4*)(dst + half * sizeof(bf16)) = o2;
+      }
+      continue;
+    }
+#pragma unroll
+    for (int it = 0; it < 32 * C4 / 64; ++it) {
+      const int u = lane + 64 * it;
       const int r = u / C4, c = (u % C4) * 4;
       const int m = mrow + r, pc = n0 + wn * WN + c;
-      if (m >= M || pc >= N) continue;
       const f32x4 x = *reinterpret_cast<const f32x4*>(slab + r * ES + c);
+      if (EPI == EPI_RESID && !SPLIT) {
+        // the residual load is unconditional (clamped) so that the loads of the unrolled
+        // loop issue together; the store is predicated
+        f32x4* hp = reinterpret_cast<f32x4*>(epi.resid + (int64_t)min(m, M - 1) * epi.ldo + min(pc, N - 4));
+        const f32x4 h0 = *hp;
+        if (m < M && pc < N) *hp = h0 + x;
+        continue;
+      }
+      if (m >= M || pc >= N) continue;
       if (SPLIT) {
         *reinterpret_cast<f32x4*>(part + ((int64_t)kz * M + m) * N + pc) = x;
-      } else if (EPI == EPI_RESID) {
-        f32x4* hp = reinterpret_cast<f32x4*>(epi.resid + (int64_t)m * epi.ldo + pc);
-        *hp = *hp + x;
       } else if (EPI == EPI_STORE) {
         bf16x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = (bf16)x[e];
         *reinterpret_cast<bf16x4*>((bf16*)epi.out + (int64_t)m * epi.ldo + pc) = o;
-      } else {  // EPI_QKV
-        const f32x4 y = *reinterpret_cast<const f32x4*>(slab + r * ES + (c ^ 16));
-        const int hb = pc - pc % D, p = pc - hb, pu = p & 31;
-        const bool second = pu >= 16;
-        const int rc = (p >> 5) * 16 + (pu & 15);  // rotary index of the first column
-        const int sec = hb / d;
-        const int hcol = hb % d + rc + (second ? half : 0);
-        const int pos = epi.rows[m];
-        const bool pos_ok = pos >= 0 && pos < epi.seq_len;
-        f32x4 out = x;
-        if (sec < 2 && pos_ok) {
-          const f32x4 cs = *reinterpret_cast<const f32x4*>(epi.rope_cos + (int64_t)pos * half + rc);
-          const f32x4 sn = *reinterpret_cast<const f32x4*>(epi.rope_sin + (int64_t)pos * half + rc);
-          // first half: x1 cos - x2 sin; second half: x1 sin + x2 cos (x1 = partner)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) out[e] = second ? y[e] * sn[e] + x[e] * cs[e] : x[e] * cs[e] - y[e] * sn[e];
-        }
-        bf16x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (bf16)out[e];
-        if (sec == 0) *reinterpret_cast<bf16x4*>((bf16*)epi.out + (int64_t)m * d + hcol) = o;
-        else if (pos_ok)
-          *reinterpret_cast<bf16x4*>(kv_dst<bf16>(epi, m, sec == 2) + (int64_t)pos * d + hcol) = o;
       }
     }
   }
@@ -666,9 +744,10 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
     return EC_OK;
   }
   EC_REQUIRE(K % BK == 0, EC_ERR_UNSUPPORTED, "gemm: K=%d not a multiple of %d", K, BK);
+  EC_REQUIRE(N % 4 == 0, EC_ERR_UNSUPPORTED, "gemm: N=%d not a multiple of 4 (4-column output vectors)", N);
   if (kind == EPI_QKV)
-    EC_REQUIRE(epi.head_dim % 32 == 0 && N % epi.head_dim == 0, EC_ERR_UNSUPPORTED,
-               "gemm: packed QKV needs head_dim %% 32 == 0");
+    EC_REQUIRE(epi.head_dim >= 32 && (epi.head_dim & (epi.head_dim - 1)) == 0 && N % epi.head_dim == 0,
+               EC_ERR_UNSUPPORTED, "gemm: packed QKV needs a power-of-two head_dim >= 32");
   if (kind == EPI_SWIGLU)
     EC_REQUIRE(N % 16 == 0, EC_ERR_UNSUPPORTED, "gemm: packed SwiGLU needs F %% 16 == 0");
   const int NB = b_rows(N, kind);
