@@ -78,6 +78,9 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
     const bf16* src = q + (int64_t)(qok ? qrow : 0) * HD + h * D + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) fq[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
+    // wait here: left to the compiler, the wait for Q would sit at its first use inside
+    // the tile loop and, repeated every tile, would also wait for the next tile's loads
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));  // vmcnt(0)
   }
 
   f32x16 o[D / 32];
@@ -137,11 +140,13 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
       f32x16 st;
 #pragma unroll
       for (int v = 0; v < 16; ++v) st[v] = 0.f;
+      // all K fragments first, so that the MFMA chain waits for LDS once
+      bf16x8 fk[D / 16];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 fk = *reinterpret_cast<const bf16x8*>(kt + (sub * 32 + lq) * KS + 16 * kk + 8 * g);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk, fq[kk], st, 0, 0, 0);
-      }
+      for (int kk = 0; kk < D / 16; ++kk)
+        fk[kk] = *reinterpret_cast<const bf16x8*>(kt + (sub * 32 + lq) * KS + 16 * kk + 8 * g);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[kk], fq[kk], st, 0, 0, 0);
       // key of st[v]: kv0 + sub*32 + 8(v/4) + 4g + v%4; mask keys past the end of the range
       if (kv0 + sub * 32 + 32 > kv_hi) {
 #pragma unroll
@@ -172,7 +177,9 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
         fp[v / 8][v % 8] = (bf16)p;
       }
       l_run += psum + __shfl_xor(psum, 32);
-      // ---- O^T[d, q] += V^T[d, keys] P^T[keys, q]; A operand by transpose reads
+      // ---- O^T[d, q] += V^T[d, keys] P^T[keys, q]; A operand by transpose reads, all
+      // eight fragments read before the MFMAs
+      bf16x8 fv[2][D / 32];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -181,16 +188,18 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
           const lds_bf16* p0 = vt + kb * KS + 32 * i + tr_dim;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * KS));
-          bf16x8 fv;
           const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            fv[e] = l4[e];
-            fv[4 + e] = h4[e];
+            fv[c][i][e] = l4[e];
+            fv[c][i][4 + e] = h4[e];
           }
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv, fp[c], o[i], 0, 0, 0);
         }
       }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[c][i], fp[c], o[i], 0, 0, 0);
     }
     if (t + 1 < ntiles) sstore(buf ^ 1);
     __syncthreads();

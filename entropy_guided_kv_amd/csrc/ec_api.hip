@@ -98,10 +98,16 @@ ec_status check_model(const ec_model_desc* m) {
   EC_REQUIRE(m->weight_layout == (packed ? EC_LAYOUT_PACKED : EC_LAYOUT_PLAIN), EC_ERR_ARG,
              "model: weight_layout must be %s for %s models (see ec_pack_weights)",
              packed ? "EC_LAYOUT_PACKED" : "EC_LAYOUT_PLAIN", packed ? "bf16" : "fp32");
+  auto a16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+  EC_REQUIRE(a16(m->embed) && a16(m->final_norm) && a16(m->lm_head) && a16(m->rope_cos) && a16(m->rope_sin),
+             EC_ERR_ARG, "model: device arrays must be 16-byte aligned");
   for (int l = 0; l < m->n_layers; ++l) {
     const ec_layer_weights& w = m->layers[l];
     EC_REQUIRE(w.attn_norm && w.wqkv && w.wo && w.mlp_norm && w.w_gate && (packed || w.w_up) && w.w_down,
                EC_ERR_ARG, "model: null weight in layer %d", l);
+    EC_REQUIRE(a16(w.attn_norm) && a16(w.wqkv) && a16(w.wo) && a16(w.mlp_norm) && a16(w.w_gate) &&
+                   a16(w.w_up) && a16(w.w_down),
+               EC_ERR_ARG, "model: weights of layer %d must be 16-byte aligned", l);
   }
   if (m->dtype == EC_BF16) {
     EC_REQUIRE(m->head_dim == 128, EC_ERR_UNSUPPORTED, "bf16 model: head_dim must be 128");
@@ -120,8 +126,11 @@ ec_status check_cache(const ec_cache_desc* c, const ec_model_desc* m) {
   EC_REQUIRE(c->seq_len >= 1 && c->k && c->v, EC_ERR_ARG, "cache: bad seq_len or null arrays");
   EC_REQUIRE(c->seq_len <= m->rope_max_pos, EC_ERR_ARG, "cache: seq_len %d > rope_max_pos %d",
              c->seq_len, m->rope_max_pos);
-  for (int l = 0; l < m->n_layers; ++l)
+  for (int l = 0; l < m->n_layers; ++l) {
     EC_REQUIRE(c->k[l] && c->v[l], EC_ERR_ARG, "cache: null pointer for layer %d", l);
+    EC_REQUIRE((((uintptr_t)c->k[l] | (uintptr_t)c->v[l]) & 15) == 0, EC_ERR_ARG,
+               "cache: layer %d arrays must be 16-byte aligned", l);
+  }
   return EC_OK;
 }
 

@@ -33,6 +33,28 @@ embed_kernel(const T* __restrict__ table, int vocab, const int32_t* __restrict__
 }
 
 // out[i, :] = T(h[src, :] / sqrt(mean(h[src]^2) + eps) * gain), src = idx ? idx[i] : i
+// The row is read once into registers when d <= 4 * kThreads * kNormRegs (d = 4096 takes
+// 4 float4 per thread); wider rows are read a second time for the scaling pass. Each
+// thread sums its own float4s in ascending order either way, so both forms round alike.
+constexpr int kNormRegs = 8;
+
+__device__ __forceinline__ void store4(bf16* y, float a, float b, float c, float e) {
+  bf16x4 o;
+  o[0] = (bf16)a;
+  o[1] = (bf16)b;
+  o[2] = (bf16)c;
+  o[3] = (bf16)e;
+  *reinterpret_cast<bf16x4*>(y) = o;
+}
+__device__ __forceinline__ void store4(float* y, float a, float b, float c, float e) {
+  *reinterpret_cast<float4*>(y) = make_float4(a, b, c, e);
+}
+__device__ __forceinline__ float4 load_gain4(const bf16* g) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(g);
+  return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+__device__ __forceinline__ float4 load_gain4(const float* g) { return *reinterpret_cast<const float4*>(g); }
+
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 rmsnorm_kernel(const float* __restrict__ h, int n_src, const int32_t* __restrict__ idx, int d,
@@ -41,10 +63,23 @@ rmsnorm_kernel(const float* __restrict__ h, int n_src, const int32_t* __restrict
   int src = idx ? idx[i] : i;
   if (src < 0 || src >= n_src) src = 0;  // invalid index: normalise row 0 (no out-of-range read)
   const float* x = h + (int64_t)src * d;
+  const bool in_regs = d <= 4 * kThreads * kNormRegs;
+  float4 v[kNormRegs];
   float ss = 0.f;
-  for (int j = threadIdx.x * 4; j < d; j += kThreads * 4) {
-    float4 v = *reinterpret_cast<const float4*>(x + j);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  if (in_regs) {
+#pragma unroll
+    for (int k = 0; k < kNormRegs; ++k) {
+      const int j = (threadIdx.x + k * kThreads) * 4;
+      if (j < d) {
+        v[k] = *reinterpret_cast<const float4*>(x + j);
+        ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+      }
+    }
+  } else {
+    for (int j = threadIdx.x * 4; j < d; j += kThreads * 4) {
+      const float4 w = *reinterpret_cast<const float4*>(x + j);
+      ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
+    }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
@@ -56,12 +91,21 @@ rmsnorm_kernel(const float* __restrict__ h, int n_src, const int32_t* __restrict
   for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
   const float rs = 1.0f / sqrtf(tot / (float)d + eps);
   T* y = out + (int64_t)i * d;
-  for (int j = threadIdx.x * 4; j < d; j += kThreads * 4) {
-    float4 v = *reinterpret_cast<const float4*>(x + j);
-    y[j + 0] = from_f<T>(v.x * rs * to_f(gain[j + 0]));
-    y[j + 1] = from_f<T>(v.y * rs * to_f(gain[j + 1]));
-    y[j + 2] = from_f<T>(v.z * rs * to_f(gain[j + 2]));
-    y[j + 3] = from_f<T>(v.w * rs * to_f(gain[j + 3]));
+  if (in_regs) {
+#pragma unroll
+    for (int k = 0; k < kNormRegs; ++k) {
+      const int j = (threadIdx.x + k * kThreads) * 4;
+      if (j < d) {
+        const float4 g = load_gain4(gain + j);
+        store4(y + j, v[k].x * rs * g.x, v[k].y * rs * g.y, v[k].z * rs * g.z, v[k].w * rs * g.w);
+      }
+    }
+  } else {
+    for (int j = threadIdx.x * 4; j < d; j += kThreads * 4) {
+      const float4 w = *reinterpret_cast<const float4*>(x + j);
+      const float4 g = load_gain4(gain + j);
+      store4(y + j, w.x * rs * g.x, w.y * rs * g.y, w.z * rs * g.z, w.w * rs * g.w);
+    }
   }
 }
 

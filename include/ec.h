@@ -156,6 +156,8 @@ typedef struct ec_layer_weights {
   const void* w_down;    /* [d, F] */
 } ec_layer_weights;
 
+/* Every device array of the model and of the cache must be 16-byte aligned (hipMalloc
+ * returns 256-byte aligned memory); ec_forward / ec_step return EC_ERR_ARG otherwise. */
 typedef struct ec_model_desc {
   uint32_t struct_size;
   ec_dtype dtype;

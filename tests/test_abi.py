@@ -100,6 +100,15 @@ def test_unsupported_shapes_and_bad_params_are_rejected(lib):
     m3.weight_layout = _lib.EC_LAYOUT_PLAIN
     assert lib.ec_step_workspace_size(C.byref(m3), C.byref(_params())) == 0
     assert b"weight_layout" in lib.ec_last_error()
+    # device arrays must be 16-byte aligned (the kernels move 16-byte vectors)
+    m4, _keep4 = _model_desc()
+    m4.final_norm = 0x1008
+    assert lib.ec_step_workspace_size(C.byref(m4), C.byref(_params())) == 0
+    assert b"aligned" in lib.ec_last_error()
+    m5, keep5 = _model_desc()
+    keep5[3].w_down = 0x1004
+    assert lib.ec_step_workspace_size(C.byref(m5), C.byref(_params())) == 0
+    assert b"layer 3" in lib.ec_last_error()
 
 
 def test_argument_errors_return_before_any_gpu_work(lib):
