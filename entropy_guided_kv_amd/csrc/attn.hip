@@ -42,7 +42,7 @@ constexpr int kAttnThreads = 512;  // MFMA kernel: 8 wavefronts
 constexpr int D = 128;       // head_dim of the MFMA kernel
 constexpr int BQ = 128;      // queries per workgroup (32 per wavefront)
 constexpr int BKV = 64;      // keys per LDS stage
-constexpr int KS = D + 16;   // LDS row stride (bf16): 288 bytes keeps b128 and transpose reads conflict-free
+constexpr int KS = D;        // LDS row stride (bf16): unpadded 256-byte rows, swizzled (below)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.f;  // lazy rescale: keep the reference max until a row max exceeds it by 2^8
 
@@ -59,10 +59,15 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                  float* __restrict__ pml) {
   // K and V tiles in natural [key][dim] layout, double-buffered
   // one allocation: after the loop the whole of it holds the (m, l, o) hand-over
-  __shared__ __align__(16) bf16 skv[2][2][BKV * KS];
-  bf16 (*sK)[BKV * KS] = skv[0];
-  bf16 (*sV)[BKV * KS] = skv[1];
-  static_assert(4 * 64 * (D / 2 + 2) * sizeof(float) <= sizeof(skv), "hand-over exceeds the K/V tiles");
+  // LDS layout (64 banks of 4 bytes): a K row keeps its 16-byte chunk c at c ^ (row % 16), so the
+  // 16 rows one b128 fragment read serves per cycle hit 16 distinct bank groups; a V row keeps
+  // its 64-byte quarter q (dims 32q .. 32q+31) at q ^ (row % 4), so the four consecutive keys of
+  // a transposing read fall in distinct quarters.
+  constexpr int kTileBytes = 2 * 2 * BKV * KS * 2;
+  constexpr int kHandBytes = 4 * 64 * (D / 2 + 2) * 4;
+  __shared__ __align__(16) unsigned char lds_raw[kTileBytes > kHandBytes ? kTileBytes : kHandBytes];
+  bf16 (*sK)[BKV * KS] = reinterpret_cast<bf16 (*)[BKV * KS]>(lds_raw);
+  bf16 (*sV)[BKV * KS] = reinterpret_cast<bf16 (*)[BKV * KS]>(lds_raw + 2 * BKV * KS * 2);
 
   const int qt = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -112,9 +117,11 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = tid + i * kAttnThreads;
-      const int off = (v / (D / 8)) * KS + (v % (D / 8)) * 8;
-      *reinterpret_cast<bf16x8*>(&sK[buf][off]) = rk[i];
-      *reinterpret_cast<bf16x8*>(&sV[buf][off]) = rv[i];
+      const int row = v / (D / 8), c = v % (D / 8);
+      const int offk = row * KS + (c ^ (row & 15)) * 8;
+      const int offv = row * KS + (((c >> 2) ^ (row & 3)) * 4 + (c & 3)) * 8;
+      *reinterpret_cast<bf16x8*>(&sK[buf][offk]) = rk[i];
+      *reinterpret_cast<bf16x8*>(&sV[buf][offv]) = rv[i];
     }
   };
 
@@ -144,7 +151,7 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
       bf16x8 fk[D / 16];
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
-        fk[kk] = *reinterpret_cast<const bf16x8*>(kt + (sub * 32 + lq) * KS + 16 * kk + 8 * g);
+        fk[kk] = *reinterpret_cast<const bf16x8*>(kt + (sub * 32 + lq) * KS + (((2 * kk + g) ^ (lq & 15)) * 8));
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[kk], fq[kk], st, 0, 0, 0);
       // key of st[v]: kv0 + sub*32 + 8(v/4) + 4g + v%4; mask keys past the end of the range
@@ -185,7 +192,7 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
           const int kb = sub * 32 + 16 * c + 4 * g + tr_key;
-          const lds_bf16* p0 = vt + kb * KS + 32 * i + tr_dim;
+          const lds_bf16* p0 = vt + kb * KS + 32 * (i ^ tr_key) + tr_dim;  // kb % 4 == tr_key
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * KS));
           const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
@@ -208,7 +215,7 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   // the upper-key wavefront of each query group hands (m, l, o) to the lower one through
   // LDS (the K/V tiles are no longer read after the loop's last barrier)
   {
-    float* xb = reinterpret_cast<float*>(&skv[0][0][0]) + (qw * 64 + lane) * (D / 2 + 2);
+    float* xb = reinterpret_cast<float*>(lds_raw) + (qw * 64 + lane) * (D / 2 + 2);
     if (kh == 1) {
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)

@@ -628,7 +628,10 @@ struct TileInfo {
   double eff;  // sustained MFMA rate relative to 4 TFLOP/s per CU, measured on MI355X
 };
 constexpr TileInfo kTile[kNumTileCfg] = {
-    {256, 192, 1.03}, {256, 128, 0.99}, {128, 128, 0.88}, {64, 128, 0.70}};
+    {256, 192, 1.10}, {256, 128, 1.00}, {128, 128, 1.00}, {64, 128, 0.65}};
+// Sustained global-to-LDS rate of one CU (bytes per microsecond) with the weights streamed
+// from HBM: a tile's staging time is (BM + BN) x K x 2 bytes at this rate.
+constexpr double kCuLoadBytesPerUs = 60e3;
 
 struct Plan {
   TileCfg cfg;
@@ -636,12 +639,14 @@ struct Plan {
 };
 
 // Tile choice by a cost model fitted to MI355X measurements of the projection
-// shapes: time = waves x per-tile time, waves = ceil(tiles * S / 256), per-tile
-// time = 2 BM BN (K / S) / (eff x 4 TFLOP/s), plus, for split K, the partials'
-// round trip through HBM and one more launch. Larger tiles carry more MFMA work
-// per staged byte; smaller ones fill the 256 CUs at skinny M (skip steps, the LM
-// head over the candidates). K is split only when a configuration's tiles cover
-// fewer than half the CUs.
+// shapes (rows 17 .. 1024, weights streamed from HBM): time = waves x per-tile
+// time, waves = ceil(tiles * S / 256), per-tile time = the larger of the MFMA time
+// 2 BM BN (K / S) / (eff x 4 TFLOP/s) and the staging time (BM + BN) (K / S) 2 bytes
+// at kCuLoadBytesPerUs, plus, for split K, the partials' round trip through HBM, one
+// more launch and 1 us per split. Larger tiles carry more MFMA work per staged byte; smaller ones
+// and split K fill the 256 CUs at skinny M (skip steps, the LM head over the
+// candidates). Every tile shape and split S in {1, 2, 4, 8} (K chunks of at least
+// 8 steps) is priced and the cheapest taken.
 Plan plan_bf16(int M, int N, int K, int kind) {
   Plan best{};
   double best_us = 1e300;
@@ -655,19 +660,22 @@ Plan plan_bf16(int M, int N, int K, int kind) {
     if ((M <= 128 || ent) && (c == T256x192 || c == T256x128)) continue;
     const int MT = (M + t.BM - 1) / t.BM, NT = (N + t.BN - 1) / t.BN;
     const int64_t tiles = (int64_t)MT * NT;
-    int S = 1;
-    if (tiles < kCUs / 2 && !ent)
-      while (tiles * S * 2 <= kCUs && S < 8 && nk % (2 * S) == 0 && nk / (2 * S) >= 8) S *= 2;
-    const int64_t waves = (tiles * S + kCUs - 1) / kCUs;
-    double us = (double)waves * 2.0 * t.BM * t.BN * (double)(K / S) / (t.eff * 4e6);
-    if (S > 1) us += (double)S * M * N * 8.0 / 5e6 + 3.0;
-    if (us < best_us) {
-      best_us = us;
-      best.cfg = (TileCfg)c;
-      best.MT = MT;
-      best.NT = NT;
-      best.S = S;
-      best.k_chunk = K / S;
+    for (int S = 1; S <= (ent ? 1 : 8); S *= 2) {
+      if (S > 1 && (nk % S != 0 || nk / S < 8)) break;
+      const int64_t waves = (tiles * S + kCUs - 1) / kCUs;
+      const double kc = (double)K / S;
+      const double mfma_us = 2.0 * t.BM * t.BN * kc / (t.eff * 4e6);
+      const double load_us = (double)(t.BM + t.BN) * kc * 2.0 / kCuLoadBytesPerUs;
+      double us = (double)waves * (mfma_us > load_us ? mfma_us : load_us);
+      if (S > 1) us += (double)S * M * N * 8.0 / 5e6 + 3.0 + (double)S;
+      if (us < best_us) {
+        best_us = us;
+        best.cfg = (TileCfg)c;
+        best.MT = MT;
+        best.NT = NT;
+        best.S = S;
+        best.k_chunk = K / S;
+      }
     }
   }
   return best;
@@ -701,13 +709,13 @@ ec_status launch_cfg(const Plan& p, const bf16* A, const bf16* B, int M, int N, 
                      const EpiArgs& epi, float* part, hipStream_t s) {
   if constexpr (EPI == EPI_ENTROPY) {
     if (p.cfg == T128x128) return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
-    return launch_bf16<64, 128, 32, 32, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+    return launch_bf16<64, 128, 32, 32, 6, true, EPI>(p, A, B, M, N, K, epi, part, s);
   } else {
     switch (p.cfg) {
       case T256x192: return launch_bf16<256, 192, 64, 96, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
       case T256x128: return launch_bf16<256, 128, 64, 64, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
       case T128x128: return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
-      default: return launch_bf16<64, 128, 32, 32, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+      default: return launch_bf16<64, 128, 32, 32, 6, true, EPI>(p, A, B, M, N, K, epi, part, s);
     }
   }
 }
