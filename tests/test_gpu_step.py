@@ -205,3 +205,25 @@ def test_tiny_sliding_window_trajectory(n, B):
     blk, _, _ = ol.run_entropycache(om.OracleModel(w), dataclasses.replace(cfg, window=False), synth.make_prompt(cfg),
                                     PEAKED_TAU)
     assert [list(r.picked) for r in blk] != [list(r.picked) for r in recs]
+
+
+@pytest.mark.parametrize("name", ["tiny_trajectory.json", "tiny_peaked_trajectory.json"])
+def test_tiny_trajectory_matches_stored_golden(name):
+    """The device trajectory against the stored oracle trajectory (tests/golden/): same path,
+    recompute-set sizes, positions, ids and final tokens; E within 1e-3 nats (fp32 model)."""
+    import json
+    import os
+    from entropy_guided_kv_amd import api
+    stored = json.load(open(os.path.join(os.path.dirname(__file__), "golden", name)))
+    cfg = synth.CONFIGS[stored["config"]]
+    w = synth.make_model(cfg.model, lm_head_scale=stored["lm_head_scale"])
+    dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+    dec = _decoder(dm, cfg, stored["tau"])
+    dec.reset(torch.from_numpy(synth.make_prompt(cfg)))
+    outs = dec.run()
+    assert len(outs) == len(stored["steps"])
+    for o, s in zip(outs, stored["steps"]):
+        assert (o.refreshed, o.rows, o.positions, o.ids) == \
+               (s["refreshed"], s["n_rows"], s["positions"], s["ids"]), f"step {s['t']}"
+        assert abs(o.emax - s["emax"]) <= 1e-3, f"step {s['t']}: E {o.emax} vs {s['emax']}"
+    assert dec.tokens.cpu().tolist() == stored["final_tokens"]
