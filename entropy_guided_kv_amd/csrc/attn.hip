@@ -335,13 +335,29 @@ struct AttnPlan {
   int qtiles, splits, chunk;
 };
 
+// Key-range split by a cost model fitted to MI355X measurements (r = 17 .. 1024,
+// L = 1024 and 4096, 32 heads): waves of workgroups x tiles per workgroup x 1.15 us,
+// plus, when split, 3 us for the merge launch and 0.018 us per (split x query) for
+// the partials' round trip (scaled by H / 32).
 AttnPlan plan_attn(int r, int L, int H) {
   AttnPlan p;
   p.qtiles = (r + BQ - 1) / BQ;
   const int base = p.qtiles * H;
-  int s = 1;
-  while (base * s < 256 && L / (2 * s) >= 2 * BKV) s *= 2;
-  p.chunk = ((L + s - 1) / s + BKV - 1) / BKV * BKV;
+  double best = 1e300;
+  int s_best = 1;
+  for (int s : {1, 2, 3, 4, 6, 8, 12, 16}) {
+    if (s > 1 && L / s < BKV) break;
+    const int chunk = ((L + s - 1) / s + BKV - 1) / BKV * BKV;
+    const int splits = (L + chunk - 1) / chunk;
+    const double waves = (double)(((int64_t)base * splits + 255) / 256);
+    double us = waves * (chunk / BKV) * 1.15;
+    if (splits > 1) us += 3.0 + 0.018 * splits * r * (H / 32.0);
+    if (us < best) {
+      best = us;
+      s_best = s;
+    }
+  }
+  p.chunk = ((L + s_best - 1) / s_best + BKV - 1) / BKV * BKV;
   p.splits = (L + p.chunk - 1) / p.chunk;
   return p;
 }

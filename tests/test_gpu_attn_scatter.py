@@ -63,7 +63,8 @@ def _attn_case(r, L, H, D, dtype, seed=0, scale=1.0):
 
 
 @pytest.mark.parametrize("r,L,H", [(143, 1024, 4), (1, 1024, 2), (257, 512, 3), (128, 128, 1),
-                                   (17, 1000, 2), (1024, 1024, 2), (33, 4096, 2)])
+                                   (17, 1000, 2), (1024, 1024, 2), (33, 4096, 2),
+                                   (40, 700, 8), (96, 900, 24)])  # 6 and 3 key splits (ragged)
 def test_partial_attn_bf16(r, L, H):
     got, want = _attn_case(r, L, H, 128, torch.bfloat16, seed=r + L, scale=0.35)
     err = row_rel_err(got.reshape(r * H, 128), want.reshape(r * H, 128))
