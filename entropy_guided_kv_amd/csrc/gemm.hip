@@ -19,9 +19,10 @@
 //
 // Block order is XCD-aware: MI355X dispatches consecutive workgroups round-
 // robin over its 8 XCDs (each with its own L2), so block ids are remapped to
-// give each XCD a contiguous range in which the M tiles of one weight tile
-// are adjacent; a weight tile is then fetched from HBM once and re-read from
-// that XCD's L2.
+// give each XCD a contiguous range of the tile order, in which the row tiles of
+// one weight tile are adjacent (a weight tile is fetched from HBM once and
+// re-read from that XCD's L2) and row tiles come in groups of four (at large M
+// a wave of tiles on one XCD then reads 4 A tiles, not 32).
 //
 // When M x N tiles cannot fill the 256 CUs (skinny M on skip steps, N = d on
 // the projections), K is split across workgroups; partial sums go to an fp32
@@ -110,6 +111,7 @@ __device__ __forceinline__ void epi_swiglu(const EpiArgs& e, int m, int col, flo
 }
 
 // -------------------------------------------------------------------- block mapping
+constexpr int kGroupM = 4;  // row tiles per group of the tile order
 __device__ __forceinline__ int xcd_remap(int pid, int nblk) {
   const int per = nblk / 8, rem = nblk % 8;
   const int x = pid % 8, local = pid / 8;
@@ -198,9 +200,17 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int MT = (M + BM - 1) / BM;
+  // tile order: groups of kGroupM row tiles; inside a group the row tile varies
+  // fastest, then the (weight tile, K split) pair, so any 32 consecutive tiles (one
+  // XCD's share of a wave) cover at most kGroupM row tiles and re-read few A tiles
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = bid % MT;
-  const int rest = bid / MT;
+  const int ntk = ((int)gridDim.x / MT);  // weight tiles x splits
+  const int per_group = kGroupM * ntk;
+  const int first_m = (bid / per_group) * kGroupM;
+  const int gm = min(MT - first_m, kGroupM);
+  const int in_group = bid % per_group;
+  const int mt = first_m + in_group % gm;
+  const int rest = in_group / gm;
   const int kz = rest % splits;
   const int nt = rest / splits;
   const int m0 = mt * BM, n0 = nt * BN;
@@ -713,7 +723,7 @@ ec_status launch_cfg(const Plan& p, const bf16* A, const bf16* B, int M, int N, 
   } else {
     switch (p.cfg) {
       case T256x192: return launch_bf16<256, 192, 64, 96, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
-      case T256x128: return launch_bf16<256, 128, 64, 64, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
+      case T256x128: return launch_bf16<256, 128, 64, 64, 3, false, EPI>(p, A, B, M, N, K, epi, part, s);
       case T128x128: return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
       default: return launch_bf16<64, 128, 32, 32, 6, true, EPI>(p, A, B, M, N, K, epi, part, s);
     }
