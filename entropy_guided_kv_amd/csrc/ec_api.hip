@@ -252,9 +252,12 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
       EC_TRY(embed(dt, m->embed, V, tokens, L, rows, n_rows, d, w.h, s, b ? b->tok_tab : nullptr,
                    b ? b->row_seq : nullptr));
     }
+    // normed: w.a already holds this layer's attention-norm input (the previous layer's
+    // down projection fused its split-K reduction with the norm)
+    bool normed = false;
     for (int l = 0; l < m->n_layers; ++l) {
       const ec_layer_weights& lw = m->layers[l];
-      {
+      if (!normed) {
         TScope t(EC_T_NORM, s, 0.0, M * dd * (4 + es));
         EC_TRY(rmsnorm(dt, w.h, n_rows, nullptr, n_rows, d, lw.attn_norm, m->rms_eps, w.a, s));
       }
@@ -305,11 +308,14 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
       r.kind = EPI_RESID;
       r.resid = w.h;
       r.ldo = d;
+      r.norm_gain = lw.mlp_norm;
+      r.norm_out = w.a;
+      r.norm_eps = m->rms_eps;
       {
         TScope t(EC_T_OPROJ, s, 2 * M * dd * dd, (dd * dd + M * dd) * es + 8 * M * dd);
-        EC_TRY(gemm(dt, w.o, lw.wo, nullptr, n_rows, d, d, r, w.splitk, w.splitk_bytes, s));
+        EC_TRY(gemm(dt, w.o, lw.wo, nullptr, n_rows, d, d, r, w.splitk, w.splitk_bytes, s, &normed));
       }
-      {
+      if (!normed) {
         TScope t(EC_T_NORM, s, 0.0, M * dd * (4 + es));
         EC_TRY(rmsnorm(dt, w.h, n_rows, nullptr, n_rows, d, lw.mlp_norm, m->rms_eps, w.a, s));
       }
@@ -321,9 +327,13 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
         TScope t(EC_T_GATEUP, s, 4 * M * FF * dd, (2 * FF * dd + M * dd + M * FF) * es);
         EC_TRY(gemm(dt, w.a, lw.w_gate, lw.w_up, n_rows, F, d, g, w.splitk, w.splitk_bytes, s));
       }
+      // the next layer's attention norm rides on the down projection's split-K reduction
+      const bool has_next = l + 1 < m->n_layers;
+      r.norm_gain = has_next ? m->layers[l + 1].attn_norm : nullptr;
+      r.norm_out = has_next ? w.a : nullptr;
       {
         TScope t(EC_T_DOWN, s, 2 * M * dd * FF, (dd * FF + M * FF) * es + 8 * M * dd);
-        EC_TRY(gemm(dt, w.s, lw.w_down, nullptr, n_rows, d, F, r, w.splitk, w.splitk_bytes, s));
+        EC_TRY(gemm(dt, w.s, lw.w_down, nullptr, n_rows, d, F, r, w.splitk, w.splitk_bytes, s, &normed));
       }
     }
   }

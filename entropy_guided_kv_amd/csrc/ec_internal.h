@@ -71,6 +71,12 @@ struct EpiArgs {
   int kind;
   void* out;          // STORE: T[M, ldo]; SWIGLU: T[M, ldo]; QKV: q rows T[M, d]
   float* resid;       // RESID: float[M, ldo] updated in place (h += acc)
+  // RESID with split K: when norm_out is set, the split-K reduction also writes
+  // norm_out[m] = T(RMSNorm(h[m]) * norm_gain) (the next projection's input), and
+  // gemm() reports it through *normed
+  const void* norm_gain;
+  void* norm_out;
+  float norm_eps;
   int64_t ldo;
   // QKV: k/v cache rows at positions rows[m]
   void* k_cache;
@@ -113,7 +119,8 @@ int gemm_col_tiles(int M, int N, int K, int kind);
 // bf16: packed weights (QKV rotary-interleaved [3d, K]; SwiGLU B = [2N, K] gate/up
 // interleave, B2 unused). N is the number of output columns.
 ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M, int N, int K,
-               const EpiArgs& epi, float* splitk_ws, size_t splitk_ws_bytes, hipStream_t s);
+               const EpiArgs& epi, float* splitk_ws, size_t splitk_ws_bytes, hipStream_t s,
+               bool* normed = nullptr);
 ec_status pack_weights(int elem_bytes, int d, int head_dim, int F, const void* wqkv,
                        const void* w_gate, const void* w_up, void* wqkv_packed,
                        void* gateup_packed, hipStream_t s);
@@ -139,6 +146,11 @@ ec_status embed(ec_dtype dt, const void* table, int vocab, const int32_t* tokens
                 const int32_t* const* tok_tab = nullptr, const int32_t* row_seq = nullptr);
 ec_status rmsnorm(ec_dtype dt, const float* h, int n_src, const int32_t* idx, int n, int d,
                   const void* gain, float eps, void* out, hipStream_t s);
+// h[m] += sum_s part[s][m] (s ascending), then out[m] = T(RMSNorm(h[m]) * gain), m < M: the
+// split-K reduction of a residual projection fused with the next RMSNorm. Bit-identical to
+// the split-K residual epilogue followed by rmsnorm().
+ec_status resid_norm(ec_dtype dt, const float* part, int S, int M, int d, float* h, const void* gain,
+                     float eps, void* out, hipStream_t s);
 ec_status scatter(ec_dtype dt, void* kc, void* vc, int64_t L, int width, const void* kr,
                   const void* vr, const int32_t* idx, int n, hipStream_t s);
 

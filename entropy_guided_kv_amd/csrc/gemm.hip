@@ -749,7 +749,9 @@ size_t gemm_splitk_ws_bytes(int M, int N, int K, int kind, bool is_bf16) {
 }
 
 ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M, int N, int K,
-               const EpiArgs& epi, float* splitk_ws, size_t splitk_ws_bytes, hipStream_t s) {
+               const EpiArgs& epi, float* splitk_ws, size_t splitk_ws_bytes, hipStream_t s,
+               bool* normed) {
+  if (normed) *normed = false;
   if (M == 0) return EC_OK;
   const int kind = epi.kind;
   if (dt == EC_F32) {
@@ -794,6 +796,13 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
   }
   if (st != EC_OK) return st;
   if (p.S > 1) {
+    if (kind == EPI_RESID && epi.norm_out && normed && epi.ldo == NB) {
+      // residual update fused with the next RMSNorm: one pass over the rows
+      const ec_status sn = resid_norm(dt, part, p.S, M, NB, epi.resid, epi.norm_gain, epi.norm_eps, epi.norm_out, s);
+      if (sn != EC_OK) return sn;
+      *normed = true;
+      return EC_OK;
+    }
     const int64_t units = (kind == EPI_QKV || kind == EPI_SWIGLU) ? (int64_t)M * (NB / 2) : (int64_t)M * NB;
     const int blocks = (int)((units + kThreads - 1) / kThreads);
     splitk_epilogue_kernel<<<blocks, kThreads, 0, s>>>(part, p.S, M, NB, kind, epi);

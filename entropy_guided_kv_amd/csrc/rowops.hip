@@ -55,14 +55,31 @@ __device__ __forceinline__ float4 load_gain4(const bf16* g) {
 }
 __device__ __forceinline__ float4 load_gain4(const float* g) { return *reinterpret_cast<const float4*>(g); }
 
-template <typename T>
+// With PARTS (the split-K residual fusion, idx unused): the row is first updated in
+// place, h[i] += sum_s part[s][i] with the partials added in ascending s to a zero
+// start (the split-K epilogue's order), and the norm then reads the updated values.
+__device__ __forceinline__ float4 add_parts(float4 v, const float* __restrict__ part, int S, int M, int i,
+                                            int d, int j) {
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < S; ++s) {
+    const float4 p = *reinterpret_cast<const float4*>(part + ((int64_t)s * M + i) * d + j);
+    a.x += p.x;
+    a.y += p.y;
+    a.z += p.z;
+    a.w += p.w;
+  }
+  return make_float4(v.x + a.x, v.y + a.y, v.z + a.z, v.w + a.w);
+}
+
+template <typename T, bool PARTS>
 __global__ void __launch_bounds__(kThreads)
-rmsnorm_kernel(const float* __restrict__ h, int n_src, const int32_t* __restrict__ idx, int d,
-               const T* __restrict__ gain, float eps, T* __restrict__ out) {
+rmsnorm_kernel(float* __restrict__ h, int n_src, const int32_t* __restrict__ idx, int d,
+               const T* __restrict__ gain, float eps, T* __restrict__ out, const float* __restrict__ part,
+               int S) {
   const int i = blockIdx.x;
-  int src = idx ? idx[i] : i;
+  int src = (!PARTS && idx) ? idx[i] : i;
   if (src < 0 || src >= n_src) src = 0;  // invalid index: normalise row 0 (no out-of-range read)
-  const float* x = h + (int64_t)src * d;
+  float* x = h + (int64_t)src * d;
   const bool in_regs = d <= 4 * kThreads * kNormRegs;
   float4 v[kNormRegs];
   float ss = 0.f;
@@ -72,12 +89,20 @@ rmsnorm_kernel(const float* __restrict__ h, int n_src, const int32_t* __restrict
       const int j = (threadIdx.x + k * kThreads) * 4;
       if (j < d) {
         v[k] = *reinterpret_cast<const float4*>(x + j);
+        if (PARTS) {
+          v[k] = add_parts(v[k], part, S, n_src, i, d, j);
+          *reinterpret_cast<float4*>(x + j) = v[k];
+        }
         ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
       }
     }
   } else {
     for (int j = threadIdx.x * 4; j < d; j += kThreads * 4) {
-      const float4 w = *reinterpret_cast<const float4*>(x + j);
+      float4 w = *reinterpret_cast<const float4*>(x + j);
+      if (PARTS) {
+        w = add_parts(w, part, S, n_src, i, d, j);
+        *reinterpret_cast<float4*>(x + j) = w;
+      }
       ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
     }
   }
@@ -168,10 +193,27 @@ ec_status rmsnorm(ec_dtype dt, const float* h, int n_src, const int32_t* idx, in
                   const void* gain, float eps, void* out, hipStream_t s) {
   if (n == 0) return EC_OK;
   EC_REQUIRE(d % 4 == 0, EC_ERR_UNSUPPORTED, "rmsnorm: d_model %d not a multiple of 4", d);
+  float* hm = const_cast<float*>(h);  // read only without parts
   if (dt == EC_BF16)
-    rmsnorm_kernel<bf16><<<n, kThreads, 0, s>>>(h, n_src, idx, d, (const bf16*)gain, eps, (bf16*)out);
+    rmsnorm_kernel<bf16, false><<<n, kThreads, 0, s>>>(hm, n_src, idx, d, (const bf16*)gain, eps, (bf16*)out,
+                                                        nullptr, 0);
   else
-    rmsnorm_kernel<float><<<n, kThreads, 0, s>>>(h, n_src, idx, d, (const float*)gain, eps, (float*)out);
+    rmsnorm_kernel<float, false><<<n, kThreads, 0, s>>>(hm, n_src, idx, d, (const float*)gain, eps,
+                                                         (float*)out, nullptr, 0);
+  EC_CHECK_LAUNCH("rmsnorm_kernel");
+  return EC_OK;
+}
+
+ec_status resid_norm(ec_dtype dt, const float* part, int S, int M, int d, float* h, const void* gain,
+                     float eps, void* out, hipStream_t s) {
+  if (M == 0) return EC_OK;
+  EC_REQUIRE(d % 4 == 0, EC_ERR_UNSUPPORTED, "resid_norm: d_model %d not a multiple of 4", d);
+  if (dt == EC_BF16)
+    rmsnorm_kernel<bf16, true><<<M, kThreads, 0, s>>>(h, M, nullptr, d, (const bf16*)gain, eps, (bf16*)out,
+                                                       part, S);
+  else
+    rmsnorm_kernel<float, true><<<M, kThreads, 0, s>>>(h, M, nullptr, d, (const float*)gain, eps,
+                                                        (float*)out, part, S);
   EC_CHECK_LAUNCH("rmsnorm_kernel");
   return EC_OK;
 }
