@@ -147,8 +147,8 @@ ec_status embed(ec_dtype dt, const void* table, int vocab, const int32_t* tokens
 ec_status rmsnorm(ec_dtype dt, const float* h, int n_src, const int32_t* idx, int n, int d,
                   const void* gain, float eps, void* out, hipStream_t s);
 // h[m] += sum_s part[s][m] (s ascending), then out[m] = T(RMSNorm(h[m]) * gain), m < M: the
-// split-K reduction of a residual projection fused with the next RMSNorm. Bit-identical to
-// the split-K residual epilogue followed by rmsnorm().
+// split-K reduction of a residual projection fused with the next RMSNorm. It performs the
+// float operations of the split-K residual epilogue followed by rmsnorm(), in their order.
 ec_status resid_norm(ec_dtype dt, const float* part, int S, int M, int d, float* h, const void* gain,
                      float eps, void* out, hipStream_t s);
 ec_status scatter(ec_dtype dt, void* kc, void* vc, int64_t L, int width, const void* kr,
