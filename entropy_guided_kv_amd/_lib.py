@@ -23,7 +23,8 @@ EXPORTS = (
     "ec_entropy_max_workspace_size", "ec_entropy_max", "ec_cache_scatter",
     "ec_partial_attn_workspace_size", "ec_partial_attn", "ec_rope_table",
     "ec_forward_workspace_size", "ec_forward", "ec_state_plan_words", "ec_state_reset",
-    "ec_step_workspace_size", "ec_step", "ec_timing_enable", "ec_timing_read", "ec_last_error",
+    "ec_step_workspace_size", "ec_step", "ec_timing_enable", "ec_timing_select", "ec_timing_read",
+    "ec_last_error",
     "ec_version", "ec_pack_weights", "ec_step_batch_workspace_size", "ec_step_batch", "ec_step_probe",
 )
 
@@ -120,6 +121,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ec_step": (C.c_int, [C.POINTER(ec_model_desc), C.POINTER(ec_cache_desc), C.POINTER(ec_state),
                               C.POINTER(ec_params), vp, sz, vp, C.POINTER(ec_step_out)]),
         "ec_timing_enable": (C.c_int, [C.c_int]),
+        "ec_timing_select": (C.c_int, [C.c_uint32]),
         "ec_timing_read": (C.c_int, [C.POINTER(ec_timing), C.c_int]),
         "ec_last_error": (C.c_char_p, []),
         "ec_version": (C.c_int, []),

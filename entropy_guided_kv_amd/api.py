@@ -429,6 +429,12 @@ def ec_timing_enable(on: bool) -> None:
     check(load().ec_timing_enable(1 if on else 0), "ec_timing_enable")
 
 
+def ec_timing_select(kinds=None) -> None:
+    """Record only the named groups (names as in ec_timing_read; None: all groups)."""
+    mask = 0xFFFFFFFF if kinds is None else sum(1 << _lib.TIMING_KINDS.index(k) for k in kinds)
+    check(load().ec_timing_select(mask), "ec_timing_select")
+
+
 def ec_timing_read(reset: bool = True) -> dict:
     """Per kernel group: summed event ms, launches, algorithmic flops and bytes."""
     t = _lib.ec_timing()

@@ -31,6 +31,7 @@ namespace {
 // ---------------------------------------------------------------- timing aid
 struct TimingState {
   bool on = false;
+  uint32_t mask = ~0u;  // groups recorded while on
   std::vector<hipEvent_t> ev;  // pairs: 2*i start, 2*i+1 stop
   struct Rec {
     int kind, slot;
@@ -48,7 +49,7 @@ struct TScope {
   hipStream_t s;
   double fl, by;
   TScope(int k, hipStream_t st, double f, double b) : kind(k), s(st), fl(f), by(b) {
-    if (!g_tm.on) return;
+    if (!g_tm.on || !((g_tm.mask >> k) & 1u)) return;
     if ((int)g_tm.ev.size() < 2 * (g_tm.used + 1)) {
       hipEvent_t a, z;
       if (hipEventCreate(&a) != hipSuccess) return;
@@ -570,6 +571,11 @@ const char* ec_last_error(void) { return g_err; }
 ec_status ec_timing_enable(int on) {
   if (!on) timing_collect();
   g_tm.on = on != 0;
+  return EC_OK;
+}
+
+ec_status ec_timing_select(uint32_t kinds) {
+  g_tm.mask = kinds;
   return EC_OK;
 }
 

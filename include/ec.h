@@ -348,8 +348,11 @@ ec_status ec_step_batch(const ec_model_desc* model, int32_t n_seq, const ec_cach
  * elapsed time, the number of launches and the algorithmic work of those
  * launches (flops of the contraction, bytes the method must move). Process-
  * wide state, for one thread at a time; it costs two event records per
- * group, so keep it off for headline timings. ec_timing_read synchronizes
- * the recorded events, fills `out` and optionally clears the totals.
+ * timed group launch. ec_timing_select restricts the recording to the groups
+ * whose bit (1 << EC_T_*) is set in `kinds` (all groups by default), so that a
+ * single group can be timed inside a throughput run at the cost of two event
+ * records per launch of that group. ec_timing_read synchronizes the recorded
+ * events, fills `out` and optionally clears the totals.
  * ---------------------------------------------------------------------- */
 enum {
   EC_T_EMBED = 0, EC_T_NORM, EC_T_QKV, EC_T_ATTN, EC_T_OPROJ, EC_T_GATEUP, EC_T_DOWN,
@@ -364,6 +367,7 @@ typedef struct ec_timing {
   double bytes[EC_T_KINDS];     /* algorithmic bytes (weights + activations read / written) */
 } ec_timing;
 ec_status ec_timing_enable(int on);
+ec_status ec_timing_select(uint32_t kinds);
 ec_status ec_timing_read(ec_timing* out, int reset);
 
 /* Message of the calling thread's last failed call ("" if none). */
