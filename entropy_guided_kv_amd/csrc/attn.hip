@@ -21,8 +21,11 @@
 // Softmax statistics are per lane (one query), completed with one
 // cross-half exchange; the reference max is only moved (and O, l rescaled)
 // when a row max exceeds it by 2^8, so most tiles skip the rescale. Q stays
-// in registers; K and V tiles of 64 keys are double-buffered in LDS, the next
-// tile's global loads in flight during the current tile's MFMAs, shared by the
+// in registers; K and V tiles of 64 keys go from global memory straight into a
+// ring of kStages LDS stages (buffer_load_dwordx4 ... lds, no staging registers),
+// so that the loads of the next kStages - 1 tiles are in flight during the
+// current tile's MFMAs (a split of up to kStages tiles issues all of its loads at
+// once). The tiles are shared by the
 // 8 wavefronts of a workgroup: 4 groups of 32 queries (128 queries), the two
 // wavefronts of a group taking the lower and the upper 32 keys of every tile
 // (two wavefronts per SIMD: one's softmax and LDS reads overlap the other's
@@ -50,43 +53,50 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
 
-// grid: (query tiles, heads, splits)
+constexpr int kStages = 4;                          // LDS ring of K/V tiles
+constexpr int kStageBytes = 2 * BKV * KS * 2;          // K and V of one tile
+constexpr int kQOff = kStages * kStageBytes;           // Q tile (BQ rows of 256 bytes) after the ring
+constexpr int kHandBytes = 4 * 64 * (D / 2 + 2) * 4;   // (m, l, o) hand-over after the loop (over the ring)
+constexpr int kAttnLds = kQOff + BQ * D * 2;
+static_assert(kHandBytes <= kQOff, "hand-over fits in the ring");
+static_assert(kAttnLds <= 160 * 1024, "LDS budget");
+
+// grid: (query tiles, heads, splits); dynamic LDS of kAttnLds bytes
 template <bool SPLIT>
 __global__ void __launch_bounds__(kAttnThreads)
 attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                  const bf16* __restrict__ vc, int r, int L, int H, float scale_log2,
                  int kv_chunk, bf16* __restrict__ out, float* __restrict__ po,
                  float* __restrict__ pml) {
-  // K and V tiles in natural [key][dim] layout, double-buffered
-  // one allocation: after the loop the whole of it holds the (m, l, o) hand-over
+  // K and V tiles in natural [key][dim] layout, one stage per tile of the ring;
+  // after the loop the LDS holds the (m, l, o) hand-over.
   // LDS layout (64 banks of 4 bytes): a K row keeps its 16-byte chunk c at c ^ (row % 16), so the
   // 16 rows one b128 fragment read serves per cycle hit 16 distinct bank groups; a V row keeps
   // its 64-byte quarter q (dims 32q .. 32q+31) at q ^ (row % 4), so the four consecutive keys of
   // a transposing read fall in distinct quarters.
-  constexpr int kTileBytes = 2 * 2 * BKV * KS * 2;
-  constexpr int kHandBytes = 4 * 64 * (D / 2 + 2) * 4;
-  __shared__ __align__(16) unsigned char lds_raw[kTileBytes > kHandBytes ? kTileBytes : kHandBytes];
-  bf16 (*sK)[BKV * KS] = reinterpret_cast<bf16 (*)[BKV * KS]>(lds_raw);
-  bf16 (*sV)[BKV * KS] = reinterpret_cast<bf16 (*)[BKV * KS]>(lds_raw + 2 * BKV * KS * 2);
+  extern __shared__ __align__(16) unsigned char lds_raw[];
 
   const int qt = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int qw = wave % 4, kh = wave / 4;   // query group, key half of every tile
   const int lq = lane % 32, g = lane / 32;
   const int64_t HD = (int64_t)H * D;
   const int qrow = qt * BQ + qw * 32 + lq;  // this lane's query (column of S^T)
   const bool qok = qrow < r;
 
-  // Q fragments (B operand of S^T): Q[qrow][16kk + 8g .. +7]
-  bf16x8 fq[D / 16];
+  // Q tile through LDS like K (chunk c of row i at c ^ (i % 16)); rows past r re-read row r - 1
   {
-    const bf16* src = q + (int64_t)(qok ? qrow : 0) * HD + h * D + 8 * g;
+    const __amdgpu_buffer_rsrc_t rQ = buffer_rsrc(q, (int64_t)r * HD * 2);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) fq[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
-    // wait here: left to the compiler, the wait for Q would sit at its first use inside
-    // the tile loop and, repeated every tile, would also wait for the next tile's loads
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));  // vmcnt(0)
+    for (int i = 0; i < BQ * D * 2 / 1024 / 8; ++i) {
+      const int sl = i * 8 + wave, row = 4 * sl + lane / 16, pos = lane % 16;
+      const int qr = min(qt * BQ + row, r - 1);
+      buffer_load_lds16(rQ, lds_raw + kQOff + sl * 1024,
+                        (int)(((int64_t)qr * HD + h * D) * 2) + (pos ^ (row & 15)) * 16, 0);
+    }
   }
+  constexpr int kQLoads = BQ * D * 2 / 1024 / 8;  // per wavefront
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -99,48 +109,80 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   const int kv_hi = min(L, kv_lo + kv_chunk);
   const int ntiles = (kv_hi - kv_lo + BKV - 1) / BKV;
 
-  // staging: 64 keys x 16 vectors of 8 dims per tile, 2 vectors per thread for K and for V
-  constexpr int NV = BKV * (D / 8) / kAttnThreads;
-  bf16x8 rk[NV], rv[NV];
-  auto gload = [&](int t) __attribute__((always_inline)) {
+  // a tile is 16 KB of K and 16 KB of V: 16 slices of 1 KB (4 rows of 256 bytes) each;
+  // wavefront w loads slices w and 8 + w of both. Lane l of a slice load fills bytes
+  // 16 l of the slice, i.e. tile row 4 s + l / 16 at position l % 16, and fetches the
+  // 16-byte chunk that the swizzle puts there. Keys past the cache end re-read row L - 1
+  // (masked below).
+  const __amdgpu_buffer_rsrc_t rK = buffer_rsrc(kc, (int64_t)L * HD * 2);
+  const __amdgpu_buffer_rsrc_t rV = buffer_rsrc(vc, (int64_t)L * HD * 2);
+  int lrow[2], ck[2], cv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int sl = i * 8 + wave, row = 4 * sl + lane / 16, pos = lane % 16;
+    lrow[i] = row;
+    ck[i] = (pos ^ (row & 15)) * 16;                                    // bytes within the row
+    cv[i] = ((((pos >> 2) ^ (row & 3)) << 2) | (pos & 3)) * 16;
+  }
+  auto issue = [&](int t) __attribute__((always_inline)) {
     const int kv0 = kv_lo + t * BKV;
+    unsigned char* st = lds_raw + (t % kStages) * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int v = tid + i * kAttnThreads;
-      const int key = min(kv0 + v / (D / 8), L - 1);  // rows past the end are masked below
-      const int dv = (v % (D / 8)) * 8;
-      rk[i] = *reinterpret_cast<const bf16x8*>(kc + (int64_t)key * HD + h * D + dv);
-      rv[i] = *reinterpret_cast<const bf16x8*>(vc + (int64_t)key * HD + h * D + dv);
+    for (int i = 0; i < 2; ++i) {
+      const int key = min(kv0 + lrow[i], L - 1);
+      const int base = (int)(((int64_t)key * HD + h * D) * 2);
+      buffer_load_lds16(rK, st + (i * 8 + wave) * 1024, base + ck[i], 0);
+      buffer_load_lds16(rV, st + BKV * KS * 2 + (i * 8 + wave) * 1024, base + cv[i], 0);
     }
   };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int v = tid + i * kAttnThreads;
-      const int row = v / (D / 8), c = v % (D / 8);
-      const int offk = row * KS + (c ^ (row & 15)) * 8;
-      const int offv = row * KS + (((c >> 2) ^ (row & 3)) * 4 + (c & 3)) * 8;
-      *reinterpret_cast<bf16x8*>(&sK[buf][offk]) = rk[i];
-      *reinterpret_cast<bf16x8*>(&sV[buf][offv]) = rv[i];
-    }
-  };
+  constexpr int kLoadsPerTile = 4;  // per wavefront
 
   // transpose-read coordinates for the V^T operand: within each 16-lane group, source lane
   // s points at (key base + s/4, dim base + 4 (s%4)); ds_read_tr16_b64 then hands lane j the
   // four keys of dim base + j
   const int tr_key = (lane % 16) / 4, tr_dim = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
 
-  if (ntiles > 0) {
-    gload(0);
-    sstore(0);
+  int issued = min(kStages, ntiles);
+  for (int t = 0; t < issued; ++t) issue(t);
+  // Q fragments (B operand of S^T): Q[qrow][16kk + 8g .. +7], read once the Q loads (older
+  // than every tile's) have landed in every wavefront
+  switch (issued) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<kLoadsPerTile>(); break;
+    case 2: wait_vmcnt<2 * kLoadsPerTile>(); break;
+    case 3: wait_vmcnt<3 * kLoadsPerTile>(); break;
+    default: wait_vmcnt<4 * kLoadsPerTile>(); break;
   }
-  __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  bf16x8 fq[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    fq[kk] = *reinterpret_cast<const bf16x8*>(lds_raw + kQOff + (qw * 32 + lq) * (D * 2) +
+                                               (((2 * kk + g) ^ (lq & 15)) * 16));
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+    // this wavefront's loads of tile t (and of Q) have landed once at most the loads of
+    // the tiles issued after t are outstanding; the barrier then publishes every
+    // wavefront's share, and tells that all have finished tile t - 1, whose stage is
+    // refilled with tile t - 1 + kStages
+    switch (issued - t - 1) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<kLoadsPerTile>(); break;
+      case 2: wait_vmcnt<2 * kLoadsPerTile>(); break;
+      default: wait_vmcnt<3 * kLoadsPerTile>(); break;
+    }
+    static_assert(kStages == 4 && kQLoads <= kLoadsPerTile, "the waits cover up to four tiles in flight");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (t >= 1 && t - 1 + kStages < ntiles) {
+      issue(t - 1 + kStages);
+      ++issued;
+    }
     const int kv0 = kv_lo + t * BKV;
-    if (t + 1 < ntiles) gload(t + 1);
-    const bf16* kt = sK[buf];
-    const lds_bf16* vt = (const lds_bf16*)sV[buf];
+    const bf16* kt = reinterpret_cast<const bf16*>(lds_raw + (t % kStages) * kStageBytes);
+    const lds_bf16* vt = (const lds_bf16*)(kt + BKV * KS);
     {
       const int sub = kh;  // this wavefront's 32 keys of the tile
       // ---- S^T[32 keys, 32 queries] (raw dot products)
@@ -208,12 +250,11 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[c][i], fp[c], o[i], 0, 0, 0);
     }
-    if (t + 1 < ntiles) sstore(buf ^ 1);
-    __syncthreads();
   }
+  __syncthreads();  // every wavefront is done with the last tile; no loads are outstanding
 
   // the upper-key wavefront of each query group hands (m, l, o) to the lower one through
-  // LDS (the K/V tiles are no longer read after the loop's last barrier)
+  // LDS
   {
     float* xb = reinterpret_cast<float*>(lds_raw) + (qw * 64 + lane) * (D / 2 + 2);
     if (kh == 1) {
@@ -260,8 +301,11 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   }
 }
 
-// combine split partials: one thread per (query, head, dim)
-template <typename T>
+// combine split partials: one thread per (query, head, dim). With the split count SP
+// known at compile time every partial is loaded before the first use (one memory round
+// trip instead of two per split); SP < 0 takes S at run time. The arithmetic and its
+// order are the same either way.
+template <typename T, int SP>
 __global__ void __launch_bounds__(kThreads)
 attn_merge_kernel(const float* __restrict__ po, const float* __restrict__ pml, int S, int r,
                   int H, int Dh, T* __restrict__ out) {
@@ -269,17 +313,47 @@ attn_merge_kernel(const float* __restrict__ po, const float* __restrict__ pml, i
   if (t >= (int64_t)r * H * Dh) return;
   const int64_t qh = t / Dh;
   const int d = (int)(t % Dh);
-  float m = -INFINITY;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, pml[((int64_t)s * r * H + qh) * 2]);
-  float l = 0.f, acc = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ms = pml[((int64_t)s * r * H + qh) * 2];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - m);
-    l += pml[((int64_t)s * r * H + qh) * 2 + 1] * w;
-    acc += po[((int64_t)s * r * H + qh) * Dh + d] * w;
+  const int64_t rh = (int64_t)r * H;
+  float m = -INFINITY, l = 0.f, acc = 0.f;
+  if constexpr (SP > 0) {
+    float mv[SP], lv[SP], ov[SP];
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      mv[s] = pml[(s * rh + qh) * 2];
+      lv[s] = pml[(s * rh + qh) * 2 + 1];
+      ov[s] = po[(s * rh + qh) * Dh + d];
+    }
+#pragma unroll
+    for (int s = 0; s < SP; ++s) m = fmaxf(m, mv[s]);
+    // a split with no finite score is skipped by selects, not a branch (which would let the
+    // compiler sink its loads behind the first wait)
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      const bool live = mv[s] != -INFINITY;
+      const float w = exp2f(mv[s] - m);
+      const float l2 = l + lv[s] * w, a2 = acc + ov[s] * w;
+      l = live ? l2 : l;
+      acc = live ? a2 : acc;
+    }
+  } else {
+    for (int s = 0; s < S; ++s) m = fmaxf(m, pml[(s * rh + qh) * 2]);
+    for (int s = 0; s < S; ++s) {
+      const float ms = pml[(s * rh + qh) * 2];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - m);
+      l += pml[(s * rh + qh) * 2 + 1] * w;
+      acc += po[(s * rh + qh) * Dh + d] * w;
+    }
   }
   out[qh * Dh + d] = from_f<T>(acc / l);
+}
+
+template <int SP>
+ec_status launch_merge(const float* po, const float* pml, int S, int r, int H, int Dh, bf16* out, hipStream_t s) {
+  const int64_t n = (int64_t)r * H * Dh;
+  attn_merge_kernel<bf16, SP><<<(int)((n + kThreads - 1) / kThreads), kThreads, 0, s>>>(po, pml, S, r, H, Dh, out);
+  EC_CHECK_LAUNCH("attn_merge_kernel");
+  return EC_OK;
 }
 
 // fp32 path: one workgroup per (query, head); scores in LDS, exact softmax.
@@ -388,10 +462,18 @@ ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, 
   AttnPlan p = plan_attn(r, L, H);
   const float sl = scale * kLog2e;
   dim3 grid(p.qtiles, H, p.splits);
+  static bool attr = false;
+  if (!attr) {
+    EC_CHECK_HIP(hipFuncSetAttribute((const void*)attn_bf16_kernel<false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds));
+    EC_CHECK_HIP(hipFuncSetAttribute((const void*)attn_bf16_kernel<true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds));
+    attr = true;
+  }
   if (p.splits == 1) {
-    attn_bf16_kernel<false><<<grid, kAttnThreads, 0, s>>>((const bf16*)q, (const bf16*)k,
-                                                      (const bf16*)v, r, L, H, sl, p.chunk,
-                                                      (bf16*)out, nullptr, nullptr);
+    attn_bf16_kernel<false><<<grid, kAttnThreads, kAttnLds, s>>>((const bf16*)q, (const bf16*)k,
+                                                             (const bf16*)v, r, L, H, sl, p.chunk,
+                                                             (bf16*)out, nullptr, nullptr);
     EC_CHECK_LAUNCH("attn_bf16_kernel");
     return EC_OK;
   }
@@ -399,14 +481,19 @@ ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, 
   EC_REQUIRE(ws && ws_bytes >= need, EC_ERR_WORKSPACE, "attn: workspace %zu < %zu", ws_bytes, need);
   float* po = (float*)ws;
   float* pml = po + (size_t)p.splits * r * H * Dh;
-  attn_bf16_kernel<true><<<grid, kAttnThreads, 0, s>>>((const bf16*)q, (const bf16*)k, (const bf16*)v,
-                                                   r, L, H, sl, p.chunk, nullptr, po, pml);
+  attn_bf16_kernel<true><<<grid, kAttnThreads, kAttnLds, s>>>((const bf16*)q, (const bf16*)k, (const bf16*)v,
+                                                          r, L, H, sl, p.chunk, nullptr, po, pml);
   EC_CHECK_LAUNCH("attn_bf16_kernel");
-  const int64_t n = (int64_t)r * H * Dh;
-  attn_merge_kernel<bf16><<<(int)((n + kThreads - 1) / kThreads), kThreads, 0, s>>>(
-      po, pml, p.splits, r, H, Dh, (bf16*)out);
-  EC_CHECK_LAUNCH("attn_merge_kernel");
-  return EC_OK;
+  bf16* o = (bf16*)out;
+  switch (p.splits) {
+#define EC_MERGE_CASE(n) \
+  case n: return launch_merge<n>(po, pml, p.splits, r, H, Dh, o, s);
+    EC_MERGE_CASE(2) EC_MERGE_CASE(3) EC_MERGE_CASE(4) EC_MERGE_CASE(5) EC_MERGE_CASE(6) EC_MERGE_CASE(7)
+    EC_MERGE_CASE(8) EC_MERGE_CASE(9) EC_MERGE_CASE(10) EC_MERGE_CASE(11) EC_MERGE_CASE(12)
+    EC_MERGE_CASE(13) EC_MERGE_CASE(14) EC_MERGE_CASE(15) EC_MERGE_CASE(16)
+#undef EC_MERGE_CASE
+    default: return launch_merge<-1>(po, pml, p.splits, r, H, Dh, o, s);
+  }
 }
 
 }  // namespace ec

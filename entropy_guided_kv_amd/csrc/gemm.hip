@@ -128,29 +128,8 @@ __device__ __forceinline__ int xcd_remap(int pid, int nblk) {
 //   SwiGLU:        [2F, d] with 32-row group g = gate rows 16g .. 16g+15, then up
 //                  rows 16g .. 16g+15.
 // Any column tile that is a multiple of 32 then keeps every pair in one wavefront.
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 typedef __attribute__((address_space(1))) bf16x4 gbf16x4;
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt out of range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-}
-// buffer resource over [base, base + bytes) (raw buffer, no stride, gfx9 dword3)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-// 16 bytes per lane from rsrc at voffset + soffset into LDS at lds + 16 * lane
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds, int voffset,
-                                                  int soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voffset, soffset, 0, 0);
-}
 
 // workgroup barrier for LDS produced by direct-to-LDS loads: the waits are explicit
 // (the loads are tracked by vmcnt only), the fences keep the compiler from moving
@@ -529,21 +508,44 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
 // -------------------------------------------------------------------- split-K reduction
 // Partials part[S][M][N] over the packed columns of the bf16 kernel. One thread per
 // output unit sums the S partials in order (deterministic), then the epilogue:
-// QKV and SwiGLU units are the (pc, pc + 16) pairs of each 32-column group.
+// QKV and SwiGLU units are the (pc, pc + 16) pairs of each 32-column group. With the
+// split count SP known at compile time every partial load is issued before the first
+// addition (one memory round trip, not S); SP < 0 takes S at run time.
+template <int SP>
+__device__ __forceinline__ void sum_parts(const float* __restrict__ part, int S, int64_t stride, int64_t o1,
+                                          int64_t o2, bool two, float& x1, float& x2) {
+  if constexpr (SP > 0) {
+    float p1[SP], p2[SP];
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      p1[s] = part[s * stride + o1];
+      p2[s] = two ? part[s * stride + o2] : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      x1 += p1[s];
+      x2 += p2[s];
+    }
+  } else {
+    for (int s = 0; s < S; ++s) {
+      x1 += part[s * stride + o1];
+      if (two) x2 += part[s * stride + o2];
+    }
+  }
+}
+
+template <int SP>
 __global__ void __launch_bounds__(kThreads)
 splitk_epilogue_kernel(const float* __restrict__ part, int S, int M, int N, int kind, EpiArgs epi) {
   const int64_t t = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+  const int64_t stride = (int64_t)M * N;
   if (kind == EPI_QKV || kind == EPI_SWIGLU) {
     const int64_t upr = N / 2;
     if (t >= (int64_t)M * upr) return;
     const int m = (int)(t / upr), u = (int)(t % upr);
     const int pc = (u >> 4) * 32 + (u & 15);
     float x1 = 0.f, x2 = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float* p = part + ((int64_t)s * M + m) * N;
-      x1 += p[pc];
-      x2 += p[pc + 16];
-    }
+    sum_parts<SP>(part, S, stride, (int64_t)m * N + pc, (int64_t)m * N + pc + 16, true, x1, x2);
     if (kind == EPI_SWIGLU) {
       epi_swiglu<bf16>(epi, m, u, x1, x2);
     } else {
@@ -553,8 +555,8 @@ splitk_epilogue_kernel(const float* __restrict__ part, int S, int M, int N, int 
   } else {
     if (t >= (int64_t)M * N) return;
     const int m = (int)(t / N), col = (int)(t % N);
-    float x = 0.f;
-    for (int s = 0; s < S; ++s) x += part[((int64_t)s * M + m) * N + col];
+    float x = 0.f, unused = 0.f;
+    sum_parts<SP>(part, S, stride, (int64_t)m * N + col, 0, false, x, unused);
     epi_single<bf16>(epi, m, col, x);
   }
 }
@@ -805,7 +807,12 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
     }
     const int64_t units = (kind == EPI_QKV || kind == EPI_SWIGLU) ? (int64_t)M * (NB / 2) : (int64_t)M * NB;
     const int blocks = (int)((units + kThreads - 1) / kThreads);
-    splitk_epilogue_kernel<<<blocks, kThreads, 0, s>>>(part, p.S, M, NB, kind, epi);
+    switch (p.S) {
+      case 2: splitk_epilogue_kernel<2><<<blocks, kThreads, 0, s>>>(part, p.S, M, NB, kind, epi); break;
+      case 4: splitk_epilogue_kernel<4><<<blocks, kThreads, 0, s>>>(part, p.S, M, NB, kind, epi); break;
+      case 8: splitk_epilogue_kernel<8><<<blocks, kThreads, 0, s>>>(part, p.S, M, NB, kind, epi); break;
+      default: splitk_epilogue_kernel<-1><<<blocks, kThreads, 0, s>>>(part, p.S, M, NB, kind, epi); break;
+    }
     EC_CHECK_LAUNCH("splitk_epilogue_kernel");
   }
   return EC_OK;

@@ -33,10 +33,6 @@ embed_kernel(const T* __restrict__ table, int vocab, const int32_t* __restrict__
 }
 
 // out[i, :] = T(h[src, :] / sqrt(mean(h[src]^2) + eps) * gain), src = idx ? idx[i] : i
-// The row is read once into registers when d <= 4 * kThreads * kNormRegs (d = 4096 takes
-// 4 float4 per thread); wider rows are read a second time for the scaling pass. Each
-// thread sums its own float4s in ascending order either way, so both forms round alike.
-constexpr int kNormRegs = 8;
 
 __device__ __forceinline__ void store4(bf16* y, float a, float b, float c, float e) {
   bf16x4 o;
@@ -55,9 +51,13 @@ __device__ __forceinline__ float4 load_gain4(const bf16* g) {
 }
 __device__ __forceinline__ float4 load_gain4(const float* g) { return *reinterpret_cast<const float4*>(g); }
 
-// With PARTS (the split-K residual fusion, idx unused): the row is first updated in
+// With partials (the split-K residual fusion, idx unused): the row is first updated in
 // place, h[i] += sum_s part[s][i] with the partials added in ascending s to a zero
 // start (the split-K epilogue's order), and the norm then reads the updated values.
+// SP > 0 is the partial count known at compile time: every load of the row and of its
+// partials is issued before the first addition, so the partials cost one memory round
+// trip rather than one per partial and register slot. SP < 0 takes the count S at run
+// time (one partial at a time); SP = 0 has no partials.
 __device__ __forceinline__ float4 add_parts(float4 v, const float* __restrict__ part, int S, int M, int i,
                                             int d, int j) {
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -71,28 +71,54 @@ __device__ __forceinline__ float4 add_parts(float4 v, const float* __restrict__ 
   return make_float4(v.x + a.x, v.y + a.y, v.z + a.z, v.w + a.w);
 }
 
-template <typename T, bool PARTS>
+// NREG float4 per thread hold the row when d <= 4 * kThreads * NREG; each thread sums its
+// own float4s in ascending order, and wider rows (read a second time for the scaling
+// pass) round alike.
+template <typename T, int SP, int NREG>
 __global__ void __launch_bounds__(kThreads)
 rmsnorm_kernel(float* __restrict__ h, int n_src, const int32_t* __restrict__ idx, int d,
                const T* __restrict__ gain, float eps, T* __restrict__ out, const float* __restrict__ part,
                int S) {
+  constexpr bool PARTS = SP != 0;
   const int i = blockIdx.x;
   int src = (!PARTS && idx) ? idx[i] : i;
   if (src < 0 || src >= n_src) src = 0;  // invalid index: normalise row 0 (no out-of-range read)
   float* x = h + (int64_t)src * d;
-  const bool in_regs = d <= 4 * kThreads * kNormRegs;
-  float4 v[kNormRegs];
+  const bool in_regs = d <= 4 * kThreads * NREG;
+  float4 v[NREG];
   float ss = 0.f;
   if (in_regs) {
+    // slots past the row end load its last float4 (kept in bounds, never used)
 #pragma unroll
-    for (int k = 0; k < kNormRegs; ++k) {
+    for (int k = 0; k < NREG; ++k) {
+      const int j = min((threadIdx.x + k * kThreads) * 4, d - 4);
+      v[k] = *reinterpret_cast<const float4*>(x + j);
+    }
+    if constexpr (SP > 0) {
+      float4 a[NREG];
+#pragma unroll
+      for (int k = 0; k < NREG; ++k) a[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int s = 0; s < SP; ++s)
+#pragma unroll
+        for (int k = 0; k < NREG; ++k) {
+          const int j = min((threadIdx.x + k * kThreads) * 4, d - 4);
+          const float4 p = *reinterpret_cast<const float4*>(part + ((int64_t)s * n_src + i) * d + j);
+          a[k].x += p.x;
+          a[k].y += p.y;
+          a[k].z += p.z;
+          a[k].w += p.w;
+        }
+#pragma unroll
+      for (int k = 0; k < NREG; ++k)
+        v[k] = make_float4(v[k].x + a[k].x, v[k].y + a[k].y, v[k].z + a[k].z, v[k].w + a[k].w);
+    }
+#pragma unroll
+    for (int k = 0; k < NREG; ++k) {
       const int j = (threadIdx.x + k * kThreads) * 4;
       if (j < d) {
-        v[k] = *reinterpret_cast<const float4*>(x + j);
-        if (PARTS) {
-          v[k] = add_parts(v[k], part, S, n_src, i, d, j);
-          *reinterpret_cast<float4*>(x + j) = v[k];
-        }
+        if constexpr (SP < 0) v[k] = add_parts(v[k], part, S, n_src, i, d, j);
+        if constexpr (PARTS) *reinterpret_cast<float4*>(x + j) = v[k];
         ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
       }
     }
@@ -100,7 +126,7 @@ rmsnorm_kernel(float* __restrict__ h, int n_src, const int32_t* __restrict__ idx
     for (int j = threadIdx.x * 4; j < d; j += kThreads * 4) {
       float4 w = *reinterpret_cast<const float4*>(x + j);
       if (PARTS) {
-        w = add_parts(w, part, S, n_src, i, d, j);
+        w = add_parts(w, part, SP > 0 ? SP : S, n_src, i, d, j);
         *reinterpret_cast<float4*>(x + j) = w;
       }
       ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
@@ -118,7 +144,7 @@ rmsnorm_kernel(float* __restrict__ h, int n_src, const int32_t* __restrict__ idx
   T* y = out + (int64_t)i * d;
   if (in_regs) {
 #pragma unroll
-    for (int k = 0; k < kNormRegs; ++k) {
+    for (int k = 0; k < NREG; ++k) {
       const int j = (threadIdx.x + k * kThreads) * 4;
       if (j < d) {
         const float4 g = load_gain4(gain + j);
@@ -175,6 +201,28 @@ __global__ void rope_table_kernel(float* c, float* sn, int max_pos, int half, in
   }
 }
 
+// register slots per thread: 4 float4 cover rows up to 4096 wide, 8 up to 8192
+template <typename T, int SP>
+ec_status launch_norm(float* h, int n_src, const int32_t* idx, int n, int d, const T* gain, float eps, T* out,
+                      const float* part, int S, hipStream_t s) {
+  if (d <= 4 * kThreads * 4)
+    rmsnorm_kernel<T, SP, 4><<<n, kThreads, 0, s>>>(h, n_src, idx, d, gain, eps, out, part, S);
+  else
+    rmsnorm_kernel<T, SP, 8><<<n, kThreads, 0, s>>>(h, n_src, idx, d, gain, eps, out, part, S);
+  EC_CHECK_LAUNCH("rmsnorm_kernel");
+  return EC_OK;
+}
+template <typename T>
+ec_status resid_norm_t(const float* part, int S, int M, int d, float* h, const T* gain, float eps, T* out,
+                       hipStream_t s) {
+  switch (S) {
+    case 2: return launch_norm<T, 2>(h, M, nullptr, M, d, gain, eps, out, part, S, s);
+    case 4: return launch_norm<T, 4>(h, M, nullptr, M, d, gain, eps, out, part, S, s);
+    case 8: return launch_norm<T, 8>(h, M, nullptr, M, d, gain, eps, out, part, S, s);
+    default: return launch_norm<T, -1>(h, M, nullptr, M, d, gain, eps, out, part, S, s);
+  }
+}
+
 }  // namespace
 
 ec_status embed(ec_dtype dt, const void* table, int vocab, const int32_t* tokens, int L,
@@ -195,27 +243,17 @@ ec_status rmsnorm(ec_dtype dt, const float* h, int n_src, const int32_t* idx, in
   EC_REQUIRE(d % 4 == 0, EC_ERR_UNSUPPORTED, "rmsnorm: d_model %d not a multiple of 4", d);
   float* hm = const_cast<float*>(h);  // read only without parts
   if (dt == EC_BF16)
-    rmsnorm_kernel<bf16, false><<<n, kThreads, 0, s>>>(hm, n_src, idx, d, (const bf16*)gain, eps, (bf16*)out,
-                                                        nullptr, 0);
-  else
-    rmsnorm_kernel<float, false><<<n, kThreads, 0, s>>>(hm, n_src, idx, d, (const float*)gain, eps,
-                                                         (float*)out, nullptr, 0);
-  EC_CHECK_LAUNCH("rmsnorm_kernel");
-  return EC_OK;
+    return launch_norm<bf16, 0>(hm, n_src, idx, n, d, (const bf16*)gain, eps, (bf16*)out, nullptr, 0, s);
+  return launch_norm<float, 0>(hm, n_src, idx, n, d, (const float*)gain, eps, (float*)out, nullptr, 0, s);
 }
 
 ec_status resid_norm(ec_dtype dt, const float* part, int S, int M, int d, float* h, const void* gain,
                      float eps, void* out, hipStream_t s) {
   if (M == 0) return EC_OK;
   EC_REQUIRE(d % 4 == 0, EC_ERR_UNSUPPORTED, "resid_norm: d_model %d not a multiple of 4", d);
-  if (dt == EC_BF16)
-    rmsnorm_kernel<bf16, true><<<M, kThreads, 0, s>>>(h, M, nullptr, d, (const bf16*)gain, eps, (bf16*)out,
-                                                       part, S);
-  else
-    rmsnorm_kernel<float, true><<<M, kThreads, 0, s>>>(h, M, nullptr, d, (const float*)gain, eps,
-                                                        (float*)out, part, S);
-  EC_CHECK_LAUNCH("rmsnorm_kernel");
-  return EC_OK;
+  EC_REQUIRE(S >= 1, EC_ERR_ARG, "resid_norm: %d partials", S);
+  if (dt == EC_BF16) return resid_norm_t<bf16>(part, S, M, d, h, (const bf16*)gain, eps, (bf16*)out, s);
+  return resid_norm_t<float>(part, S, M, d, h, (const float*)gain, eps, (float*)out, s);
 }
 
 ec_status scatter(ec_dtype dt, void* kc, void* vc, int64_t L, int width, const void* kr,
