@@ -409,10 +409,10 @@ struct AttnPlan {
   int qtiles, splits, chunk;
 };
 
-// Key-range split by a cost model fitted to MI355X measurements (r = 17 .. 1024,
-// L = 1024 and 4096, 32 heads): waves of workgroups x tiles per workgroup x 1.15 us,
-// plus, when split, 3 us for the merge launch and 0.018 us per (split x query) for
-// the partials' round trip (scaled by H / 32).
+// Key-range split by a cost model fitted to MI355X measurements of every split count
+// (r = 17 .. 4096 queries, L = 1024 and 4096, 32 heads; it picks the fastest on each):
+// waves of workgroups x tiles per workgroup x 0.9 us, plus, when split, 0.008 us per
+// (split x query) for the partials' round trip and merge (scaled by H / 32).
 AttnPlan plan_attn(int r, int L, int H) {
   AttnPlan p;
   p.qtiles = (r + BQ - 1) / BQ;
@@ -424,8 +424,8 @@ AttnPlan plan_attn(int r, int L, int H) {
     const int chunk = ((L + s - 1) / s + BKV - 1) / BKV * BKV;
     const int splits = (L + chunk - 1) / chunk;
     const double waves = (double)(((int64_t)base * splits + 255) / 256);
-    double us = waves * (chunk / BKV) * 1.15;
-    if (splits > 1) us += 3.0 + 0.018 * splits * r * (H / 32.0);
+    double us = waves * (chunk / BKV) * 0.9;
+    if (splits > 1) us += 0.008 * splits * r * (H / 32.0);
     if (us < best) {
       best = us;
       s_best = s;
