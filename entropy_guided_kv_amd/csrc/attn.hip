@@ -20,12 +20,13 @@
 // element j of each of four source lanes' 8-byte rows), two per fragment.
 // Softmax statistics are per lane (one query), completed with one
 // cross-half exchange; the reference max is only moved (and O, l rescaled)
-// when a row max exceeds it by 2^8, so most tiles skip the rescale. Q stays
-// in registers; K and V tiles of 64 keys go from global memory straight into a
-// ring of kStages LDS stages (buffer_load_dwordx4 ... lds, no staging registers),
-// so that the loads of the next kStages - 1 tiles are in flight during the
-// current tile's MFMAs (a split of up to kStages tiles issues all of its loads at
-// once). The tiles are shared by the
+// when a row max exceeds it by 2^8, so most tiles skip the rescale. All global
+// loads go straight into LDS (buffer_load_dwordx4 ... lds, no staging registers):
+// the 128-query Q tile once, issued with the first K/V tiles and then read into
+// registers for the whole loop, and the K and V tiles of 64 keys through a ring
+// of kStages LDS stages, so that the loads of the next kStages - 1 tiles are in
+// flight during the current tile's MFMAs (a split of up to kStages tiles issues
+// all of its loads at once). The tiles are shared by the
 // 8 wavefronts of a workgroup: 4 groups of 32 queries (128 queries), the two
 // wavefronts of a group taking the lower and the upper 32 keys of every tile
 // (two wavefronts per SIMD: one's softmax and LDS reads overlap the other's
@@ -53,10 +54,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
 
-constexpr int kStages = 4;                          // LDS ring of K/V tiles
-constexpr int kStageBytes = 2 * BKV * KS * 2;          // K and V of one tile
-constexpr int kQOff = kStages * kStageBytes;           // Q tile (BQ rows of 256 bytes) after the ring
-constexpr int kHandBytes = 4 * 64 * (D / 2 + 2) * 4;   // (m, l, o) hand-over after the loop (over the ring)
+constexpr int kStages = 4;                            // LDS ring of K/V tiles
+constexpr int kStageBytes = 2 * BKV * KS * 2;           // K and V of one tile
+constexpr int kQOff = kStages * kStageBytes;            // Q tile (BQ rows of 256 bytes) after the ring
+constexpr int kHandBytes = 4 * 64 * (D / 2 + 2) * 4;    // (m, l, o) hand-over after the loop, over the ring
 constexpr int kAttnLds = kQOff + BQ * D * 2;
 static_assert(kHandBytes <= kQOff, "hand-over fits in the ring");
 static_assert(kAttnLds <= 160 * 1024, "LDS budget");
