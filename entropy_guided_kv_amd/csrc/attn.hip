@@ -48,6 +48,7 @@ constexpr int BQ = 128;      // queries per workgroup (32 per wavefront)
 constexpr int BKV = 64;      // keys per LDS stage
 constexpr int KS = D;        // LDS row stride (bf16): unpadded 256-byte rows, swizzled (below)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMaxFloor = -1e30f;  // below every reachable score in log2 units
 constexpr float kRescale = 8.f;  // lazy rescale: keep the reference max until a row max exceeds it by 2^8
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -104,7 +105,11 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
-  float m_ref = -INFINITY, l_run = 0.f;  // reference max (log2 units) and row sum
+  // reference max (log2 units) and row sum. The max starts at a finite floor, not -inf:
+  // a wavefront whose keys are all masked (its half of a split holding at most 32 keys,
+  // or a cache of at most 32 rows) then gets p = 2^(-inf - floor) = 0 instead of
+  // 2^(-inf + inf) = NaN, and hands over o = 0, l = 0 with a weight of 0.
+  float m_ref = kMaxFloor, l_run = 0.f;
 
   const int kv_lo = split * kv_chunk;
   const int kv_hi = min(L, kv_lo + kv_chunk);

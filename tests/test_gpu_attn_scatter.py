@@ -64,7 +64,15 @@ def _attn_case(r, L, H, D, dtype, seed=0, scale=1.0):
 
 @pytest.mark.parametrize("r,L,H", [(143, 1024, 4), (1, 1024, 2), (257, 512, 3), (128, 128, 1),
                                    (17, 1000, 2), (1024, 1024, 2), (33, 4096, 2),
-                                   (40, 700, 8), (96, 900, 24)])  # 6 and 3 key splits (ragged)
+                                   (40, 700, 8), (96, 900, 24),
+                                   # with the split cost model of the kernel these take 3, 7, 9,
+                                   # 10, 11, 12, 13, 14 and 15 key splits (most with a ragged last
+                                   # tile), so that every merge width is compared with the oracle
+                                   (1, 192, 1), (1, 769, 1), (1, 1025, 1), (3, 1250, 2), (5, 1400, 3),
+                                   (2, 768, 1), (1, 1600, 1), (1, 1700, 1), (1, 1800, 1),
+                                   # caches of 1, 29 and 33 rows: the upper-key wavefront of the
+                                   # only tile sees no key (or one), whose softmax terms must be 0
+                                   (4, 1, 2), (7, 29, 3), (1, 33, 1)])
 def test_partial_attn_bf16(r, L, H):
     got, want = _attn_case(r, L, H, 128, torch.bfloat16, seed=r + L, scale=0.35)
     err = row_rel_err(got.reshape(r * H, 128), want.reshape(r * H, 128))
