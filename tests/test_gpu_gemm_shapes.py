@@ -2,12 +2,16 @@
 
 One layer with d=4096, 32 heads of 128, SwiGLU width 12288 (the 8B-shaped
 model's projection shapes) and a small vocabulary, so the oracle forward
-stays fast. The row counts pick every tile configuration the GEMMs use:
-1024 rows (a refresh: 256x192 tiles for q|k|v and gate/up, 128x128 for the
-output and down projections), 300 rows (128x128, split K), 40 rows (64-row
-tiles, split K) and 17 rows (32-row tiles, split K). Bars as in the other
-forward tests: 2e-2 relative for hidden states, logits and cached K/V, argmax
-exact where the logit margin clears the gate.
+stays fast. The row counts pick every tile configuration and split width the
+GEMM planner uses on these shapes: 1024 rows (a refresh: 256x192 tiles for
+q|k|v and gate/up, 128x128 for the output projection, 256x128 with two K
+splits for down, reduced together with the next RMSNorm), 300 rows (256x128
+q|k|v, 64x128 output projection, down in four splits), 144 rows (128x128 q|k|v,
+output projection in four splits, down in eight), 40 and 17 rows (64x128 tiles,
+q|k|v in two and eight splits) and 1 row (gate/up in four splits: the split-K
+SwiGLU epilogue). Bars as in the other forward tests: 2e-2 relative for hidden
+states, logits and cached K/V, argmax exact where the logit margin clears the
+gate.
 
 Also: ec_pack_weights moves exactly the rows its layout definition names.
 """
@@ -24,7 +28,7 @@ pytestmark = pytest.mark.gpu
 WIDE = synth.ModelShape("wide", "bf16", 1, 4096, 32, 128, 12288, 1024)
 
 
-@pytest.mark.parametrize("n_rows", [1024, 300, 144, 40, 17])
+@pytest.mark.parametrize("n_rows", [1024, 300, 144, 40, 17, 1])
 def test_forward_at_8b_layer_width(n_rows):
     L = 1024
     w, omm, dm, cache, oc = _setup(WIDE, L, seed=11, stale=n_rows < L)
