@@ -46,7 +46,7 @@ def _setup(shape, L, seed=0, n_layers=None, stale=True):
     return w, om_model, dm, cache, ocache
 
 
-def _compare(shape, om_model, dm, cache, ocache, tokens, rows, out_pos):
+def _compare(shape, om_model, dm, cache, ocache, tokens, rows, out_pos, check_ids=True):
     from entropy_guided_kv_amd import api
     L = len(tokens)
     where = {int(p): i for i, p in enumerate(rows)}
@@ -63,8 +63,10 @@ def _compare(shape, om_model, dm, cache, ocache, tokens, rows, out_pos):
     ev = max(rel_err(to_f64(cache.v[i]), ocache[i][1]) for i in range(len(ocache)))
     print(f"{shape.name}: rows={len(rows)} hidden {eh:.2e} logits {el:.2e} K {ek:.2e} V {ev:.2e}")
     assert eh <= tol and el <= tol and ek <= tol and ev <= tol
-    # argmax ids: identical wherever the oracle's top-1/top-2 margin clears the gate
     lg = to_f64(logits)
+    if not check_ids:
+        return lg, ref
+    # argmax ids: identical wherever the oracle's top-1/top-2 margin clears the gate
     srt = np.sort(ref["logits"], axis=1)
     margin = srt[:, -1] - srt[:, -2]
     gate = margin_gate(srt[:, -1], margin) if shape.dtype == "bf16" else margin > 1e-2

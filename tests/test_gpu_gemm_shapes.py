@@ -39,6 +39,27 @@ def test_forward_at_8b_layer_width(n_rows):
     _compare(WIDE, omm, dm, cache, oc, tokens, rows, out)
 
 
+WIDE13 = synth.ModelShape("wide13", "bf16", 1, 5120, 40, 128, 13824, 1024)
+
+
+@pytest.mark.parametrize("n_rows", [256, 77])
+def test_forward_wider_than_4096(n_rows):
+    """A 13B-shaped layer (d = 5120, 40 heads, SwiGLU width 13824): rows wider than 4096
+    take the RMSNorm form that holds eight float4 per thread, and the GEMM planner sees
+    projection shapes it was not fitted on. Checked against the hidden-state, logit and
+    K/V bars only: the argmax gate is exercised at the 8B width above, while here one
+    of the 77-row case's sampled rows is a near tie (top-1 4.59, margin 0.0625 = 1.4 % of
+    it, two bf16 steps) whose order the bf16 path's logit error (6e-3 relative, the same
+    as at the 8B width) can flip."""
+    L = 256
+    w, omm, dm, cache, oc = _setup(WIDE13, L, seed=21, stale=n_rows < L)
+    rng = np.random.default_rng(22)
+    tokens = rng.integers(0, WIDE13.vocab - 1, L).astype(np.int32)
+    rows = np.arange(L) if n_rows == L else np.sort(rng.choice(L, n_rows, replace=False))
+    out = rows[np.sort(rng.choice(len(rows), min(len(rows), 24), replace=False))]
+    _compare(WIDE13, omm, dm, cache, oc, tokens, rows, out, check_ids=False)
+
+
 def _packed_qkv_order(d, D):
     """Row order of the packed q|k|v matrix: inside each head, group g of 32 rows is
     first-half rows 16g..16g+15 then their rotary partners D/2 + 16g .. D/2 + 16g + 15."""
