@@ -63,6 +63,14 @@ constexpr int kAttnLds = kQOff + BQ * D * 2;
 static_assert(kHandBytes <= kQOff, "hand-over fits in the ring");
 static_assert(kAttnLds <= 160 * 1024, "LDS budget");
 
+// {x[l % 32], x[l % 32 + 32]} on every lane l: a lane's value and its partner's in the
+// other half of the wavefront, lower half first (v_permlane32_swap_b32, no LDS round trip)
+__device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
 // grid: (query tiles, heads, splits); dynamic LDS of kAttnLds bytes
 template <bool SPLIT>
 __global__ void __launch_bounds__(kAttnThreads)
@@ -211,7 +219,11 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
       float tmax = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, st[v]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;
+      {
+        float a, b;
+        half_pair(tmax, a, b);
+        tmax = fmaxf(a, b) * scale_log2;
+      }
       // lazy rescale: only when some row's max moved past the reference by 2^kRescale
       if (__any(tmax > m_ref + kRescale)) {
         const float m_new = fmaxf(m_ref, tmax);
@@ -231,7 +243,11 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
         psum += p;
         fp[v / 8][v % 8] = (bf16)p;
       }
-      l_run += psum + __shfl_xor(psum, 32);
+      {
+        float a, b;
+        half_pair(psum, a, b);
+        l_run += a + b;
+      }
       // ---- O^T[d, q] += V^T[d, keys] P^T[keys, q]; A operand by transpose reads, all
       // eight fragments read before the MFMAs
       bf16x8 fv[2][D / 32];
