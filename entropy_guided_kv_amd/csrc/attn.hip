@@ -56,8 +56,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
 
 constexpr int kStages = 4;                            // LDS ring of K/V tiles
-constexpr int kStageBytes = 2 * BKV * KS * 2;           // K and V of one tile
-constexpr int kQOff = kStages * kStageBytes;            // Q tile (BQ rows of 256 bytes) after the ring
+constexpr int kTileBytes = BKV * KS * 2;                // K (or V) of one tile
+constexpr int kVOff = kStages * kTileBytes;             // V stages after the K stages
+constexpr int kQOff = 2 * kStages * kTileBytes;         // Q tile (BQ rows of 256 bytes) after the ring
 constexpr int kHandBytes = 4 * 64 * (D / 2 + 2) * 4;    // (m, l, o) hand-over after the loop, over the ring
 constexpr int kAttnLds = kQOff + BQ * D * 2;
 static_assert(kHandBytes <= kQOff, "hand-over fits in the ring");
@@ -78,8 +79,11 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                  const bf16* __restrict__ vc, int r, int L, int H, float scale_log2,
                  int kv_chunk, bf16* __restrict__ out, float* __restrict__ po,
                  float* __restrict__ pml) {
-  // K and V tiles in natural [key][dim] layout, one stage per tile of the ring;
-  // after the loop the LDS holds the (m, l, o) hand-over.
+  // K and V tiles in natural [key][dim] layout, one stage per tile of the ring: the four
+  // K stages in the first 64 KB, the four V stages in the next, so that with the tile loop
+  // unrolled over the stages every fragment read is a per-lane base register (computed
+  // once) plus an immediate offset below 64 KB. After the loop the LDS holds the
+  // (m, l, o) hand-over.
   // LDS layout (64 banks of 4 bytes): a K row keeps its 16-byte chunk c at c ^ (row % 16), so the
   // 16 rows one b128 fragment read serves per cycle hit 16 distinct bank groups; a V row keeps
   // its 64-byte quarter q (dims 32q .. 32q+31) at q ^ (row % 4), so the four consecutive keys of
@@ -130,23 +134,38 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   // (masked below).
   const __amdgpu_buffer_rsrc_t rK = buffer_rsrc(kc, (int64_t)L * HD * 2);
   const __amdgpu_buffer_rsrc_t rV = buffer_rsrc(vc, (int64_t)L * HD * 2);
-  int lrow[2], ck[2], cv[2];
+  int lrow[2], ok_[2], ov_[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int sl = i * 8 + wave, row = 4 * sl + lane / 16, pos = lane % 16;
     lrow[i] = row;
-    ck[i] = (pos ^ (row & 15)) * 16;                                    // bytes within the row
-    cv[i] = ((((pos >> 2) ^ (row & 3)) << 2) | (pos & 3)) * 16;
+    const int ck = (pos ^ (row & 15)) * 16;  // bytes within the row
+    const int cv = ((((pos >> 2) ^ (row & 3)) << 2) | (pos & 3)) * 16;
+    const int rb = (int)(((int64_t)row * HD + h * D) * 2);
+    ok_[i] = rb + ck;
+    ov_[i] = rb + cv;
   }
-  auto issue = [&](int t) __attribute__((always_inline)) {
+  // a whole tile takes its key offset in the scalar offset of the load; the last tile of a
+  // range that ends past the cache (keys >= L) clamps each lane's row instead
+  auto issue = [&](int t, int stage) __attribute__((always_inline)) {
     const int kv0 = kv_lo + t * BKV;
-    unsigned char* st = lds_raw + (t % kStages) * kStageBytes;
+    unsigned char* sk = lds_raw + stage * kTileBytes;
+    unsigned char* sv = lds_raw + kVOff + stage * kTileBytes;
+    if (kv0 + BKV <= L) {
+      const int so = (int)((int64_t)kv0 * HD * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int key = min(kv0 + lrow[i], L - 1);
-      const int base = (int)(((int64_t)key * HD + h * D) * 2);
-      buffer_load_lds16(rK, st + (i * 8 + wave) * 1024, base + ck[i], 0);
-      buffer_load_lds16(rV, st + BKV * KS * 2 + (i * 8 + wave) * 1024, base + cv[i], 0);
+      for (int i = 0; i < 2; ++i) {
+        buffer_load_lds16(rK, sk + (i * 8 + wave) * 1024, ok_[i], so);
+        buffer_load_lds16(rV, sv + (i * 8 + wave) * 1024, ov_[i], so);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int key = min(kv0 + lrow[i], L - 1);
+        const int d0 = (int)(((int64_t)(key - lrow[i]) * HD) * 2);
+        buffer_load_lds16(rK, sk + (i * 8 + wave) * 1024, ok_[i] + d0, 0);
+        buffer_load_lds16(rV, sv + (i * 8 + wave) * 1024, ov_[i] + d0, 0);
+      }
     }
   };
   constexpr int kLoadsPerTile = 4;  // per wavefront
@@ -157,7 +176,9 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   const int tr_key = (lane % 16) / 4, tr_dim = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
 
   int issued = min(kStages, ntiles);
-  for (int t = 0; t < issued; ++t) issue(t);
+#pragma unroll
+  for (int t = 0; t < kStages; ++t)
+    if (t < issued) issue(t, t);
   // Q fragments (B operand of S^T): Q[qrow][16kk + 8g .. +7], read once the Q loads (older
   // than every tile's) have landed in every wavefront
   switch (issued) {
@@ -175,7 +196,23 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   for (int kk = 0; kk < D / 16; ++kk)
     fq[kk] = *reinterpret_cast<const bf16x8*>(lds_raw + kQOff + (qw * 32 + lq) * (D * 2) +
                                                (((2 * kk + g) ^ (lq & 15)) * 16));
-  for (int t = 0; t < ntiles; ++t) {
+  // per-lane LDS offsets of the fragment reads (the stage adds an immediate): the V ones
+  // carry the V region's 64 KB themselves, passed through an empty asm so that the
+  // compiler keeps it in the register and the stage offset stays a 16-bit immediate
+  int koff[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = ((kh * 32 + lq) * KS + (((2 * kk + g) ^ (lq & 15)) * 8)) * 2;
+  int voff[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    voff[i] = kVOff + ((kh * 32 + 4 * g + tr_key) * KS + 32 * (i ^ tr_key) + tr_dim) * 2;
+    __asm__ volatile("" : "+v"(voff[i]));
+  }
+  for (int t0 = 0; t0 < ntiles; t0 += kStages)
+#pragma unroll
+  for (int u = 0; u < kStages; ++u) {
+    const int t = t0 + u;
+    if (t >= ntiles) break;
     // this wavefront's loads of tile t (and of Q) have landed once at most the loads of
     // the tiles issued after t are outstanding; the barrier then publishes every
     // wavefront's share, and tells that all have finished tile t - 1, whose stage is
@@ -191,12 +228,12 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (t >= 1 && t - 1 + kStages < ntiles) {
-      issue(t - 1 + kStages);
+      issue(t - 1 + kStages, (u + kStages - 1) % kStages);
       ++issued;
     }
     const int kv0 = kv_lo + t * BKV;
-    const bf16* kt = reinterpret_cast<const bf16*>(lds_raw + (t % kStages) * kStageBytes);
-    const lds_bf16* vt = (const lds_bf16*)(kt + BKV * KS);
+    const unsigned char* kst = lds_raw + u * kTileBytes;   // + koff[kk]
+    const unsigned char* vst = lds_raw + u * kTileBytes;   // + voff[i] (which holds kVOff)
     {
       const int sub = kh;  // this wavefront's 32 keys of the tile
       // ---- S^T[32 keys, 32 queries] (raw dot products)
@@ -206,8 +243,7 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
       // all K fragments first, so that the MFMA chain waits for LDS once
       bf16x8 fk[D / 16];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        fk[kk] = *reinterpret_cast<const bf16x8*>(kt + (sub * 32 + lq) * KS + (((2 * kk + g) ^ (lq & 15)) * 8));
+      for (int kk = 0; kk < D / 16; ++kk) fk[kk] = *reinterpret_cast<const bf16x8*>(kst + koff[kk]);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[kk], fq[kk], st, 0, 0, 0);
       // key of st[v]: kv0 + sub*32 + 8(v/4) + 4g + v%4; mask keys past the end of the range
@@ -255,8 +291,8 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
-          const int kb = sub * 32 + 16 * c + 4 * g + tr_key;
-          const lds_bf16* p0 = vt + kb * KS + 32 * (i ^ tr_key) + tr_dim;  // kb % 4 == tr_key
+          // key sub*32 + 16c + 4g + tr_key (= tr_key mod 4), dims 32 (i ^ tr_key) + tr_dim
+          const lds_bf16* p0 = (const lds_bf16*)(vst + voff[i] + 16 * c * KS * 2);
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * KS));
           const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
