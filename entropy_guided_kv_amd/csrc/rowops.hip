@@ -85,14 +85,16 @@ rmsnorm_kernel(float* __restrict__ h, int n_src, const int32_t* __restrict__ idx
   if (src < 0 || src >= n_src) src = 0;  // invalid index: normalise row 0 (no out-of-range read)
   float* x = h + (int64_t)src * d;
   const bool in_regs = d <= 4 * kThreads * NREG;
-  float4 v[NREG];
+  float4 v[NREG], gv[NREG];
   float ss = 0.f;
   if (in_regs) {
-    // slots past the row end load its last float4 (kept in bounds, never used)
+    // slots past the row end load its last float4 (kept in bounds, never used); the gain
+    // is loaded with the row, so the scaling pass does not wait for memory again
 #pragma unroll
     for (int k = 0; k < NREG; ++k) {
       const int j = min((threadIdx.x + k * kThreads) * 4, d - 4);
       v[k] = *reinterpret_cast<const float4*>(x + j);
+      gv[k] = load_gain4(gain + j);
     }
     if constexpr (SP > 0) {
       float4 a[NREG];
@@ -147,7 +149,7 @@ rmsnorm_kernel(float* __restrict__ h, int n_src, const int32_t* __restrict__ idx
     for (int k = 0; k < NREG; ++k) {
       const int j = (threadIdx.x + k * kThreads) * 4;
       if (j < d) {
-        const float4 g = load_gain4(gain + j);
+        const float4 g = gv[k];
         store4(y + j, v[k].x * rs * g.x, v[k].y * rs * g.y, v[k].z * rs * g.z, v[k].w * rs * g.w);
       }
     }
