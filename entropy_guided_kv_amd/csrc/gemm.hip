@@ -195,6 +195,14 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   const int m0 = mt * BM, n0 = nt * BN;
   const int kbeg = kz * k_chunk;
   const int nk = k_chunk / BKS;
+  // With one row tile (skinny M: skip steps, the LM head over the candidates) and at least
+  // 64 weight tiles, the K loop of weight tile nt starts at step rot and wraps: tiles
+  // running at the same time then read different K columns, which spreads their weight
+  // rows (K x 2 bytes apart) over the L2 channels instead of one (up to 18 % faster at
+  // 17 .. 256 rows). With several row tiles the tiles of a group walk K together to share
+  // A in L2, and with few weight tiles the K splits already spread the reads, so there is
+  // no rotation. The order depends only on the weight tile and the plan.
+  const int rot = (MT == 1 && ntk / splits >= 64) ? (int)(((unsigned)nt * 5u) % (unsigned)nk) : 0;
 
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -221,7 +229,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   }
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
     unsigned char* base = smem + stage * STAGE;
-    const int ks = kt * BKS * 2;
+    const int ks = (kt + rot < nk ? kt + rot : kt + rot - nk) * BKS * 2;
 #pragma unroll
     for (int i = 0; i < LPA; ++i) buffer_load_lds16(rA, base + (i * NW + wave) * 1024, oa[i], ks);
 #pragma unroll
@@ -640,10 +648,10 @@ struct TileInfo {
   double eff;  // sustained MFMA rate relative to 4 TFLOP/s per CU, measured on MI355X
 };
 constexpr TileInfo kTile[kNumTileCfg] = {
-    {256, 192, 1.10}, {256, 128, 1.10}, {128, 128, 0.90}, {64, 128, 0.55}};
+    {256, 192, 1.10}, {256, 128, 1.10}, {128, 128, 0.80}, {64, 128, 0.45}};
 // Sustained global-to-LDS rate of one CU (bytes per microsecond) with the weights streamed
 // from HBM: a tile's staging time is (BM + BN) x K x 2 bytes at this rate.
-constexpr double kCuLoadBytesPerUs = 50e3;
+constexpr double kCuLoadBytesPerUs = 60e3;
 
 struct Plan {
   TileCfg cfg;
@@ -656,8 +664,9 @@ struct Plan {
 // ceil(tiles * S / 256), per-tile time = the larger of the MFMA time
 // 2 BM BN (K / S) / (eff x 4 TFLOP/s) and the staging time (BM + BN) (K / S) 2 bytes
 // at kCuLoadBytesPerUs, plus, for split K, the partials' round trip (S M N x 8 bytes at
-// 3 TB/s) and 6 us for the reduction launch. Over the measured shapes the choice costs
-// 0.1 % more than the best candidate in total and at most 8 % on one shape. Larger
+// 3 TB/s) and 6 us for the reduction launch (measured with the K rotation of skinny
+// tiles). Over the measured shapes the choice costs 0.2 % more than the best candidate
+// in total, at most 4 % on a shape but one (17 x 12288 x 4096: 26 %). Larger
 // tiles carry more MFMA work per staged byte; smaller ones
 // and split K fill the 256 CUs at skinny M (skip steps, the LM head over the
 // candidates). Every tile shape and split S in {1, 2, 4, 8} (K chunks of at least
