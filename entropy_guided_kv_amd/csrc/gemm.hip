@@ -195,14 +195,16 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   const int m0 = mt * BM, n0 = nt * BN;
   const int kbeg = kz * k_chunk;
   const int nk = k_chunk / BKS;
-  // With one row tile (skinny M: skip steps, the LM head over the candidates) and at least
-  // 64 weight tiles, the K loop of weight tile nt starts at step rot and wraps: tiles
-  // running at the same time then read different K columns, which spreads their weight
-  // rows (K x 2 bytes apart) over the L2 channels instead of one (up to 18 % faster at
-  // 17 .. 256 rows). With several row tiles the tiles of a group walk K together to share
-  // A in L2, and with few weight tiles the K splits already spread the reads, so there is
-  // no rotation. The order depends only on the weight tile and the plan.
-  const int rot = (MT == 1 && ntk / splits >= 64) ? (int)(((unsigned)nt * 5u) % (unsigned)nk) : 0;
+  // With one row tile (skinny M: the projections of skip steps) and at least 64 weight
+  // tiles, the K loop of weight tile nt starts at step rot and wraps: tiles running at the
+  // same time then read different K columns, which spreads their weight rows (K x 2 bytes
+  // apart) over the L2 channels instead of one (up to 18 % faster at 17 .. 256 rows).
+  // With several row tiles the tiles of a group walk K together to share A in L2, and
+  // with few weight tiles the K splits already spread the reads, so there is no rotation;
+  // nor for the LM head with the entropy epilogue (988 weight tiles), which it made 10 %
+  // slower. The order depends only on the weight tile and the plan.
+  const int rot = (EPI != EPI_ENTROPY && MT == 1 && ntk / splits >= 64)
+                      ? (int)(((unsigned)nt * 5u) % (unsigned)nk) : 0;
 
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
