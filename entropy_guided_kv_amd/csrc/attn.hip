@@ -517,6 +517,9 @@ ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, 
     return EC_OK;
   }
   EC_REQUIRE(Dh == D, EC_ERR_UNSUPPORTED, "attn: bf16 path needs head_dim 128 (got %d)", Dh);
+  // q and the caches are addressed through buffer resources with 32-bit byte offsets
+  EC_REQUIRE((int64_t)(L > r ? L : r) * H * Dh * 2 <= 0x7fffffff, EC_ERR_UNSUPPORTED,
+             "attn: %d rows of %d x %d bf16 exceed the 2 GiB buffer range", L > r ? L : r, H, Dh);
   AttnPlan p = plan_attn(r, L, H);
   const float sl = scale * kLog2e;
   dim3 grid(p.qtiles, H, p.splits);

@@ -116,9 +116,24 @@ ec_status check_model(const ec_model_desc* m) {
                EC_ERR_UNSUPPORTED, "bf16 model: need d %% 256, F %% 128, V %% 128 == 0");
     EC_REQUIRE(m->d_model % 64 == 0 && m->ffn_dim % 64 == 0, EC_ERR_UNSUPPORTED,
                "bf16 model: d and F must be multiples of 64");
+    // the bf16 kernels address every weight matrix through 32-bit byte offsets
+    const int64_t widest = std::max<int64_t>({3 * (int64_t)m->d_model, 2 * (int64_t)m->ffn_dim, m->vocab});
+    EC_REQUIRE(widest * m->d_model * 2 <= 0x7fffffff, EC_ERR_UNSUPPORTED,
+               "bf16 model: a %lld x %d weight matrix exceeds the 2 GiB buffer range", (long long)widest,
+               m->d_model);
   } else {
     EC_REQUIRE(m->d_model % 4 == 0, EC_ERR_UNSUPPORTED, "f32 model: d_model %% 4 != 0");
   }
+  return EC_OK;
+}
+
+// bf16 forwards over up to `rows` rows: activations [rows, max(d, F)] and the K / V caches
+// [rows, d] are addressed through 32-bit byte offsets
+ec_status check_rows_fit(const ec_model_desc* m, int64_t rows) {
+  if (m->dtype != EC_BF16) return EC_OK;
+  EC_REQUIRE(rows * std::max(m->d_model, m->ffn_dim) * 2 <= 0x7fffffff, EC_ERR_UNSUPPORTED,
+             "bf16 model: %lld rows of width %d exceed the 2 GiB buffer range", (long long)rows,
+             std::max(m->d_model, m->ffn_dim));
   return EC_OK;
 }
 
@@ -487,6 +502,7 @@ ec_status check_params(const ec_params* p, const ec_model_desc* m, const ec_cach
              "params: candidates must be EC_CAND_BLOCKS or EC_CAND_WINDOW");
   if (m) EC_REQUIRE(p->mask_id >= 0 && p->mask_id < m->vocab, EC_ERR_ARG, "params: mask_id out of range");
   if (c) EC_REQUIRE(c->seq_len == p->seq_len, EC_ERR_ARG, "params: seq_len differs from cache");
+  if (m) return check_rows_fit(m, p->seq_len);
   return EC_OK;
 }
 
@@ -693,6 +709,8 @@ ec_status ec_forward(const ec_model_desc* model, const ec_cache_desc* cache, con
   if (st != EC_OK) return st;
   EC_REQUIRE(n_rows >= 0 && n_rows <= cache->seq_len && n_out >= 0 && n_out <= std::max(n_rows, 0),
              EC_ERR_ARG, "ec_forward: n_rows %d n_out %d", n_rows, n_out);
+  st = check_rows_fit(model, cache->seq_len);
+  if (st != EC_OK) return st;
   EC_REQUIRE(tokens && (rows || n_rows == 0) && (out_idx || n_out == 0) && (logits || n_out == 0),
              EC_ERR_ARG, "ec_forward: null pointer");
   const size_t need = carve_fwd(model, std::max(n_rows, 1), n_out, cache->seq_len, nullptr, 0, nullptr);
@@ -768,6 +786,8 @@ ec_status ec_step_batch(const ec_model_desc* model, int32_t n_seq, const ec_cach
              n_seq, EC_MAX_SEQ);
   EC_REQUIRE(caches && states && outs, EC_ERR_ARG, "ec_step_batch: null caches, states or outs");
   st = check_params(params, model, &caches[0]);
+  if (st != EC_OK) return st;
+  st = check_rows_fit(model, (int64_t)n_seq * params->seq_len);
   if (st != EC_OK) return st;
   for (int q = 0; q < n_seq; ++q) {
     st = check_cache(&caches[q], model);

@@ -759,6 +759,9 @@ int gemm_col_tiles(int M, int N, int K, int kind) {
 size_t gemm_splitk_ws_bytes(int M, int N, int K, int kind, bool is_bf16) {
   if (!is_bf16 || M <= 0) return 0;
   const int NB = b_rows(N, kind);
+  // the kernel addresses A and B through buffer resources with 32-bit byte offsets
+  EC_REQUIRE((int64_t)M * K * 2 <= 0x7fffffff && (int64_t)NB * K * 2 <= 0x7fffffff, EC_ERR_UNSUPPORTED,
+             "gemm: operands of %d x %d and %d x %d bf16 exceed the 2 GiB buffer range", M, K, NB, K);
   Plan p = plan_bf16(M, NB, K, kind);
   if (p.S <= 1) return 0;
   return (size_t)p.S * M * NB * sizeof(float);
@@ -787,6 +790,9 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
   if (kind == EPI_SWIGLU)
     EC_REQUIRE(N % 16 == 0, EC_ERR_UNSUPPORTED, "gemm: packed SwiGLU needs F %% 16 == 0");
   const int NB = b_rows(N, kind);
+  // the kernel addresses A and B through buffer resources with 32-bit byte offsets
+  EC_REQUIRE((int64_t)M * K * 2 <= 0x7fffffff && (int64_t)NB * K * 2 <= 0x7fffffff, EC_ERR_UNSUPPORTED,
+             "gemm: operands of %d x %d and %d x %d bf16 exceed the 2 GiB buffer range", M, K, NB, K);
   Plan p = plan_bf16(M, NB, K, kind);
   EpiArgs e = epi;
   if (kind == EPI_ENTROPY) {

@@ -113,7 +113,9 @@ ec_status ec_cache_scatter(void* k_cache, void* v_cache, int64_t seq_len, int32_
  * q, out: [r, n_heads * head_dim]; k_cache, v_cache: [seq_len, n_heads *
  * head_dim]; all of dtype; scale > 0. bf16 runs on MFMA with fp32 softmax; the
  * probabilities enter the P.V product rounded to bf16.
- * Supported: head_dim == 128 for bf16, head_dim <= 256 for f32.
+ * Supported: head_dim == 128 for bf16, with max(r, seq_len) * n_heads * 256
+ * bytes below 2 GiB (32-bit buffer offsets); head_dim <= 256 for f32.
+ * EC_ERR_UNSUPPORTED otherwise.
  * workspace: >= ec_partial_attn_workspace_size(...) bytes (may be 0 -> NULL ok).
  * ---------------------------------------------------------------------- */
 size_t ec_partial_attn_workspace_size(int32_t r, int32_t seq_len, int32_t n_heads,
@@ -157,7 +159,12 @@ typedef struct ec_layer_weights {
 } ec_layer_weights;
 
 /* Every device array of the model and of the cache must be 16-byte aligned (hipMalloc
- * returns 256-byte aligned memory); ec_forward / ec_step return EC_ERR_ARG otherwise. */
+ * returns 256-byte aligned memory); ec_forward / ec_step return EC_ERR_ARG otherwise.
+ * bf16 models run on kernels that address weights, activations and caches through
+ * 32-bit byte offsets, and need: head_dim 128; d a multiple of 256; F and V multiples
+ * of 128; every weight matrix (V x d, 3d x d, 2F x d) below 2 GiB; seq_len * max(d, F)
+ * * 2 bytes below 2 GiB (n_seq times that for ec_step_batch). The calls and their
+ * workspace queries return EC_ERR_UNSUPPORTED (size 0) otherwise, before any work. */
 typedef struct ec_model_desc {
   uint32_t struct_size;
   ec_dtype dtype;

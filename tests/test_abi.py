@@ -111,6 +111,28 @@ def test_unsupported_shapes_and_bad_params_are_rejected(lib):
     assert b"layer 3" in lib.ec_last_error()
 
 
+def test_shapes_beyond_the_32bit_buffer_range_are_rejected(lib):
+    """The bf16 kernels address weights, activations and caches with 32-bit byte offsets:
+    a matrix over 2 GiB is refused up front instead of wrapping."""
+    ok, _k0 = _model_desc()
+    assert lib.ec_step_workspace_size(C.byref(ok), C.byref(_params())) > 0
+    # LM head of 262144 x 4096 bf16 = 2 GiB: one byte past the range
+    big_v, _k1 = _model_desc(V=262144)
+    assert lib.ec_step_workspace_size(C.byref(big_v), C.byref(_params(mask=0))) == 0
+    assert b"2 GiB" in lib.ec_last_error()
+    # just inside: 262016 x 4096 x 2 bytes < 2^31
+    fits_v, _k2 = _model_desc(V=262016)
+    assert lib.ec_step_workspace_size(C.byref(fits_v), C.byref(_params(mask=0))) > 0
+    # activations [L, F]: 65536 rows of F = 16384 bf16 = 2 GiB
+    wide, _k3 = _model_desc(F=16384)
+    wide.rope_max_pos = 1 << 17
+    assert lib.ec_step_workspace_size(C.byref(wide), C.byref(_params(L=65536, P=65536 - 256))) == 0
+    assert b"rows" in lib.ec_last_error()
+    # fp32 models take the 64-bit-indexed kernels: no such limit
+    f32, _k4 = _model_desc(dtype=_lib.EC_F32, V=262144)
+    assert lib.ec_step_workspace_size(C.byref(f32), C.byref(_params(mask=0))) > 0
+
+
 def test_argument_errors_return_before_any_gpu_work(lib):
     E = _lib
     # bad dtype / sizes: rejected by the host checks, nothing is launched
