@@ -90,10 +90,11 @@ def test_pack_weights_layout(d, D, F, dtype):
     got_q = qp.float().cpu().numpy()
     got_gu = gu.float().cpu().numpy()
     np.testing.assert_array_equal(got_q, host(wqkv)[_packed_qkv_order(d, D)])
+    hg, hu = host(wg), host(wu)
     exp_gu = np.empty((2 * F, d), np.float32)
     for g in range(F // 16):
-        exp_gu[32 * g: 32 * g + 16] = host(wg)[16 * g: 16 * g + 16]
-        exp_gu[32 * g + 16: 32 * g + 32] = host(wu)[16 * g: 16 * g + 16]
+        exp_gu[32 * g: 32 * g + 16] = hg[16 * g: 16 * g + 16]
+        exp_gu[32 * g + 16: 32 * g + 32] = hu[16 * g: 16 * g + 16]
     np.testing.assert_array_equal(got_gu, exp_gu)
     # a permutation: every plain row appears exactly once
     assert sorted(_packed_qkv_order(d, D).tolist()) == list(range(3 * d))
