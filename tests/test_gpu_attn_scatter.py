@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("L,width,n", [(1024, 4096, 143), (512, 2048, 1), (128, 256, 128), (97, 24, 13)])
+@pytest.mark.parametrize("L,width,n", [(1024, 4096, 143), (512, 2048, 1), (128, 256, 128), (97, 24, 13),
+                                     (64, 128, 0)])
 def test_cache_scatter_bit_exact(dtype, L, width, n):
     import entropy_guided_kv_amd as ek
     g = torch.Generator().manual_seed(L + n)

@@ -111,6 +111,30 @@ def test_tiny_multi_token_steps_and_ring_cut():
     _compare_run(cfg, synth.make_model(cfg.model), math.inf)
 
 
+@pytest.mark.parametrize("name,P,M,n,B,k", [("no_recent", 96, 32, 1, 8, 0), ("no_prompt", 0, 32, 2, 8, 3)])
+def test_tiny_degenerate_budgets(name, P, M, n, B, k):
+    """k = 0: R is the still-masked positions alone and the decode-time ring stays empty;
+    P = 0: every position starts masked. Skip steps after the first exercise both.
+
+    With P = 0 the first step is an exact tie: every row holds the mask token, so every V
+    row is the same and every row's attention output is that row whatever the weights;
+    all candidates then share one entropy, confidence and argmax, and rounding decides
+    which n of them are picked. That step is checked on what is unique (path, set sizes,
+    E, the shared id, n distinct candidates), and the trajectories may part after it."""
+    cfg = synth.DecodeConfig(name, synth.TINY, P, M, n, B, k, (math.inf,))
+    outs, recs = _compare_run(cfg, synth.make_model(cfg.model), math.inf, expect_full_compare=P > 0)
+    if k == 0:
+        assert [o.rows for o in outs[1:]] == [M - n * t for t in range(1, len(outs))]
+    if P == 0:
+        o, r = outs[0], recs[0]
+        # equal up to the oracle's own float64 rounding
+        assert np.ptp(r.entropy) < 1e-9 and np.ptp(np.log(r.maxprob)) < 1e-9 and len(set(r.argmax)) == 1
+        assert o.refreshed and o.rows == len(r.rows) and o.n_cand == len(r.cand)
+        assert len(set(o.positions)) == n and set(o.positions) <= set(int(c) for c in r.cand)
+        assert o.ids == [int(r.argmax[0])] * n
+        assert abs(o.emax - r.emax) <= 1e-3
+
+
 def test_tau_minus_inf_equals_vanilla_on_gpu():
     """tau = -inf refreshes every step; it must match a run that forces a refresh each step."""
     from entropy_guided_kv_amd import api
