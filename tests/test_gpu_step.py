@@ -111,10 +111,12 @@ def test_tiny_multi_token_steps_and_ring_cut():
     _compare_run(cfg, synth.make_model(cfg.model), math.inf)
 
 
-@pytest.mark.parametrize("name,P,M,n,B,k", [("no_recent", 96, 32, 1, 8, 0), ("no_prompt", 0, 32, 2, 8, 3)])
+@pytest.mark.parametrize("name,P,M,n,B,k", [("no_recent", 96, 32, 1, 8, 0), ("no_prompt", 0, 32, 2, 8, 3),
+                                            ("ragged_last_block", 90, 30, 2, 8, 4)])
 def test_tiny_degenerate_budgets(name, P, M, n, B, k):
     """k = 0: R is the still-masked positions alone and the decode-time ring stays empty;
-    P = 0: every position starts masked. Skip steps after the first exercise both.
+    P = 0: every position starts masked; M = 30 with B = 8: the last block holds 6 positions.
+    Skip steps after the first exercise all three.
 
     With P = 0 the first step is an exact tie: every row holds the mask token, so every V
     row is the same and every row's attention output is that row whatever the weights;
