@@ -240,10 +240,13 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
       f32x16 st;
 #pragma unroll
       for (int v = 0; v < 16; ++v) st[v] = 0.f;
-      // all K fragments first, so that the MFMA chain waits for LDS once
+      // all K fragments first, so that the MFMA chain waits for LDS once; the fence keeps
+      // the scheduler from folding the eight reads into one register set read just in time
+      // (one LDS round trip per MFMA)
       bf16x8 fk[D / 16];
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) fk[kk] = *reinterpret_cast<const bf16x8*>(kst + koff[kk]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[kk], fq[kk], st, 0, 0, 0);
       // key of st[v]: kv0 + sub*32 + 8(v/4) + 4g + v%4; mask keys past the end of the range
@@ -523,14 +526,10 @@ ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, 
   AttnPlan p = plan_attn(r, L, H);
   const float sl = scale * kLog2e;
   dim3 grid(p.qtiles, H, p.splits);
-  static bool attr = false;
-  if (!attr) {
-    EC_CHECK_HIP(hipFuncSetAttribute((const void*)attn_bf16_kernel<false>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds));
-    EC_CHECK_HIP(hipFuncSetAttribute((const void*)attn_bf16_kernel<true>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds));
-    attr = true;
-  }
+  static LdsLimit whole, split;
+  ec_status st = p.splits == 1 ? whole.ensure((const void*)attn_bf16_kernel<false>, kAttnLds)
+                               : split.ensure((const void*)attn_bf16_kernel<true>, kAttnLds);
+  if (st != EC_OK) return st;
   if (p.splits == 1) {
     attn_bf16_kernel<false><<<grid, kAttnThreads, kAttnLds, s>>>((const bf16*)q, (const bf16*)k,
                                                              (const bf16*)v, r, L, H, sl, p.chunk,
