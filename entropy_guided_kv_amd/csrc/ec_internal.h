@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <atomic>
+
 #include "ec.h"
 
 namespace ec {
@@ -63,6 +65,21 @@ ec_status hip_fail(hipError_t e, const char* what);
   do {                                                       \
     if (!(cond)) { ::ec::set_error(__VA_ARGS__); return code; } \
   } while (0)
+
+// Raises a kernel's dynamic LDS limit once per device (the attribute belongs to the
+// device the call is made on); safe with several host threads launching at once.
+struct LdsLimit {
+  std::atomic<uint64_t> done{0};  // bit d: set on device d (devices >= 64 set it on every call)
+  ec_status ensure(const void* kern, int bytes) {
+    int dev = 0;
+    EC_CHECK_HIP(hipGetDevice(&dev));
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return EC_OK;
+    EC_CHECK_HIP(hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+    done.fetch_or(bit, std::memory_order_release);
+    return EC_OK;
+  }
+};
 
 // ---------------------------------------------------------------- workspace carving
 struct Carver {

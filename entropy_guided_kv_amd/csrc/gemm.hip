@@ -715,11 +715,9 @@ ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, int M, int N,
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int grid = p.MT * p.NT * p.S;
   auto run = [&](auto kern) -> ec_status {
-    static bool attr = false;
-    if (!attr) {
-      EC_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-      attr = true;
-    }
+    static LdsLimit limit;
+    const ec_status st = limit.ensure((const void*)kern, (int)lds);
+    if (st != EC_OK) return st;
     kern<<<grid, NT, lds, s>>>(A, B, M, N, K, p.k_chunk, p.S, epi, part);
     EC_CHECK_LAUNCH("gemm_bf16_kernel");
     return EC_OK;
