@@ -194,7 +194,11 @@ select_kernel(const float* __restrict__ H, const int32_t* __restrict__ amax,
     const int id = amax[i];
     tokens[p] = id;
     masked[p] = 0;
-    if (k > 0) plan[8 + (count0 + slot) % lay.K] = p;
+    // The step's positions enter the decode record in ascending order (slots 0 ..
+    // npick-1 after the count0 earlier entries). Only the last k of them can be among
+    // the k most recent entries, so only those write the ring: they are at most k
+    // consecutive record indices, hence distinct ring slots (one writer per slot).
+    if (k > 0 && slot >= npick - k) plan[8 + (count0 + slot) % lay.K] = p;
     res->pos[slot] = p;
     res->ids[slot] = id;
     res->ent[slot] = H[i];

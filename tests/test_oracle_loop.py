@@ -183,3 +183,43 @@ def test_select_ranks_nan_confidence_last():
     conf = np.array([np.nan, 0.2, 0.1], dtype=np.float32)
     np.testing.assert_array_equal(ol.select(cand, conf, 1), [5])
     np.testing.assert_array_equal(ol.select(cand, conf, 3), [3, 5, 9])
+
+
+def _device_ring(steps, k):
+    """The decode-time ring as the device keeps it (O(k) memory): record index c lives in
+    slot c mod k; a step appends its positions in ascending order at indices count0 ..
+    count0 + n - 1, and only the indices >= count0 + n - k write their slot (one writer per
+    slot). Returns (ring, count)."""
+    ring, count = [-1] * k, 0
+    for picked in steps:
+        n = len(picked)
+        for slot, p in enumerate(sorted(picked)):
+            if slot >= n - k:
+                ring[(count + slot) % k] = p
+        count += n
+    return ring, count
+
+
+@pytest.mark.parametrize("n,k", [(4, 2), (3, 1), (5, 5), (7, 3), (1, 4), (2, 4), (64, 16)])
+def test_decode_ring_slot_rule_keeps_the_last_k_entries(n, k):
+    """With more positions decoded in a step than the recent budget (n > k) a step's own
+    positions overflow the ring; the slot rule must still leave exactly the last k entries of
+    the decode log (the higher positions of the last step), and the recompute set built from
+    the ring must equal the oracle's (masked positions + decode_log[-k:])."""
+    rng = np.random.default_rng(n * 100 + k)
+    L = 400
+    order = rng.permutation(L)
+    masked = np.ones(L, dtype=bool)
+    log, steps, i = [], [], 0
+    while i < L:
+        m = int(rng.integers(1, n + 1))  # steps of 1 .. n positions (a block's ragged end)
+        picked = sorted(int(p) for p in order[i:i + m])
+        i += m
+        steps.append(picked)
+        log += picked
+        masked[picked] = False
+        ring, count = _device_ring(steps, k)
+        held = set(ring[:min(count, k)])
+        assert held == set(log[-k:])
+        R = sorted(set(np.flatnonzero(masked).tolist()) | held)
+        np.testing.assert_array_equal(R, ol.recompute_set(masked, log, k))
