@@ -20,7 +20,11 @@
 // element j of each of four source lanes' 8-byte rows), two per fragment.
 // Softmax statistics are per lane (one query), completed with one
 // cross-half exchange; the reference max is only moved (and O, l rescaled)
-// when a row max exceeds it by 2^8, so most tiles skip the rescale. All global
+// when a row max exceeds it by 2^8, so most tiles skip the rescale. The
+// reference is an integer in base-2 units, so the probabilities that enter the
+// P.V product in bf16 are the weights 2^(t - M), t = score * log2(e) / sqrt(D),
+// rounded to bf16 for an integer M: the same rounded values for any tiling (the
+// row sum l takes the unrounded weights). All global
 // loads go straight into LDS (buffer_load_dwordx4 ... lds, no staging registers):
 // the 128-query Q tile once, issued with the first K/V tiles and then read into
 // registers for the whole loop, and the K and V tiles of 64 keys through a ring
@@ -263,9 +267,13 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
         half_pair(tmax, a, b);
         tmax = fmaxf(a, b) * scale_log2;
       }
-      // lazy rescale: only when some row's max moved past the reference by 2^kRescale
+      // lazy rescale: only when some row's max moved past the reference by 2^kRescale.
+      // The reference is kept an integer (base-2 units), so every probability rounded to
+      // bf16 below is 2^(t - M) for an integer M: bf16 rounding commutes with scaling by
+      // powers of two, so the rounded weights equal those taken against the row's final
+      // (integer) maximum, whatever the tiling, the split or the order of rescales.
       if (__any(tmax > m_ref + kRescale)) {
-        const float m_new = fmaxf(m_ref, tmax);
+        const float m_new = ceilf(fmaxf(m_ref, tmax));
         const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
         l_run *= alpha;
 #pragma unroll

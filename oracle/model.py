@@ -21,9 +21,10 @@ head give the logits of position i at row i. Projection matrices are stored
 
 Precision: all arithmetic in float64. For bf16 models, values are rounded to
 bf16 (round to nearest, ties to even) at the points where the device path
-stores bf16: the normed GEMM inputs, q/k/v after RoPE (the cache), the
-attention output, the SwiGLU product and the logits. The residual stream is
-kept unrounded (the device keeps it in fp32).
+holds bf16: the normed GEMM inputs, q/k/v after RoPE (the cache), the
+attention weights that multiply V (as 2^(t - M) for an integer M, see
+attention()), the attention output, the SwiGLU product and the logits. The
+residual stream is kept unrounded (the device keeps it in fp32).
 """
 from __future__ import annotations
 
@@ -89,24 +90,41 @@ def rope(u: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return np.concatenate([lo * c - hi * s, lo * s + hi * c], axis=-1)
 
 
+LOG2E = 1.0 / math.log(2.0)
+
+
 def softmax(s: np.ndarray) -> np.ndarray:
     m = s.max(axis=-1, keepdims=True)
     e = np.exp(s - m)
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, round_weights=None) -> np.ndarray:
     """Bidirectional attention of query rows over every cached row.
 
     q: [r, H, D]; K, V: [L, H, D]. For each head, softmax(q K^T / sqrt(D)) V
     over all L keys, no mask.
+
+    With ``round_weights`` (bf16 models: the P.V product takes its weights in
+    bf16), the weights of each query row are written in base 2 as
+    w_j = 2^(t_j - M), t_j = s_j log2(e), with M the smallest integer >= max_j t_j;
+    the weights that multiply V are round_weights(w_j) and the normaliser is the
+    unrounded sum: out = sum_j round(w_j) v_j / sum_j w_j. Without rounding this is
+    softmax(s) V exactly. Rounding to bf16 commutes with scaling by powers of two,
+    so any integer M >= max t gives the same result.
     """
     r, H, D = q.shape
     out = np.empty_like(q)
     scale = 1.0 / math.sqrt(D)
     for h in range(H):
-        p = softmax((q[:, h, :] @ K[:, h, :].T) * scale)
-        out[:, h, :] = p @ V[:, h, :]
+        s = (q[:, h, :] @ K[:, h, :].T) * scale
+        if round_weights is None:
+            out[:, h, :] = softmax(s) @ V[:, h, :]
+        else:
+            t = s * LOG2E
+            M = np.ceil(t.max(axis=-1, keepdims=True))
+            w = np.exp2(t - M)
+            out[:, h, :] = (round_weights(w) @ V[:, h, :]) / w.sum(axis=-1, keepdims=True)
     return out
 
 
@@ -195,7 +213,8 @@ def forward(model: OracleModel, tokens: np.ndarray, rows: Sequence[int], cache,
         v = rnd(qkv[:, 2 * d:])
         K[rows] = k.reshape(r, d)
         V[rows] = v
-        o = rnd(attention(q, K.reshape(-1, H, D), V.reshape(-1, H, D)).reshape(r, d))
+        o = rnd(attention(q, K.reshape(-1, H, D), V.reshape(-1, H, D),
+                          round_weights=rnd if model.mirror else None).reshape(r, d))
         h = h + o @ lw["wo"].T
         b = rnd(rmsnorm(h, lw["mlp_norm"], m.rms_eps))
         s = rnd(silu(b @ lw["w_gate"].T) * (b @ lw["w_up"].T))

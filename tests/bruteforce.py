@@ -61,11 +61,15 @@ def forward(weights, tokens, rows, cache, n_heads, eps=1e-5, base=10000.0, rnd=l
                 sl = slice(hh * D, (hh + 1) * D)
                 qv = qs[j][sl]
                 scores = [sum(a * b for a, b in zip(qv, K[t][sl])) / math.sqrt(D) for t in range(L)]
-                mx = max(scores)
-                w = [math.exp(s - mx) for s in scores]
+                # weights against the power of two 2^M just above the largest one (M integer):
+                # w_t = e^(s_t) / 2^M; the ones that multiply V pass through rnd, the
+                # normaliser is their unrounded sum
+                M = math.ceil(max(scores) / math.log(2.0))
+                w = [math.exp(s - M * math.log(2.0)) for s in scores]
                 tot = sum(w)
+                wr = [rnd(x) for x in w]
                 for e in range(D):
-                    o[hh * D + e] = sum(w[t] / tot * V[t][hh * D + e] for t in range(L))
+                    o[hh * D + e] = sum(wr[t] * V[t][hh * D + e] for t in range(L)) / tot
             o = [rnd(x) for x in o]
             h[j] = [h[j][i] + y for i, y in enumerate(_matvec(lw["wo"], o))]
             b = [rnd(v) for v in _rms(h[j], lw["mlp_norm"], eps)]

@@ -84,6 +84,42 @@ def test_attention_matches_torch_sdpa():
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
 
 
+def _rounded_weight_attention_loops(q, K, V, rnd, extra):
+    """Scalar restatement: weights e^s / 2^M' against M' = (smallest integer >= max s log2 e)
+    + extra, rounded by rnd where they multiply V, normalised by the unrounded sum."""
+    r, H, D = q.shape
+    out = np.zeros_like(q)
+    for i in range(r):
+        for h in range(H):
+            s = [float(np.dot(q[i, h], K[j, h])) / math.sqrt(D) for j in range(K.shape[0])]
+            M = math.ceil(max(s) / math.log(2.0)) + extra
+            w = [math.exp(x - M * math.log(2.0)) for x in s]
+            for e in range(D):
+                out[i, h, e] = sum(rnd(w[j]) * V[j, h, e] for j in range(len(w))) / sum(w)
+    return out
+
+
+def test_attention_rounded_weights_independent_of_reference_and_bounded():
+    """bf16 attention weights (reading: rounded as 2^(t - M), M integer): the result must not
+    depend on which integer M is taken (the device moves its reference by integers, per tile),
+    must lie within 2^-8 max|v| of the exact softmax (bf16 unit roundoff 2^-8 on each weight),
+    must equal a scalar-loop restatement, and without rounding must equal softmax exactly."""
+    rng = np.random.default_rng(11)
+    q = om.round_bf16(rng.standard_normal((5, 2, 8)) * 2.0)
+    K = om.round_bf16(rng.standard_normal((23, 2, 8)) * 2.0)
+    V = om.round_bf16(rng.standard_normal((23, 2, 8)))
+    got = om.attention(q, K, V, round_weights=om.round_bf16)
+    rnd1 = lambda x: float(om.round_bf16(np.array(x)))
+    for extra in (0, 3, 40):
+        np.testing.assert_allclose(got, _rounded_weight_attention_loops(q, K, V, rnd1, extra),
+                                   rtol=1e-13, atol=1e-15)
+    exact = om.attention(q, K, V)
+    for h in range(2):
+        assert np.abs(got[:, h] - exact[:, h]).max() <= 2.0 ** -8 * np.abs(V[:, h]).max()
+    assert np.abs(got - exact).max() > 0  # the rounding is really applied
+    np.testing.assert_allclose(om.attention(q, K, V, round_weights=lambda w: w), exact, rtol=1e-13, atol=1e-15)
+
+
 def test_silu_matches_torch():
     x = np.linspace(-30, 30, 1001)
     np.testing.assert_allclose(om.silu(x), torch.nn.functional.silu(torch.from_numpy(x)).numpy(),
