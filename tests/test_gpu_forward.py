@@ -2,10 +2,11 @@
 
 A refresh step is the forward over every position; a skip step recomputes only
 the listed rows against the cached (stale) K/V of the others (EntropyCache
-explainer, Arabic technical summary section 2, phase 1). Bars: fp32 models
-1e-5 relative (per row) for hidden states, cached K/V and logits; bf16 models
-2e-2 relative, with argmax ids bit-exact wherever the top-1/top-2 logit
-margin exceeds 1e-2.
+explainer, Arabic technical summary section 2, phase 1). Bars, per row: fp32
+models 1e-5 relative for hidden states, the recomputed K/V rows and logits;
+bf16 models 2e-2 relative; cache rows outside the recomputed set bit-identical;
+argmax ids bit-exact wherever the top-1/top-2 logit margin clears the id gate
+(1e-2, and two bf16 steps of |top-1| for bf16 models).
 """
 import numpy as np
 import pytest
@@ -47,8 +48,17 @@ def _setup(shape, L, seed=0, n_layers=None, stale=True):
 
 
 def _compare(shape, om_model, dm, cache, ocache, tokens, rows, out_pos, check_ids=True):
+    """ec_forward over ``rows`` against the oracle's forward on the same (stale) cache.
+
+    Per row: hidden states and logits of the listed rows, and the K / V rows the call wrote
+    (the recomputed positions only, so stale rows with zero error do not dilute the bar);
+    every cache row outside ``rows`` must be bit-identical to what it held before the call.
+    Argmax ids must match where the oracle's margin clears the id gate."""
     from entropy_guided_kv_amd import api
     L = len(tokens)
+    rows = np.asarray(rows)
+    outside = torch.from_numpy(np.setdiff1d(np.arange(L), rows)).cuda()
+    before = [(cache.k[i][outside].clone(), cache.v[i][outside].clone()) for i in range(len(ocache))]
     where = {int(p): i for i, p in enumerate(rows)}
     out_idx = np.array([where[int(p)] for p in out_pos], dtype=np.int32)
     logits, hidden = api.ec_forward(dm, cache, torch.from_numpy(tokens).cuda(),
@@ -59,17 +69,20 @@ def _compare(shape, om_model, dm, cache, ocache, tokens, rows, out_pos, check_id
     tol = _tol(shape)
     eh = row_rel_err(to_f64(hidden), ref["hidden"])
     el = row_rel_err(to_f64(logits), ref["logits"])
-    ek = max(rel_err(to_f64(cache.k[i]), ocache[i][0]) for i in range(len(ocache)))
-    ev = max(rel_err(to_f64(cache.v[i]), ocache[i][1]) for i in range(len(ocache)))
-    print(f"{shape.name}: rows={len(rows)} hidden {eh:.2e} logits {el:.2e} K {ek:.2e} V {ev:.2e}")
+    ek = max(row_rel_err(to_f64(cache.k[i])[rows], ocache[i][0][rows]) for i in range(len(ocache)))
+    ev = max(row_rel_err(to_f64(cache.v[i])[rows], ocache[i][1][rows]) for i in range(len(ocache)))
+    print(f"{shape.name}: rows={len(rows)} worst row: hidden {eh:.2e} logits {el:.2e} K {ek:.2e} V {ev:.2e}")
     assert eh <= tol and el <= tol and ek <= tol and ev <= tol
+    for i, (kb, vb) in enumerate(before):
+        assert torch.equal(cache.k[i][outside], kb) and torch.equal(cache.v[i][outside], vb), \
+            f"layer {i}: a cache row outside the recomputed set changed"
     lg = to_f64(logits)
     if not check_ids:
         return lg, ref
-    # argmax ids: identical wherever the oracle's top-1/top-2 margin clears the gate
+    # argmax ids: identical wherever the oracle's top-1/top-2 margin clears the id gate
     srt = np.sort(ref["logits"], axis=1)
     margin = srt[:, -1] - srt[:, -2]
-    gate = margin_gate(srt[:, -1], margin) if shape.dtype == "bf16" else margin > 1e-2
+    gate = margin_gate(srt[:, -1], margin, shape.dtype)
     bad = np.flatnonzero(gate & (lg.argmax(1) != ref["logits"].argmax(1)))
     for i in bad:
         print(f"row {i}: device argmax {lg[i].argmax()} oracle {ref['logits'][i].argmax()} "
@@ -129,7 +142,10 @@ def test_partial_after_full_is_idempotent_bf16():
     lg_p, h_p = api.ec_forward(dm, cache, tk, rows, torch.arange(4, dtype=torch.int32, device="cuda"),
                                want_hidden=True)
     torch.cuda.synchronize()
-    assert row_rel_err(to_f64(h_p), to_f64(h_full)[rows.long().cpu().numpy()]) < 2e-2
-    assert row_rel_err(to_f64(lg_p), to_f64(lg_full)[rows.long().cpu().numpy()]) < 2e-2
+    ri = rows.long().cpu().numpy()
+    assert row_rel_err(to_f64(h_p), to_f64(h_full)[ri]) < 2e-2
+    assert row_rel_err(to_f64(lg_p), to_f64(lg_full)[ri]) < 2e-2
+    outside = np.setdiff1d(np.arange(L), ri)
     for a, b in zip(cache.k, k0):
-        assert rel_err(to_f64(a), to_f64(b)) < 2e-2
+        assert row_rel_err(to_f64(a)[ri], to_f64(b)[ri]) < 2e-2
+        assert torch.equal(a[outside], b[outside])

@@ -4,15 +4,15 @@ Per step (EntropyCache explainer, Arabic technical summary section 2): the
 path taken (refresh or skip), the recompute-set size, the decoded positions
 and ids, E_{t+1} and the next step's flag. Decoded ids and positions must be
 identical wherever the oracle's top-1/top-2 logit margin of the decoded rows
-exceeds 1e-2 (of max(1, |top-1|) for bf16 models, whose logits are stored
-with a step of 1/64 at |logit| >= 2) and the confidence gap at the selection
-cut exceeds 1e-2 in log space (for bf16 models, of max(1, |top-1|) of the two
-rows at the cut: a rounding flip of a stored top-1 logit shifts that row's
-log-confidence by one bf16 step of the logit); the first step that fails that gate ends the
-comparison (the two trajectories may legitimately part there). E within 1e-3
-nats for fp32 models; for bf16 models E is checked against the oracle's
-entropy of the device's own logits (within 1e-3) by the forward tests, and
-end to end within 2e-2.
+exceeds the id gate (1e-2 for fp32 models, max(1e-2, 2 bf16 ulps of |top-1|)
+for bf16 models, whose logits are stored in bf16) and the confidence gap at the
+selection cut (log space) exceeds the cut gate (1e-2 for fp32 models; for bf16
+the most two rows' log-confidences can move when every stored logit moves by
+one bf16 step, tests/gpu_util.py); the first step that
+fails that gate ends the comparison (the two trajectories may legitimately
+part there). E within 1e-3 nats for fp32 models; for bf16 models E is checked
+against the oracle's entropy of the device's own logits (within 1e-3) by the
+forward tests, and end to end within 2e-2.
 """
 import math
 
@@ -23,7 +23,7 @@ import torch
 import synth
 from oracle import loop as ol
 from oracle import model as om
-from tests.gpu_util import margin_gate
+from tests.gpu_util import cut_gate_threshold, margin_gate
 
 pytestmark = pytest.mark.gpu
 
@@ -38,19 +38,19 @@ def _decoder(dm, cfg, tau):
 
 
 def _gate_ok(rec, n, dtype):
+    """True when the oracle's step is decided by more than the gates: every decoded row's
+    top-1/top-2 margin clears id_gate_threshold and the confidence gap at the selection cut
+    (log space) clears cut_gate_threshold."""
     where = {int(p): i for i, p in enumerate(rec.cand)}
     idx = [where[int(p)] for p in rec.picked]
-    ok = margin_gate(rec.top1, rec.margin) if dtype == "bf16" else rec.margin > 1e-2
+    ok = margin_gate(rec.top1, rec.margin, dtype)
     if not all(ok[i] for i in idx):
         return False
     order = np.argsort(-np.log(rec.maxprob), kind="stable")
     if len(order) > n:
         a, b = order[n - 1], order[n]
         gap = abs(np.log(rec.maxprob[a]) - np.log(rec.maxprob[b]))
-        # a bf16 rounding flip of a row's top-1 logit moves its log-confidence by one
-        # bf16 step of that logit, so for bf16 the cut scales like the margin gate
-        scale = max(1.0, abs(float(rec.top1[a])), abs(float(rec.top1[b]))) if dtype == "bf16" else 1.0
-        if gap <= 1e-2 * scale:
+        if gap <= cut_gate_threshold(rec.maxprob[a], rec.top1[a], rec.maxprob[b], rec.top1[b], dtype):
             return False
     return True
 
@@ -109,6 +109,28 @@ def test_tiny_tau_plus_inf_all_skips():
 def test_tiny_multi_token_steps_and_ring_cut():
     cfg = synth.DecodeConfig("t3", synth.TINY, 96, 32, 3, 8, 5, (math.inf,))
     _compare_run(cfg, synth.make_model(cfg.model), math.inf)
+
+
+@pytest.mark.parametrize("n,k", [(4, 2), (3, 1)])
+@pytest.mark.parametrize("peaked", [False, True])
+def test_tiny_more_tokens_per_step_than_recent_budget(n, k, peaked):
+    """n > k: a step decodes more positions than the decode-time ring holds, so only the
+    step's last k positions (the highest) stay in the ring (the k most recently decoded of
+    the decode record, Arabic technical summary section 2, phase 3). At tau = +inf every
+    step after the first is a skip step; on the peaked model the path follows E (the
+    oracle's path, which mixes refresh and skip steps for n = 4). |R|, path, positions
+    and ids must equal the oracle's on every step."""
+    cfg = synth.DecodeConfig(f"t{n}{k}", synth.TINY, 96, 32, n, 8, k, (math.inf,))
+    w = synth.make_model(cfg.model, lm_head_scale=PEAKED_SCALE if peaked else 1.0)
+    tau = PEAKED_TAU if peaked else math.inf
+    outs, recs = _compare_run(cfg, w, tau)
+    assert all(o.rows == len(r.rows) for o, r in zip(outs, recs))
+    flags = [o.refreshed for o in outs]
+    print("paths", "".join("F" if f else "." for f in flags))
+    if not peaked:
+        assert flags == [True] + [False] * (len(flags) - 1)
+    elif n == 4:
+        assert any(flags[1:]) and not all(flags[1:])
 
 
 @pytest.mark.parametrize("name,P,M,n,B,k", [("no_recent", 96, 32, 1, 8, 0), ("no_prompt", 0, 32, 2, 8, 3),
