@@ -48,7 +48,7 @@ def common_flags(debug: bool = False):
         "-Wno-unused-result",
     ]
     if debug:
-        flags += ["-g", "-DEC_DEBUG=1"]
+        flags += ["-g"]
     return flags
 
 

@@ -377,7 +377,7 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
   if (fe && n_out > 0) {
     TScope t(EC_T_ENTROPY, s, 0.0, NO * (VV / 128.0) * sizeof(EntPart));
     EC_TRY(entropy_merge(fe->parts, n_out, gemm_col_tiles(n_out, V, d, EPI_ENTROPY), fe->H, fe->amax,
-                         fe->conf, nullptr, 0, nullptr, s));
+                         fe->conf, s));
   }
 #undef EC_TRY
   return EC_OK;

@@ -173,9 +173,10 @@ ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, 
 
 // ---------------------------------------------------------------- entropy
 size_t entropy_ws_bytes(int rows, int vocab);
-// merge parts[rows][splits] in order into entropy / argmax / confidence, and E over sel
+// merge parts[rows][splits] (the fused LM-head epilogue's states) in order into entropy /
+// argmax / confidence
 ec_status entropy_merge(const EntPart* parts, int rows, int splits, float* H, int32_t* amax, float* c,
-                        const int32_t* sel, int n_sel, float* emax, hipStream_t s);
+                        hipStream_t s);
 ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t stride,
                   const int32_t* sel, int n_sel, float* H, int32_t* amax, float* c, float* emax,
                   void* ws, size_t ws_bytes, hipStream_t s);

@@ -11,27 +11,24 @@
 //   m = max(ma, mb); Z = Za e^(ma-m) + Zb e^(mb-m);
 //   S = (Sa + (ma-m) Za) e^(ma-m) + (Sb + (mb-m) Zb) e^(mb-m).
 //
-// Kernel 1: each wavefront owns one slice of one row and reads it exactly once
-// from HBM with 16-byte loads, all issued up front (U vectors per lane held in
-// registers; consecutive lanes read consecutive vectors). The slice max and its
-// first index come from DPP wavefront reductions (no LDS, no barrier); then
-// every element is exponentiated once against the slice max (exp2 of
-// x log2 e - max log2 e, one FMA) and Z, S are summed the same way. No
-// per-element rescaling and no data reread. A NaN logit is skipped by the max
-// but turns Z into NaN, so the row's entropy and confidence come out NaN.
-// Kernel 2 (grid: rows, one wavefront each): merges the slices of a row in a
-// fixed order (deterministic) and writes entropy / argmax / confidence.
-// Kernel 3 (one workgroup, only when E is requested): max over selected rows.
+// ec_entropy_max runs as one launch (entropy_fused_kernel, described there): every
+// logit is read once from HBM with 16-byte loads, exponentiated once (exp2 of
+// x log2 e - m log2 e, one FMA) against its lane's running maximum, and the slice
+// states of a row merge in a fixed order, so results are reproducible. A NaN logit
+// is skipped by the maximum and carried as a flag, which makes its row's entropy and
+// confidence NaN. The fused LM-head epilogue of the GEMM produces slice states of its
+// own; entropy_merge_kernel (one wavefront per row) merges those.
 #include "ec_internal.h"
 
 #include <math.h>
+
+#include <algorithm>
+#include <atomic>
 
 namespace ec {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kU = 2;  // 16-byte vectors per lane per slice (measured best of 1, 2, 4)
 constexpr float kNegInf = -INFINITY;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -58,126 +55,6 @@ template <> struct Vec<float> {
     for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(u[k]);
   }
 };
-
-// ---- wavefront reductions with DPP (no LDS round trip). After the six steps
-// lane 63 holds the result over all 64 lanes; readlane broadcasts it.
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ int dpp(int old, int x) {
-  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROW_MASK, 0xF, false);
-}
-#define EC_WAVE_REDUCE(NAME, TYPE, OP, TO, FROM)                                 \
-  __device__ __forceinline__ TYPE NAME(TYPE v) {                                 \
-    int x = TO(v);                                                               \
-    x = TO(OP(FROM(x), FROM(dpp<0xB1>(x, x))));        /* quad_perm 1,0,3,2 */   \
-    x = TO(OP(FROM(x), FROM(dpp<0x4E>(x, x))));        /* quad_perm 2,3,0,1 */   \
-    x = TO(OP(FROM(x), FROM(dpp<0x141>(x, x))));       /* row_half_mirror */     \
-    x = TO(OP(FROM(x), FROM(dpp<0x140>(x, x))));       /* row_mirror */          \
-    x = TO(OP(FROM(x), FROM(dpp<0x142, 0xA>(x, x))));  /* row_bcast15 */         \
-    x = TO(OP(FROM(x), FROM(dpp<0x143, 0xC>(x, x))));  /* row_bcast31 */         \
-    return FROM(__builtin_amdgcn_readlane(x, 63));                               \
-  }
-__device__ __forceinline__ int f2i(float v) { return __float_as_int(v); }
-__device__ __forceinline__ float i2f(int v) { return __int_as_float(v); }
-__device__ __forceinline__ int iid(int v) { return v; }
-__device__ __forceinline__ float fadd(float a, float b) { return a + b; }
-__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
-EC_WAVE_REDUCE(wave_max_f, float, fmaxf, f2i, i2f)
-EC_WAVE_REDUCE(wave_sum_f, float, fadd, f2i, i2f)
-EC_WAVE_REDUCE(wave_min_i, int, imin, iid, iid)
-#undef EC_WAVE_REDUCE
-
-// One wavefront per slice of one row (grid: ceil(slices / 4) x rows, 256 threads).
-// Lane l reads vectors l, l+64, ... of the slice (coalesced 1 KB per step), all
-// loads issued before any use. Two register passes: the max (and its first
-// index), then one exp2 per element against that max for Z and S.
-template <typename T, bool VEC, int U>
-__global__ void __launch_bounds__(256)
-entropy_slice_kernel(const T* __restrict__ logits, int V, int64_t stride, int chunk,
-                     int slices, Part* __restrict__ parts) {
-  constexpr int E = Vec<T>::E;
-  constexpr int NV = U * E;  // values per lane
-  const int lane = threadIdx.x % 64;
-  const int slice = blockIdx.x * 4 + threadIdx.x / 64, row = blockIdx.y;
-  if (slice >= slices) return;
-  const T* base = logits + (int64_t)row * stride;
-  const int lo = slice * chunk;
-  const int hi = min(V, lo + chunk);
-
-  float x[NV];
-  int j0[U];
-#pragma unroll
-  for (int k = 0; k < U; ++k) j0[k] = lo + (lane + 64 * k) * E;
-  if (VEC) {
-    const int hiv = lo + ((hi - lo) / E) * E;  // end of the whole vectors
-    v4u u[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k)
-      if (j0[k] < hiv) u[k] = *reinterpret_cast<const v4u*>(base + j0[k]);
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      if (j0[k] < hiv) {
-        Vec<T>::unpack(u[k], x + k * E);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int j = j0[k] + e;
-          x[k * E + e] = (j >= hiv && j < hi) ? to_f(base[j]) : kNegInf;  // ragged row end
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < U; ++k)
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int j = j0[k] + e;
-        x[k * E + e] = j < hi ? to_f(base[j]) : kNegInf;
-      }
-  }
-
-  // ---- pass 1: max (NaN is skipped here; it reaches Z below and makes H NaN)
-  float lm = kNegInf;
-#pragma unroll
-  for (int q = 0; q < NV; ++q) lm = fmaxf(lm, x[q]);
-  const float mv = wave_max_f(lm);
-  // first index of the max: only lanes holding it search their values
-  int mi = 0x7fffffff;
-  if (lm == mv) {
-#pragma unroll
-    for (int k = U - 1; k >= 0; --k)
-#pragma unroll
-      for (int e = E - 1; e >= 0; --e)
-        if (x[k * E + e] == mv) mi = j0[k] + e;  // ends at this lane's first hit
-  }
-  mi = wave_min_i(mi);
-
-  // ---- pass 2: Z and S against the max, log2 domain, one exp2 per element:
-  // t = x log2e - m log2e, e = 2^t, Z += e, S2 += max(t, -1000) e. The clamp
-  // makes a -inf logit (e = 0) add -1000 * 0 = 0 instead of -inf * 0 = NaN;
-  // a NaN logit gives e = NaN, which still reaches Z and S.
-  float z = 0.f, s2 = 0.f;
-  if (mv != kNegInf) {
-    const float mb = mv * kLog2e;
-#pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      const float t = fmaf(x[q], kLog2e, -mb);
-      const float e = __builtin_amdgcn_exp2f(t);  // v_exp_f32; results below 2^-126 flush to 0
-      z += e;
-      s2 = fmaf(fmaxf(t, -1000.f), e, s2);
-    }
-  }
-  z = wave_sum_f(z);
-  s2 = wave_sum_f(s2);
-  if (lane == 0) {
-    Part p;
-    p.m = mv;
-    p.z = z;
-    p.s = s2 * kLn2;
-    p.idx = mi;
-    p.nan = 0;
-    parts[(int64_t)row * slices + slice] = p;
-  }
-}
 
 // a <- merge(a, b) of two partial states: m = max, z and s rescaled to it,
 // argmax = larger value, lower index on ties
@@ -247,45 +124,300 @@ entropy_merge_kernel(const Part* __restrict__ parts, int splits, float* __restri
   }
 }
 
-// E = max entropy over the selected rows (NaN if any selected row is NaN).
-__global__ void __launch_bounds__(kThreads)
-entropy_emax_kernel(const float* __restrict__ H, int rows, const int32_t* __restrict__ sel,
-                    int n_sel, float* __restrict__ emax) {
-  __shared__ float red[kThreads];
-  __shared__ int rnan[kThreads];
-  float m = kNegInf;
-  int nan = 0;
-  const int n = sel ? n_sel : rows;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const int r = sel ? sel[i] : i;
-    const float h = (r >= 0 && r < rows) ? H[r] : NAN;
-    if (h != h) nan = 1;
-    else m = fmaxf(m, h);
-  }
-  red[threadIdx.x] = m;
-  rnan[threadIdx.x] = nan;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) {
-      red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
-      rnan[threadIdx.x] |= rnan[threadIdx.x + w];
+// ---------------------------------------------------------------- single-launch reduction
+// ec_entropy_max in one launch. Workgroup b handles slice split = b / rows of row
+// row = b % rows (S slices per row), so the slices of every row are dispatched in
+// split order and the last slice of each row comes after every other workgroup but
+// the last slices of other rows. A workgroup reduces its slice (every element read
+// once, loads of a pass issued before their use, one exp2 per element against the
+// running maximum of its lane, lanes and wavefronts merged along a fixed order).
+// Slices 0 .. S-2 publish their partial state as four 64-bit words {call tag, value}
+// written with device-scope atomic stores; the last slice of the row (the merger)
+// polls them with device-scope atomic loads until every word carries the call's tag,
+// merges the S states in slice order and writes the row's entropy, argmax and
+// confidence. No word can be read before it is written in this call (the tag is new
+// for every call) and no fence is needed (each word carries its own tag). The merger
+// clears the tags it consumed, so a replay of the same launch with the same tag (a
+// captured graph) cannot read last replay's words. When E is requested every merger
+// publishes its row's entropy the same way and the last workgroup of the grid (the
+// merger of the last row) waits for all of them, takes the maximum over the selected
+// rows and clears those tags. Every workgroup a wait depends on was dispatched
+// before the waiting one and never waits itself; each wait is also bounded (after
+// kSpinLimit polls the row reads as NaN).
+constexpr int kFThreads = 512;
+constexpr int kFWaves = kFThreads / 64;
+constexpr int kFU = 8;                 // 16-byte vectors per lane per pass
+constexpr int kSpinLimit = 1 << 22;    // polls before a wait gives up (far beyond any normal wait)
+constexpr int kMaxSplits = 256;
+
+__device__ __forceinline__ void tag_store(uint64_t* p, uint32_t tag, uint32_t v) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// waits until each of the N words at p carries `tag` (the N loads of a poll are issued
+// together: one memory round trip per poll); false if the wait gave up
+template <int N>
+__device__ __forceinline__ bool tag_wait(uint64_t* p, uint32_t tag, uint32_t* v) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    uint64_t w[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) all = all && (uint32_t)(w[i] >> 32) == tag;
+    if (all) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[i] = (uint32_t)w[i];
+      return true;
     }
-    __syncthreads();
+    __builtin_amdgcn_s_sleep(2);
   }
-  if (threadIdx.x == 0) *emax = rnan[0] ? NAN : red[0];
+  return false;
+}
+
+__device__ __forceinline__ Part shfl_part(const Part& a, int o) {
+  Part b;
+  b.m = __shfl_xor(a.m, o);
+  b.z = __shfl_xor(a.z, o);
+  b.s = __shfl_xor(a.s, o);
+  b.idx = __shfl_xor(a.idx, o);
+  b.nan = __shfl_xor(a.nan, o);
+  return b;
+}
+
+// online update of a lane's state (m, z, s2, idx) by the values x[0..NV) at indices
+// j0[k] + e (increasing in k then e); -inf entries are empty. A NaN value is skipped by
+// the maximum and turns z into NaN through its exponential; only a pass with no finite
+// value is scanned for NaN explicitly.
+template <int NV, int E>
+__device__ __forceinline__ void lane_update(const float* x, const int* j0, float& m, float& z, float& s2, int& idx,
+                                            int& has_nan) {
+  float cm = kNegInf;
+#pragma unroll
+  for (int q = 0; q < NV; ++q) cm = fmaxf(cm, x[q]);
+  if (cm == kNegInf) {  // nothing finite here: a NaN would not reach z below, so look for one
+#pragma unroll
+    for (int q = 0; q < NV; ++q) has_nan |= x[q] != x[q];
+  }
+  if (cm > m) {  // a strictly larger maximum moves idx to its first occurrence in this pass
+#pragma unroll
+    for (int q = NV - 1; q >= 0; --q)
+      if (x[q] == cm) idx = j0[q / E] + q % E;
+    if (m != kNegInf) {  // rescale the sums to the new maximum
+      const float dl = (m - cm) * kLog2e, f = __builtin_amdgcn_exp2f(dl);
+      s2 = (s2 + dl * z) * f;
+      z *= f;
+    }
+    m = cm;
+  }
+  if (m != kNegInf) {
+    const float mb = m * kLog2e;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const float t = fmaf(x[q], kLog2e, -mb);
+      const float e = __builtin_amdgcn_exp2f(t);
+      z += e;
+      s2 = fmaf(fmaxf(t, -1000.f), e, s2);  // -inf logit: -1000 * 0 = 0
+    }
+  }
+}
+
+// partial state of elements [lo, hi) of one row over the workgroup (valid in thread 0).
+// Whole vectors [lo, hiv): every load of a pass is issued unconditionally (vectors past
+// hiv re-read the slice's first vector and are masked to -inf), so the loads of a pass
+// are in flight together; the < E elements of a ragged end [hiv, hi) follow one per
+// thread.
+template <typename T, bool VEC>
+__device__ Part slice_state(const T* __restrict__ base, int lo, int hi, Part* red) {
+  constexpr int E = Vec<T>::E;
+  constexpr int NV = kFU * E;
+  const int tid = threadIdx.x;
+  float m = kNegInf, z = 0.f, s2 = 0.f;  // s2 = sum (x - m) log2(e) e^(x - m), against this lane's m
+  int idx = 0x7fffffff, has_nan = 0;
+  const int hiv = VEC ? lo + ((hi - lo) / E) * E : hi;
+  for (int blk = lo; blk < hiv; blk += kFThreads * NV) {
+    float x[NV];
+    int j0[kFU];
+#pragma unroll
+    for (int k = 0; k < kFU; ++k) j0[k] = blk + (k * kFThreads + tid) * E;
+    if (VEC) {
+      v4u u[kFU];
+#pragma unroll
+      for (int k = 0; k < kFU; ++k) u[k] = *reinterpret_cast<const v4u*>(base + (j0[k] < hiv ? j0[k] : lo));
+#pragma unroll
+      for (int k = 0; k < kFU; ++k) {
+        Vec<T>::unpack(u[k], x + k * E);
+        if (j0[k] >= hiv) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) x[k * E + e] = kNegInf;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kFU; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int j = j0[k] + e;
+          const float v = to_f(base[j < hiv ? j : lo]);
+          x[k * E + e] = j < hiv ? v : kNegInf;
+        }
+    }
+    // two halves, so that the first half's arithmetic runs while the second half's loads
+    // are still in flight
+    lane_update<NV / 2, E>(x, j0, m, z, s2, idx, has_nan);
+    lane_update<NV / 2, E>(x + NV / 2, j0 + kFU / 2, m, z, s2, idx, has_nan);
+  }
+  if (VEC && hiv < hi && tid < hi - hiv) {  // ragged end: one element per thread
+    const int j0t[1] = {hiv + tid};
+    const float xt[1] = {to_f(base[hiv + tid])};
+    lane_update<1, 1>(xt, j0t, m, z, s2, idx, has_nan);
+  }
+  // a NaN among finite values has reached z through its exponential
+  Part p{m, z, s2 * kLn2, idx, has_nan | (z != z), {0, 0, 0}};
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {  // symmetric merge: every lane ends with the same state
+    const Part q = shfl_part(p, o);
+    part_merge(p, q);
+  }
+  if ((tid & 63) == 0) red[tid >> 6] = p;
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kFWaves; ++w) part_merge(p, red[w]);
+  }
+  return p;
+}
+
+__device__ __forceinline__ void write_row(const Part& a, int row, float* H, int32_t* amax, float* conf, float* h_out) {
+  const bool bad = a.nan || a.m == kNegInf;
+  const float h = bad ? NAN : __logf(a.z) - a.s / a.z;
+  H[row] = h;
+  conf[row] = bad ? NAN : 1.0f / a.z;
+  amax[row] = a.idx == 0x7fffffff ? 0 : a.idx;
+  *h_out = h;
+}
+
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(kFThreads)
+entropy_fused_kernel(const T* __restrict__ logits, int rows, int V, int64_t stride, int S, int chunk,
+                     const int32_t* __restrict__ sel, int n_sel, float* __restrict__ H,
+                     int32_t* __restrict__ amax, float* __restrict__ conf, float* __restrict__ emax,
+                     uint64_t* __restrict__ parts, uint64_t* __restrict__ hpub, uint32_t tag) {
+  __shared__ Part red[kFWaves];
+  __shared__ Part got[kMaxSplits];
+  __shared__ int fail_sh;
+  __shared__ float emax_sh[kFWaves];
+  __shared__ int enan_sh[kFWaves];
+  const int split = blockIdx.x / rows, row = blockIdx.x % rows, tid = threadIdx.x;
+  const int lo = min(V, split * chunk), hi = min(V, lo + chunk);
+  Part p = slice_state<T, VEC>(logits + (int64_t)row * stride, lo, hi, red);
+  uint64_t* pr = parts + (int64_t)row * S * 4;
+  if (split < S - 1) {  // publish this slice's state for the row's merger
+    if (tid == 0) {
+      uint64_t* q = pr + split * 4;
+      tag_store(q + 0, tag, __float_as_uint(p.m));
+      tag_store(q + 1, tag, __float_as_uint(p.z));
+      tag_store(q + 2, tag, __float_as_uint(p.s));
+      tag_store(q + 3, tag, (uint32_t)p.idx | (p.nan ? 0x80000000u : 0u));
+    }
+    return;
+  }
+  // ---- merger of this row: thread j < S - 1 collects slice j
+  if (tid == 0) fail_sh = 0;
+  __syncthreads();
+  if (tid < S - 1) {
+    uint64_t* q = pr + tid * 4;
+    uint32_t w[4] = {0x7fc00000u, 0u, 0u, 0x80000000u};  // read as a NaN row if the wait gives up
+    if (!tag_wait<4>(q, tag, w)) atomicOr(&fail_sh, 1);
+    got[tid] = Part{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), (int)(w[3] & 0x7fffffffu),
+                    (int)(w[3] >> 31), {0, 0, 0}};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tag_store(q + i, 0u, 0u);  // consumed
+  }
+  __syncthreads();
+  float h_row = NAN;
+  if (tid == 0) {
+    Part a = S > 1 ? got[0] : p;
+    for (int j = 1; j < S - 1; ++j) part_merge(a, got[j]);
+    if (S > 1) part_merge(a, p);
+    if (fail_sh) a.nan = 1;
+    write_row(a, row, H, amax, conf, &h_row);
+    if (emax) tag_store(hpub + row, tag, __float_as_uint(h_row));
+  }
+  if (!emax || blockIdx.x != gridDim.x - 1) return;
+  // ---- the last workgroup: E over the selected rows once every row has published
+  // (all rows' words are awaited and cleared, also rows outside the selection)
+  if (tid == 0) fail_sh = 0;
+  __syncthreads();
+  for (int r = tid; r < rows; r += kFThreads) {
+    uint32_t w = 0;
+    if (!tag_wait<1>(hpub + r, tag, &w)) atomicOr(&fail_sh, 1);
+  }
+  __syncthreads();
+  float mx = kNegInf;
+  int nan = fail_sh;
+  const int n = sel ? n_sel : rows;
+  for (int i = tid; i < n; i += kFThreads) {
+    const int r = sel ? sel[i] : i;
+    if (r < 0 || r >= rows) {
+      nan = 1;
+      continue;
+    }
+    const float h = __uint_as_float((uint32_t)__hip_atomic_load(hpub + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (h != h) nan = 1;
+    else mx = fmaxf(mx, h);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+    nan |= __shfl_xor(nan, o);
+  }
+  if ((tid & 63) == 0) {
+    emax_sh[tid >> 6] = mx;
+    enan_sh[tid >> 6] = nan;
+  }
+  __syncthreads();
+  for (int r = tid; r < rows; r += kFThreads) tag_store(hpub + r, 0u, 0u);  // consumed
+  if (tid == 0) {
+    for (int w = 1; w < kFWaves; ++w) {
+      mx = fmaxf(mx, emax_sh[w]);
+      nan |= enan_sh[w];
+    }
+    *emax = nan ? NAN : mx;
+  }
 }
 
 __global__ void fill_kernel(float* p, float v) { *p = v; }
 
-// slice length: kU vectors per lane of one wavefront -> 1024 bf16 / 512 f32 elements
-int slice_len(ec_dtype dt) { return 64 * kU * (dt == EC_BF16 ? 8 : 4); }
+// slices per row: enough workgroups to cover the CUs, slices of at least 2048 elements
+int splits_for(int rows, int vocab) {
+  const int by_cus = (256 + rows - 1) / rows;
+  const int by_len = (vocab + 2047) / 2048;
+  return std::max(1, std::min({by_cus, by_len, kMaxSplits}));
+}
 
+}  // namespace
+
+namespace {
+// A fresh tag per call: a counter passed through a 32-bit mixing bijection, so that tags
+// do not look like the small integers a reused workspace may hold; never 0 (the tag of
+// a cleared word).
+uint32_t next_tag() {
+  static std::atomic<uint32_t> counter{0};
+  for (;;) {
+    uint32_t t = counter.fetch_add(1, std::memory_order_relaxed) + 0x632BE5ABu;
+    t ^= t >> 16;
+    t *= 0x85EBCA6Bu;
+    t ^= t >> 13;
+    t *= 0xC2B2AE35u;
+    t ^= t >> 16;
+    if (t != 0) return t;
+  }
+}
 }  // namespace
 
 size_t entropy_ws_bytes(int rows, int vocab) {
   if (rows <= 0 || vocab <= 0) return 0;
-  const int splits = (vocab + slice_len(EC_F32) - 1) / slice_len(EC_F32);  // the larger count
-  return (size_t)rows * splits * sizeof(Part) + 256;
+  // tagged slice states [rows][S][4] and published row entropies [rows], 64-bit words
+  return ((size_t)rows * splits_for(rows, vocab) * 4 + (size_t)rows) * sizeof(uint64_t) + 256;
 }
 
 ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t stride,
@@ -298,35 +430,34 @@ ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t 
     }
     return EC_OK;
   }
-  const int chunk = slice_len(dt);
-  const int splits = (vocab + chunk - 1) / chunk;
-  Part* parts = (Part*)ws;
+  const int S = splits_for(rows, vocab);
+  const int E = dt == EC_BF16 ? 8 : 4;
+  const int chunk = ((vocab + S - 1) / S + E - 1) / E * E;  // slice starts stay 16-byte aligned
+  uint64_t* parts = (uint64_t*)ws;
+  uint64_t* hpub = parts + (size_t)rows * S * 4;
+  const uint32_t tag = next_tag();
   const size_t esz = dt == EC_BF16 ? 2 : 4;
   const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * esz) % 16 == 0);
-  dim3 grid((splits + 3) / 4, rows);
+  const dim3 grid((unsigned)((int64_t)rows * S));
+#define EC_LAUNCH(T, V)                                                                                  \
+  entropy_fused_kernel<T, V><<<grid, kFThreads, 0, s>>>((const T*)logits, rows, vocab, stride, S, chunk, \
+                                                        sel, n_sel, H, amax, c, emax, parts, hpub, tag)
   if (dt == EC_BF16) {
-    if (vec)
-      entropy_slice_kernel<bf16, true, kU><<<grid, 256, 0, s>>>((const bf16*)logits, vocab, stride, chunk, splits, parts);
-    else
-      entropy_slice_kernel<bf16, false, kU><<<grid, 256, 0, s>>>((const bf16*)logits, vocab, stride, chunk, splits, parts);
+    if (vec) EC_LAUNCH(bf16, true);
+    else EC_LAUNCH(bf16, false);
   } else {
-    if (vec)
-      entropy_slice_kernel<float, true, kU><<<grid, 256, 0, s>>>((const float*)logits, vocab, stride, chunk, splits, parts);
-    else
-      entropy_slice_kernel<float, false, kU><<<grid, 256, 0, s>>>((const float*)logits, vocab, stride, chunk, splits, parts);
+    if (vec) EC_LAUNCH(float, true);
+    else EC_LAUNCH(float, false);
   }
-  EC_CHECK_LAUNCH("entropy_slice_kernel");
-  return entropy_merge(parts, rows, splits, H, amax, c, sel, n_sel, emax, s);
+#undef EC_LAUNCH
+  EC_CHECK_LAUNCH("entropy_fused_kernel");
+  return EC_OK;
 }
 
 ec_status entropy_merge(const EntPart* parts, int rows, int splits, float* H, int32_t* amax, float* c,
-                        const int32_t* sel, int n_sel, float* emax, hipStream_t s) {
+                        hipStream_t s) {
   entropy_merge_kernel<<<rows, 64, 0, s>>>(parts, splits, H, amax, c);
   EC_CHECK_LAUNCH("entropy_merge_kernel");
-  if (emax) {
-    entropy_emax_kernel<<<1, kThreads, 0, s>>>(H, rows, sel, n_sel, emax);
-    EC_CHECK_LAUNCH("entropy_emax_kernel");
-  }
   return EC_OK;
 }
 

@@ -52,6 +52,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ void part_merge(EntPart& a, const EntPart& b) {
   const float mm = fmaxf(a.m, b.m);
   if (b.m > a.m || (b.m == a.m && b.idx < a.idx)) a.idx = b.idx;
+  a.nan |= b.nan;
   if (mm == -INFINITY) return;  // both empty: z = s = 0
   float z = 0.f, s = 0.f;
   if (a.m != -INFINITY) {
@@ -67,7 +68,6 @@ __device__ __forceinline__ void part_merge(EntPart& a, const EntPart& b) {
   a.m = mm;
   a.z = z;
   a.s = s;
-  a.nan |= b.nan;
 }
 
 // Rotary pair (x1, x2) at columns (col, col + D/2) of the [3d] q|k|v output, col in
@@ -203,7 +203,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   // with few weight tiles the K splits already spread the reads, so there is no rotation;
   // nor for the LM head with the entropy epilogue (988 weight tiles), which it made 10 %
   // slower. The order depends only on the weight tile and the plan.
-  const int rot = (EPI != EPI_ENTROPY && MT == 1 && ntk / splits >= 64)
+  const int rot = (EPI != EPI_ENTROPY && EPI != EPI_STORE && MT == 1 && ntk / splits >= 64)
                       ? (int)(((unsigned)nt * 5u) % (unsigned)nk) : 0;
 
   const int tid = threadIdx.x, lane = tid % 64;
@@ -355,10 +355,11 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
       const int r = lane & 31, cb = (lane >> 5) * CW;
       const int colb = n0 + wn * WN + cb;
       float mx = -INFINITY, z = 0.f, s2 = 0.f;
-      int ix = 0x7fffffff;
+      int ix = 0x7fffffff, has_nan = 0;
 #pragma unroll
       for (int c = 0; c < CW; ++c) {
         const float x = colb + c < N ? (float)(bf16)slab[r * ES + cb + c] : -INFINITY;
+        has_nan |= x != x;  // carried as a flag: a share of NaN / -inf alone keeps z = 0
         if (x > mx) {  // NaN never wins; the first index of the max stays
           mx = x;
           ix = colb + c;
@@ -375,9 +376,9 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
           s2 = fmaf(fmaxf(t, -1000.f), e, s2);     // -inf logit: -1000 * 0 = 0
         }
       }
-      EntPart a{mx, z, s2 * kLn2, ix, 0, {0, 0, 0}};
-      EntPart b{__shfl_xor(a.m, 32), __shfl_xor(a.z, 32), __shfl_xor(a.s, 32), __shfl_xor(a.idx, 32), 0,
-                {0, 0, 0}};
+      EntPart a{mx, z, s2 * kLn2, ix, has_nan, {0, 0, 0}};
+      EntPart b{__shfl_xor(a.m, 32), __shfl_xor(a.z, 32), __shfl_xor(a.s, 32), __shfl_xor(a.idx, 32),
+                __shfl_xor(a.nan, 32), {0, 0, 0}};
       if (lane < 32) {
         part_merge(a, b);
         reinterpret_cast<EntPart*>(smem + NW * 32 * ES * 4)[(wm * WM + 32 * i + r) * WAVES_N + wn] = a;
@@ -678,8 +679,10 @@ Plan plan_bf16(int M, int N, int K, int kind) {
   double best_us = 1e300;
   const int nk = K / BK;
   // the fused entropy epilogue needs whole K and stages one state per row and
-  // wavefront column next to the slabs: 128x128 and 64x128 tiles only
-  const bool ent = kind == EPI_ENTROPY;
+  // wavefront column next to the slabs: 128x128 and 64x128 tiles only. The stored-logits
+  // LM head (EPI_STORE) takes the same plan and K order, so the logits it writes are
+  // exactly the values the fused epilogue reduces.
+  const bool ent = kind == EPI_ENTROPY || kind == EPI_STORE;
   for (int c = 0; c < kNumTileCfg; ++c) {
     const TileInfo& t = kTile[c];
     if (M <= 64 && c != T64x128) continue;
@@ -714,8 +717,10 @@ ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, int M, int N,
   constexpr size_t lds = (size_t)NSTG * (BM + BN) * BKS * 2;
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int grid = p.MT * p.NT * p.S;
-  auto run = [&](auto kern) -> ec_status {
-    static LdsLimit limit;
+  // one limit record per kernel: the split and whole-K kernels share a function type,
+  // so a static inside the generic lambda would be shared by both
+  static LdsLimit whole, split;
+  auto run = [&](auto kern, LdsLimit& limit) -> ec_status {
     const ec_status st = limit.ensure((const void*)kern, (int)lds);
     if (st != EC_OK) return st;
     kern<<<grid, NT, lds, s>>>(A, B, M, N, K, p.k_chunk, p.S, epi, part);
@@ -723,15 +728,15 @@ ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, int M, int N,
     return EC_OK;
   };
   if constexpr (EPI != EPI_ENTROPY) {
-    if (p.S > 1) return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, true, BKS>);
+    if (p.S > 1) return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, true, BKS>, split);
   }
-  return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, false, BKS>);
+  return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, false, BKS>, whole);
 }
 
 template <int EPI>
 ec_status launch_cfg(const Plan& p, const bf16* A, const bf16* B, int M, int N, int K,
                      const EpiArgs& epi, float* part, hipStream_t s) {
-  if constexpr (EPI == EPI_ENTROPY) {
+  if constexpr (EPI == EPI_ENTROPY || EPI == EPI_STORE) {
     if (p.cfg == T128x128) return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
     return launch_bf16<64, 128, 32, 32, 6, true, EPI>(p, A, B, M, N, K, epi, part, s);
   } else {

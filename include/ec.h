@@ -111,8 +111,11 @@ ec_status ec_cache_scatter(void* k_cache, void* v_cache, int64_t seq_len, int32_
  *
  * out[i, h, :] = softmax_j(q[i,h,:] . k_cache[j,h,:] * scale) @ v_cache[:,h,:]
  * q, out: [r, n_heads * head_dim]; k_cache, v_cache: [seq_len, n_heads *
- * head_dim]; all of dtype; scale > 0. bf16 runs on MFMA with fp32 softmax; the
- * probabilities enter the P.V product rounded to bf16.
+ * head_dim]; all of dtype; scale > 0. bf16 runs on MFMA with fp32 softmax: with
+ * t_j = q . k_j * scale * log2(e) and M an integer >= max_j t_j, the weights
+ * w_j = 2^(t_j - M) enter the P.V product rounded to bf16 and the row sum
+ * unrounded, out = sum_j bf16(w_j) v_j / sum_j w_j (bf16 rounding commutes with
+ * powers of two, so the result does not depend on M).
  * Supported: head_dim == 128 for bf16, with max(r, seq_len) * n_heads * 256
  * bytes below 2 GiB (32-bit buffer offsets); head_dim <= 256 for f32.
  * EC_ERR_UNSUPPORTED otherwise.
@@ -311,21 +314,6 @@ ec_status ec_step(const ec_model_desc* model, const ec_cache_desc* cache, ec_sta
                   const ec_params* params, void* workspace, size_t workspace_bytes,
                   void* stream, ec_step_out* out);
 
-/* ec_step_batch -- one denoising step of n_seq independent sequences of the same
- * model with the same params (every field but the state and cache is shared),
- * decided per sequence exactly as ec_step decides it: sequence s refreshes when
- * its own t == 0 or its refresh_next is set, otherwise it recomputes its own
- * recompute set, and it reads its own E. All sequences' rows go through one
- * forward (one launch per GEMM over the concatenated rows, so every weight is
- * read once per step for the whole batch; attention runs per sequence against
- * that sequence's cache); one LM head over all candidates with the entropy
- * reduction fused for bf16; selection per sequence.
- * (EntropyCache explainer, Arabic technical summary, section 2, with the
- * decision taken per sequence; the batching itself is not on the pages.)
- * caches, states, outs: HOST arrays of n_seq entries (1 <= n_seq <= EC_MAX_SEQ);
- * a sequence with no masked position left is not stepped (its out has
- * n_decoded = 0). Synchronises `stream` once. Returns EC_ERR_NAN if any
- * sequence's E is NaN (that sequence's out->status says which). */
 /* ec_step_probe -- ec_step plus the KV-drift probe (the pages' drift measure: the
  * cosine distance of cached vs freshly computed value vectors between consecutive
  * steps, which they report tracks the previous step's E; EntropyCache explainer,
@@ -342,6 +330,21 @@ ec_status ec_step_probe(const ec_model_desc* model, const ec_cache_desc* cache, 
                         const ec_params* params, void* workspace, size_t workspace_bytes, void* stream,
                         ec_step_out* out, float* drift);
 
+/* ec_step_batch -- one denoising step of n_seq independent sequences of the same
+ * model with the same params (every field but the state and cache is shared),
+ * decided per sequence exactly as ec_step decides it: sequence s refreshes when
+ * its own t == 0 or its refresh_next is set, otherwise it recomputes its own
+ * recompute set, and it reads its own E. All sequences' rows go through one
+ * forward (one launch per GEMM over the concatenated rows, so every weight is
+ * read once per step for the whole batch; attention runs per sequence against
+ * that sequence's cache); one LM head over all candidates with the entropy
+ * reduction fused for bf16; selection per sequence.
+ * (EntropyCache explainer, Arabic technical summary, section 2, with the
+ * decision taken per sequence; the batching itself is not on the pages.)
+ * caches, states, outs: HOST arrays of n_seq entries (1 <= n_seq <= EC_MAX_SEQ);
+ * a sequence with no masked position left is not stepped (its out has
+ * n_decoded = 0). Synchronises `stream` once. Returns EC_ERR_NAN if any
+ * sequence's E is NaN (that sequence's out->status says which). */
 size_t ec_step_batch_workspace_size(const ec_model_desc* model, int32_t n_seq, const ec_params* params);
 ec_status ec_step_batch(const ec_model_desc* model, int32_t n_seq, const ec_cache_desc* caches,
                         ec_state* states, const ec_params* params, void* workspace,

@@ -104,3 +104,27 @@ def test_entropy_deterministic():
     r2 = [t.cpu() for t in ek.ec_entropy_max(x)]
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_entropy_row_with_a_whole_block_of_nan(dtype):
+    """A NaN logit makes its row's entropy and confidence NaN even when a whole block of
+    the row the reduction handles as one piece (2048 aligned columns cover every split the
+    kernels use) holds nothing but NaN, or NaN and -inf: the block's maximum is then -inf
+    and its sums are empty, so the NaN must travel as a flag. E over those rows is NaN."""
+    V = 20000
+    rng = np.random.default_rng(5)
+    z = (rng.standard_normal((4, V)) * 2).astype(np.float32)
+    z[0, 2048:4096] = np.nan
+    z[1, 4096:6144] = np.nan
+    z[1, 4096:6144:3] = -np.inf
+    z[2, :] = -np.inf
+    z[2, 8192:10240] = np.nan
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(z)
+        x, ref = bf16_tensor(bits), bf16_bits_to_f64(bits)
+    else:
+        x, ref = torch.from_numpy(z).cuda(), z.astype(np.float64)
+    Hg, h0 = _check(x, ref)
+    assert np.isnan(Hg[:3]).all() and not np.isnan(Hg[3])
+    _check(x, ref, sel=torch.tensor([3], dtype=torch.int32, device="cuda"))
