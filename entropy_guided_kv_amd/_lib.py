@@ -13,6 +13,7 @@ EC_LAYOUT_PLAIN, EC_LAYOUT_PACKED = 0, 1
 EC_CAND_BLOCKS, EC_CAND_WINDOW = 0, 1
 EC_MAX_TOKENS_PER_STEP = 64
 EC_MAX_SEQ = 16
+EC_ENTROPY_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 STATUS_NAMES = {
     0: "EC_OK", 1: "EC_ERR_ARG", 2: "EC_ERR_DTYPE", 3: "EC_ERR_WORKSPACE", 4: "EC_ERR_HIP",
@@ -20,7 +21,7 @@ STATUS_NAMES = {
 }
 
 EXPORTS = (
-    "ec_entropy_max_workspace_size", "ec_entropy_max", "ec_cache_scatter",
+    "ec_entropy_max_workspace_size", "ec_entropy_max", "ec_entropy_max_noalloc", "ec_cache_scatter",
     "ec_partial_attn_workspace_size", "ec_partial_attn", "ec_rope_table",
     "ec_forward_workspace_size", "ec_forward", "ec_state_plan_words", "ec_state_reset",
     "ec_step_workspace_size", "ec_step", "ec_timing_enable", "ec_timing_select", "ec_timing_read",
@@ -108,6 +109,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     sig = {
         "ec_entropy_max_workspace_size": (sz, [i32, i32]),
         "ec_entropy_max": (C.c_int, [vp, C.c_int, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "ec_entropy_max_noalloc": (C.c_int, [vp, C.c_int, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp]),
         "ec_cache_scatter": (C.c_int, [vp, vp, i64, i32, C.c_int, vp, vp, vp, i32, vp]),
         "ec_partial_attn_workspace_size": (sz, [i32, i32, i32, i32]),
         "ec_partial_attn": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, f32, C.c_int, vp, vp, sz, vp]),

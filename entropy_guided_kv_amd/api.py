@@ -84,6 +84,35 @@ def ec_entropy_max(logits: torch.Tensor, sel: Optional[torch.Tensor] = None, str
     return H, a, c, e
 
 
+def ec_entropy_max_noalloc(logits: torch.Tensor, sel: Optional[torch.Tensor] = None, stream=None, out=None):
+    """ec_entropy_max without a workspace (the library's own device scratch array): for
+    callers that cannot allocate. Same arguments and results as ec_entropy_max; ``out``
+    (four tensors as there) avoids allocating the outputs too."""
+    lib = load()
+    _need_cuda(logits, sel)
+    if logits.dim() != 2 or (logits.shape[0] > 0 and logits.stride(1) != 1):
+        raise ValueError("logits must be 2-D with unit column stride")
+    rows, V = logits.shape
+    dev = logits.device
+    if out is not None:
+        H, a, c, e = out
+        if (H.numel() < rows or a.numel() < rows or c.numel() < rows or e.numel() < 1
+                or (H.dtype, a.dtype, c.dtype, e.dtype) != (torch.float32, torch.int32, torch.float32, torch.float32)):
+            raise ValueError("out: need float32[rows], int32[rows], float32[rows], float32[1]")
+    else:
+        H = torch.empty(rows, dtype=torch.float32, device=dev)
+        a = torch.empty(rows, dtype=torch.int32, device=dev)
+        c = torch.empty(rows, dtype=torch.float32, device=dev)
+        e = torch.empty(1, dtype=torch.float32, device=dev)
+    if sel is not None and sel.dtype != torch.int32:
+        raise ValueError("sel must be int32 (no conversion is made here)")
+    stride = logits.stride(0) if rows > 0 else V
+    check(lib.ec_entropy_max_noalloc(_ptr(logits), _dtype(logits), rows, V, stride, _ptr(sel),
+                                     0 if sel is None else sel.numel(), _ptr(H), _ptr(a), _ptr(c), _ptr(e),
+                                     _stream(stream)), "ec_entropy_max_noalloc")
+    return H, a, c, e
+
+
 def ec_cache_scatter(k_cache: torch.Tensor, v_cache: torch.Tensor, k_rows: torch.Tensor,
                      v_rows: torch.Tensor, idx: torch.Tensor, stream=None) -> None:
     """k_cache[idx[i]] = k_rows[i]; v_cache[idx[i]] = v_rows[i] (in place)."""

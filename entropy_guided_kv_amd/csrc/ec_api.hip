@@ -657,6 +657,21 @@ ec_status ec_entropy_max(const void* logits, ec_dtype dtype, int32_t rows, int32
                      workspace, workspace_bytes, (hipStream_t)stream);
 }
 
+ec_status ec_entropy_max_noalloc(const void* logits, ec_dtype dtype, int32_t rows, int32_t vocab,
+                                 int64_t row_stride, const int32_t* sel, int32_t n_sel, float* entropy,
+                                 int32_t* argmax, float* maxprob, float* emax, void* stream) {
+  static_assert(EC_ENTROPY_NOALLOC_SCRATCH_BYTES == kEntropyScratchBytes, "scratch size mismatch");
+  EC_REQUIRE(dtype_ok(dtype), EC_ERR_DTYPE, "ec_entropy_max_noalloc: bad dtype %d", (int)dtype);
+  EC_REQUIRE(rows >= 0 && vocab >= 1 && row_stride >= vocab, EC_ERR_ARG,
+             "ec_entropy_max_noalloc: rows %d vocab %d stride %lld", rows, vocab, (long long)row_stride);
+  EC_REQUIRE(n_sel >= 0, EC_ERR_ARG, "ec_entropy_max_noalloc: n_sel < 0");
+  if (rows > 0)
+    EC_REQUIRE(logits && entropy && argmax && maxprob, EC_ERR_ARG, "ec_entropy_max_noalloc: null pointer");
+  TScope t(EC_T_ENTROPY, (hipStream_t)stream, 0.0, (double)rows * vocab * esize(dtype));
+  return ec::entropy_noalloc(dtype, logits, rows, vocab, row_stride, sel, n_sel, entropy, argmax, maxprob, emax,
+                             (hipStream_t)stream);
+}
+
 ec_status ec_cache_scatter(void* k_cache, void* v_cache, int64_t seq_len, int32_t width,
                            ec_dtype dtype, const void* k_rows, const void* v_rows,
                            const int32_t* idx, int32_t n_rows, void* stream) {

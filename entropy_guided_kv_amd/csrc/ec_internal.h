@@ -177,6 +177,10 @@ size_t entropy_ws_bytes(int rows, int vocab);
 // argmax / confidence
 ec_status entropy_merge(const EntPart* parts, int rows, int splits, float* H, int32_t* amax, float* c,
                         hipStream_t s);
+// ec_entropy_max_noalloc: the same reduction with its scratch in the library's device array
+constexpr size_t kEntropyScratchBytes = (size_t)1 << 20;
+ec_status entropy_noalloc(ec_dtype dt, const void* logits, int rows, int vocab, int64_t stride, const int32_t* sel,
+                          int n_sel, float* H, int32_t* amax, float* c, float* emax, hipStream_t s);
 ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t stride,
                   const int32_t* sel, int n_sel, float* H, int32_t* amax, float* c, float* emax,
                   void* ws, size_t ws_bytes, hipStream_t s);

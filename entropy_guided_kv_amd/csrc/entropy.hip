@@ -454,6 +454,47 @@ ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t 
   return EC_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free variant
+// Scratch of ec_entropy_max_noalloc: the tagged slice states and row entropies of the
+// single-launch reduction, in a device array of the library instead of a caller's
+// workspace. It is zero when the code object loads, and every word a call tags is set
+// back to zero by the workgroup that consumes it, so each call finds it cleared. One
+// array per GPU (each device has its own copy at its own address), shared by every call
+// on that GPU: calls that overlap in time on one GPU race.
+static __device__ __align__(256) uint64_t scratch[kEntropyScratchBytes / sizeof(uint64_t)];
+
+namespace {
+std::atomic<void*> g_scratch_ptr[64];  // device address of `scratch` per device ordinal
+
+// `scratch` is only a host-side stand-in for the array: kernels get its device address,
+// looked up once per device with that device current
+ec_status scratch_ptr(void** out) {
+  int dev = 0;
+  EC_CHECK_HIP(hipGetDevice(&dev));
+  EC_REQUIRE(dev >= 0 && dev < 64, EC_ERR_UNSUPPORTED, "ec_entropy_max_noalloc: device ordinal %d >= 64", dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    EC_CHECK_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    EC_REQUIRE(p != nullptr, EC_ERR_HIP, "ec_entropy_max_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return EC_OK;
+}
+}  // namespace
+
+ec_status entropy_noalloc(ec_dtype dt, const void* logits, int rows, int vocab, int64_t stride, const int32_t* sel,
+                          int n_sel, float* H, int32_t* amax, float* c, float* emax, hipStream_t s) {
+  const size_t need = entropy_ws_bytes(rows, vocab);
+  EC_REQUIRE(need <= kEntropyScratchBytes, EC_ERR_UNSUPPORTED,
+             "ec_entropy_max_noalloc: %d rows of %d need %zu bytes of scratch, above the %zu-byte array", rows,
+             vocab, need, (size_t)kEntropyScratchBytes);
+  void* p = nullptr;
+  const ec_status st = scratch_ptr(&p);
+  if (st != EC_OK) return st;
+  return entropy(dt, logits, rows, vocab, stride, sel, n_sel, H, amax, c, emax, p, kEntropyScratchBytes, s);
+}
+
 ec_status entropy_merge(const EntPart* parts, int rows, int splits, float* H, int32_t* amax, float* c,
                         hipStream_t s) {
   entropy_merge_kernel<<<rows, 64, 0, s>>>(parts, splits, H, amax, c);

@@ -87,6 +87,25 @@ ec_status ec_entropy_max(const void* logits, ec_dtype dtype, int32_t rows, int32
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * ec_entropy_max_noalloc -- ec_entropy_max for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments and results as ec_entropy_max
+ * (bit-identical outputs), without the workspace: the reduction's scratch lives in a
+ * device array of the library, EC_ENTROPY_NOALLOC_SCRATCH_BYTES per GPU, held until the
+ * process ends. The call allocates nothing. Every call on one GPU shares that GPU's
+ * array (each word a call uses is left cleared for the next call): calls on one GPU
+ * must be ordered (one stream, or streams with events between them); calls that overlap
+ * in time on one GPU race.
+ * Errors: as ec_entropy_max; EC_ERR_UNSUPPORTED (nothing enqueued) when
+ * ec_entropy_max_workspace_size(rows, vocab) exceeds EC_ENTROPY_NOALLOC_SCRATCH_BYTES
+ * (about 26000 rows at any vocabulary up to 2^31).
+ * ---------------------------------------------------------------------- */
+#define EC_ENTROPY_NOALLOC_SCRATCH_BYTES (1u << 20)
+ec_status ec_entropy_max_noalloc(const void* logits, ec_dtype dtype, int32_t rows, int32_t vocab,
+                                 int64_t row_stride, const int32_t* sel, int32_t n_sel, float* entropy,
+                                 int32_t* argmax, float* maxprob, float* emax, void* stream);
+
+/* ------------------------------------------------------------------------
  * ec_cache_scatter -- write recomputed K/V rows into one layer's cache.
  *
  * k_cache[idx[i], :] = k_rows[i, :] and v_cache[idx[i], :] = v_rows[i, :]

@@ -169,3 +169,14 @@ def test_argument_errors_return_before_any_gpu_work(lib):
     ws4 = lib.ec_step_batch_workspace_size(C.byref(m), 4, C.byref(_params()))
     assert ws1 > 0 and ws4 > 3 * ws1 // 2
 
+
+def test_noalloc_entropy_rejects_before_any_gpu_work(lib):
+    """ec_entropy_max_noalloc: bad arguments and inputs whose scratch need exceeds the
+    library's array are rejected on the host, before any device call."""
+    rows, V = 40000, 4096
+    assert lib.ec_entropy_max_workspace_size(rows, V) > _lib.EC_ENTROPY_NOALLOC_SCRATCH_BYTES
+    p = 0x1000  # never dereferenced: every case fails its checks first
+    assert lib.ec_entropy_max_noalloc(p, _lib.EC_BF16, rows, V, V, None, 0, p, p, p, p, None) == _lib.EC_ERR_UNSUPPORTED
+    assert lib.ec_entropy_max_noalloc(p, 7, 4, V, V, None, 0, p, p, p, p, None) == _lib.EC_ERR_DTYPE
+    assert lib.ec_entropy_max_noalloc(p, _lib.EC_BF16, 4, V, V - 1, None, 0, p, p, p, p, None) == _lib.EC_ERR_ARG
+    assert lib.ec_entropy_max_noalloc(None, _lib.EC_BF16, 4, V, V, None, 0, p, p, p, p, None) == _lib.EC_ERR_ARG
