@@ -79,9 +79,8 @@ __device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
 // grid: (query tiles, heads, splits); dynamic LDS of kAttnLds bytes
 template <bool SPLIT>
 __global__ void __launch_bounds__(kAttnThreads)
-attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
-                 const bf16* __restrict__ vc, int r, int L, int H, float scale_log2,
-                 int kv_chunk, bf16* __restrict__ out, float* __restrict__ po,
+attn_bf16_kernel(const bf16* __restrict__ q_all, const AttnSeqs seqs, int L, int H, float scale_log2,
+                 int kv_chunk, int nsplit, int r_all, bf16* __restrict__ out_all, float* __restrict__ po,
                  float* __restrict__ pml) {
   // K and V tiles in natural [key][dim] layout, one stage per tile of the ring: the four
   // K stages in the first 64 KB, the four V stages in the next, so that with the tile loop
@@ -94,7 +93,24 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
   // a transposing read fall in distinct quarters.
   extern __shared__ __align__(16) unsigned char lds_raw[];
 
-  const int qt = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
+  // Logical block order: sequence by sequence, inside one split-major, then head, with the
+  // query tiles of a head consecutive; the XCD-aware remap gives each XCD a contiguous
+  // run of it, so the query tiles that read one head's K / V share one L2.
+  int bid = xcd_remap(blockIdx.x, gridDim.x), si = 0, qtiles = 1;
+  for (;;) {
+    qtiles = (seqs.s[si].nr + BQ - 1) / BQ;
+    const int nb = qtiles * H * nsplit;
+    if (bid < nb || si + 1 >= seqs.n) break;
+    bid -= nb;
+    ++si;
+  }
+  if (seqs.s[si].nr <= 0) return;  // (the grid counts only sequences with rows; uniform per workgroup)
+  const int qt = bid % qtiles, h = (bid / qtiles) % H, split = bid / (qtiles * H);
+  const int row0 = seqs.s[si].row0, r = seqs.s[si].nr;
+  const bf16* __restrict__ q = q_all + (int64_t)row0 * H * D;
+  const bf16* __restrict__ kc = (const bf16*)seqs.s[si].k;
+  const bf16* __restrict__ vc = (const bf16*)seqs.s[si].v;
+  bf16* __restrict__ out = SPLIT ? nullptr : out_all + (int64_t)row0 * H * D;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int qw = wave % 4, kh = wave / 4;   // query group, key half of every tile
@@ -357,13 +373,13 @@ attn_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
 #pragma unroll
       for (int v = 0; v < 16; ++v) dst[32 * i + 8 * (v / 4) + 4 * g + (v % 4)] = (bf16)(o[i][v] * inv);
   } else {
-    float* dst = po + (((int64_t)split * r + qrow) * H + h) * D;
+    float* dst = po + (((int64_t)split * r_all + row0 + qrow) * H + h) * D;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) dst[32 * i + 8 * (v / 4) + 4 * g + (v % 4)] = o[i][v];
     if (g == 0) {
-      float* ml = pml + (((int64_t)split * r + qrow) * H + h) * 2;
+      float* ml = pml + (((int64_t)split * r_all + row0 + qrow) * H + h) * 2;
       ml[0] = m_ref;
       ml[1] = l_run;
     }
@@ -427,12 +443,15 @@ ec_status launch_merge(const float* po, const float* pml, int S, int r, int H, i
 
 // fp32 path: one workgroup per (query, head); scores in LDS, exact softmax.
 __global__ void __launch_bounds__(kThreads)
-attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ kc,
-                const float* __restrict__ vc, int L, int H, int Dh, float scale,
+attn_f32_kernel(const float* __restrict__ q, const AttnSeqs seqs, int L, int H, int Dh, float scale,
                 float* __restrict__ out) {
   extern __shared__ float sc[];  // [L] scores, then [Dh] query
   float* sq = sc + L;
-  const int i = blockIdx.x, h = blockIdx.y;
+  const int i = blockIdx.x, h = blockIdx.y;  // i: row of the compact q / out of all sequences
+  int si = 0;
+  while (si + 1 < seqs.n && i >= seqs.s[si].row0 + seqs.s[si].nr) ++si;
+  const float* __restrict__ kc = (const float*)seqs.s[si].k;
+  const float* __restrict__ vc = (const float*)seqs.s[si].v;
   const int64_t HD = (int64_t)H * Dh;
   for (int d = threadIdx.x; d < Dh; d += kThreads) sq[d] = q[(int64_t)i * HD + h * Dh + d];
   __syncthreads();
@@ -475,23 +494,25 @@ attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ kc,
 }
 
 struct AttnPlan {
-  int qtiles, splits, chunk;
+  int splits, chunk;
 };
 
 // Key-range split by a cost model fitted to MI355X measurements of every split count
 // (r = 17 .. 4096 queries, L = 1024 and 4096, 32 heads; it picks the fastest on each):
 // waves of workgroups x tiles per workgroup x 0.9 us, plus, when split, 0.008 us per
-// (split x query) for the partials' round trip and merge (scaled by H / 32).
-AttnPlan plan_attn(int r, int L, int H) {
+// (split x query) for the partials' round trip and merge (scaled by H / 32). r is the
+// number of query rows and qtiles the number of 128-query tiles over every sequence of
+// the launch; splits whose partials would not fit max_ws bytes are skipped.
+AttnPlan plan_attn(int r, int qtiles, int L, int H, size_t max_ws = (size_t)-1) {
   AttnPlan p;
-  p.qtiles = (r + BQ - 1) / BQ;
-  const int base = p.qtiles * H;
+  const int base = qtiles * H;
   double best = 1e300;
   int s_best = 1;
   for (int s : {1, 2, 3, 4, 6, 8, 12, 16}) {
     if (s > 1 && L / s < BKV) break;
     const int chunk = ((L + s - 1) / s + BKV - 1) / BKV * BKV;
     const int splits = (L + chunk - 1) / chunk;
+    if (splits > 1 && (size_t)splits * r * H * (D + 2) * sizeof(float) + 512 > max_ws) continue;
     const double waves = (double)(((int64_t)base * splits + 255) / 256);
     double us = waves * (chunk / BKV) * 0.9;
     if (splits > 1) us += 0.008 * splits * r * (H / 32.0);
@@ -509,21 +530,37 @@ AttnPlan plan_attn(int r, int L, int H) {
 
 size_t attn_ws_bytes(int r, int L, int H, int Dh) {
   if (r <= 0 || Dh != D) return 0;
-  AttnPlan p = plan_attn(r, L, H);
+  AttnPlan p = plan_attn(r, (r + BQ - 1) / BQ, L, H);
   if (p.splits <= 1) return 0;
   return (size_t)p.splits * r * H * (Dh + 2) * sizeof(float) + 512;
 }
 
 ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, int L, int H,
                int Dh, float scale, void* out, void* ws, size_t ws_bytes, hipStream_t s) {
+  AttnSeqs one{};
+  one.n = 1;
+  one.s[0] = AttnSeq{0, r, k, v};
+  return attn_batch(dt, q, one, L, H, Dh, scale, out, ws, ws_bytes, s);
+}
+
+ec_status attn_batch(ec_dtype dt, const void* q, const AttnSeqs& seqs, int L, int H, int Dh, float scale, void* out,
+                     void* ws, size_t ws_bytes, hipStream_t s) {
+  EC_REQUIRE(seqs.n >= 1 && seqs.n <= EC_MAX_SEQ, EC_ERR_ARG, "attn: %d sequences", seqs.n);
+  int r = 0, qtiles = 0;
+  for (int i = 0; i < seqs.n; ++i) {
+    EC_REQUIRE(seqs.s[i].nr >= 0 && seqs.s[i].row0 == r, EC_ERR_ARG, "attn: sequence %d rows not contiguous", i);
+    EC_REQUIRE(seqs.s[i].nr == 0 || (seqs.s[i].k && seqs.s[i].v), EC_ERR_ARG, "attn: null cache of sequence %d", i);
+    r += seqs.s[i].nr;
+    qtiles += (seqs.s[i].nr + BQ - 1) / BQ;
+  }
   if (r == 0) return EC_OK;
   EC_REQUIRE(L >= 1, EC_ERR_ARG, "attn: seq_len must be >= 1");
   if (dt == EC_F32) {
     EC_REQUIRE(Dh <= 1024 && (size_t)(L + Dh) * 4 <= 64 * 1024, EC_ERR_UNSUPPORTED,
                "attn: f32 path supports L + head_dim <= 16384");
     dim3 grid(r, H);
-    attn_f32_kernel<<<grid, kThreads, (L + Dh) * sizeof(float), s>>>(
-        (const float*)q, (const float*)k, (const float*)v, L, H, Dh, scale, (float*)out);
+    attn_f32_kernel<<<grid, kThreads, (L + Dh) * sizeof(float), s>>>((const float*)q, seqs, L, H, Dh, scale,
+                                                                     (float*)out);
     EC_CHECK_LAUNCH("attn_f32_kernel");
     return EC_OK;
   }
@@ -531,26 +568,23 @@ ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, 
   // q and the caches are addressed through buffer resources with 32-bit byte offsets
   EC_REQUIRE((int64_t)(L > r ? L : r) * H * Dh * 2 <= 0x7fffffff, EC_ERR_UNSUPPORTED,
              "attn: %d rows of %d x %d bf16 exceed the 2 GiB buffer range", L > r ? L : r, H, Dh);
-  AttnPlan p = plan_attn(r, L, H);
+  const AttnPlan p = plan_attn(r, qtiles, L, H, ws ? ws_bytes : 0);
   const float sl = scale * kLog2e;
-  dim3 grid(p.qtiles, H, p.splits);
+  const unsigned grid = (unsigned)((int64_t)qtiles * H * p.splits);
   static LdsLimit whole, split;
   ec_status st = p.splits == 1 ? whole.ensure((const void*)attn_bf16_kernel<false>, kAttnLds)
                                : split.ensure((const void*)attn_bf16_kernel<true>, kAttnLds);
   if (st != EC_OK) return st;
   if (p.splits == 1) {
-    attn_bf16_kernel<false><<<grid, kAttnThreads, kAttnLds, s>>>((const bf16*)q, (const bf16*)k,
-                                                             (const bf16*)v, r, L, H, sl, p.chunk,
-                                                             (bf16*)out, nullptr, nullptr);
+    attn_bf16_kernel<false><<<grid, kAttnThreads, kAttnLds, s>>>((const bf16*)q, seqs, L, H, sl, p.chunk, 1, r,
+                                                                (bf16*)out, nullptr, nullptr);
     EC_CHECK_LAUNCH("attn_bf16_kernel");
     return EC_OK;
   }
-  const size_t need = attn_ws_bytes(r, L, H, Dh);
-  EC_REQUIRE(ws && ws_bytes >= need, EC_ERR_WORKSPACE, "attn: workspace %zu < %zu", ws_bytes, need);
   float* po = (float*)ws;
   float* pml = po + (size_t)p.splits * r * H * Dh;
-  attn_bf16_kernel<true><<<grid, kAttnThreads, kAttnLds, s>>>((const bf16*)q, (const bf16*)k, (const bf16*)v,
-                                                          r, L, H, sl, p.chunk, nullptr, po, pml);
+  attn_bf16_kernel<true><<<grid, kAttnThreads, kAttnLds, s>>>((const bf16*)q, seqs, L, H, sl, p.chunk, p.splits, r,
+                                                             nullptr, po, pml);
   EC_CHECK_LAUNCH("attn_bf16_kernel");
   bf16* o = (bf16*)out;
   switch (p.splits) {

@@ -222,9 +222,7 @@ size_t carve_fwd(const ec_model_desc* m, int max_rows, int max_out, int L, void*
 struct BatchRows {
   int n_seq;
   const int32_t* row_seq;          // device [rows]: sequence of each row
-  const int32_t* const* tok_tab;   // device [n_seq]: token array of each sequence
-  void* const* k_tab;              // device [n_layers * n_seq]: K cache of (layer, sequence)
-  void* const* v_tab;
+  SeqPtrs tok;                     // token array of each sequence (kernel arguments)
   const int* row_off;              // host [n_seq + 1]
   const ec_cache_desc* caches;     // host [n_seq]
 };
@@ -265,7 +263,7 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
   if (n_rows > 0) {
     {
       TScope t(EC_T_EMBED, s, 0.0, M * dd * (es + 4));
-      EC_TRY(embed(dt, m->embed, V, tokens, L, rows, n_rows, d, w.h, s, b ? b->tok_tab : nullptr,
+      EC_TRY(embed(dt, m->embed, V, tokens, L, rows, n_rows, d, w.h, s, b ? &b->tok : nullptr,
                    b ? b->row_seq : nullptr));
     }
     // normed: w.a already holds this layer's attention-norm input (the previous layer's
@@ -283,8 +281,10 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
       e.ldo = d;
       if (b) {
         e.row_seq = b->row_seq;
-        e.k_tab = b->k_tab + (size_t)l * b->n_seq;
-        e.v_tab = b->v_tab + (size_t)l * b->n_seq;
+        for (int q = 0; q < b->n_seq; ++q) {
+          e.k_seq.p[q] = b->caches[q].k[l];
+          e.v_seq.p[q] = b->caches[q].v[l];
+        }
       } else {
         e.k_cache = c->k[l];
         e.v_cache = c->v[l];
@@ -307,15 +307,12 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
       {
         TScope t(EC_T_ATTN, s, 4 * M * Lq * dd, (2 * Lq * dd + 2 * M * dd) * es);
         if (b) {
-          // each sequence's rows attend to that sequence's cache (stream order keeps the
-          // split partials of consecutive launches apart)
-          for (int q = 0; q < b->n_seq; ++q) {
-            const int r0 = b->row_off[q], nr = b->row_off[q + 1] - r0;
-            if (nr == 0) continue;
-            const size_t off = (size_t)r0 * d * esize(dt);
-            EC_TRY(attn(dt, (const char*)w.q + off, b->caches[q].k[l], b->caches[q].v[l], nr, L, H, Dh,
-                        scale, (char*)w.o + off, w.attn, w.attn_bytes, s));
-          }
+          // one launch for every sequence: each sequence's rows attend to its own cache
+          AttnSeqs as{};
+          as.n = b->n_seq;
+          for (int q = 0; q < b->n_seq; ++q)
+            as.s[q] = AttnSeq{b->row_off[q], b->row_off[q + 1] - b->row_off[q], b->caches[q].k[l], b->caches[q].v[l]};
+          EC_TRY(attn_batch(dt, w.q, as, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
         } else {
           EC_TRY(attn(dt, w.q, c->k[l], c->v[l], n_rows, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
         }
@@ -461,9 +458,6 @@ struct BatchWs {
   int32_t* rows_all;
   int32_t* row_seq;
   int32_t* out_all;
-  const int32_t** tok_tab;
-  void** k_tab;
-  void** v_tab;
 };
 
 size_t carve_batch(const ec_model_desc* m, int n_seq, const ec_params* p, void* base, size_t cap, BatchWs* w) {
@@ -482,9 +476,6 @@ size_t carve_batch(const ec_model_desc* m, int n_seq, const ec_params* p, void* 
   x.rows_all = c.take<int32_t>(MR);
   x.row_seq = c.take<int32_t>(MR);
   x.out_all = c.take<int32_t>(MO);
-  x.tok_tab = c.take<const int32_t*>(n_seq);
-  x.k_tab = c.take<void*>((size_t)m->n_layers * n_seq);
-  x.v_tab = c.take<void*>((size_t)m->n_layers * n_seq);
   if (w) *w = x;
   return c.off + 256;
 }
@@ -697,6 +688,9 @@ ec_status ec_partial_attn(const void* q, const void* k_cache, const void* v_cach
   if (r == 0) return EC_OK;
   EC_REQUIRE(q && k_cache && v_cache && out, EC_ERR_ARG, "ec_partial_attn: null pointer");
   EC_REQUIRE(scale > 0.f, EC_ERR_ARG, "ec_partial_attn: scale must be positive");
+  const size_t need = attn_ws_bytes(r, seq_len, n_heads, head_dim);
+  EC_REQUIRE(need == 0 || (workspace && workspace_bytes >= need), EC_ERR_WORKSPACE,
+             "ec_partial_attn: workspace %zu < %zu bytes", workspace_bytes, need);
   return attn(dtype, q, k_cache, v_cache, r, seq_len, n_heads, head_dim, scale, out, workspace,
               workspace_bytes, (hipStream_t)stream);
 }
@@ -825,7 +819,7 @@ ec_status ec_step_batch(const ec_model_desc* model, int32_t n_seq, const ec_cach
   BatchWs w;
   carve_batch(model, n_seq, params, workspace, workspace_bytes, &w);
   const PlanLayout lay(params->seq_len, params->k_recent);
-  const int L = params->seq_len, nl = model->n_layers;
+  const int L = params->seq_len;
 
   // this step's rows and candidates of every sequence, concatenated in sequence order
   BatchSegs segs{};
@@ -850,24 +844,11 @@ ec_status ec_step_batch(const ec_model_desc* model, int32_t n_seq, const ec_cach
   cand_off[n_seq] = C;
   if (segs.n == 0) return EC_OK;
 
-  // device tables of token arrays and of every (layer, sequence) cache; the host
-  // vectors outlive the copies (the stream is synchronised before returning)
-  std::vector<const int32_t*> tok(n_seq);
-  std::vector<void*> kt((size_t)nl * n_seq), vt((size_t)nl * n_seq);
-  for (int q = 0; q < n_seq; ++q) {
-    tok[q] = states[q].tokens;
-    for (int l = 0; l < nl; ++l) {
-      kt[(size_t)l * n_seq + q] = caches[q].k[l];
-      vt[(size_t)l * n_seq + q] = caches[q].v[l];
-    }
-  }
-  EC_CHECK_HIP(hipMemcpyAsync(w.tok_tab, tok.data(), tok.size() * sizeof(void*), hipMemcpyHostToDevice, s));
-  EC_CHECK_HIP(hipMemcpyAsync(w.k_tab, kt.data(), kt.size() * sizeof(void*), hipMemcpyHostToDevice, s));
-  EC_CHECK_HIP(hipMemcpyAsync(w.v_tab, vt.data(), vt.size() * sizeof(void*), hipMemcpyHostToDevice, s));
   st = batch_gather(segs, L, w.rows_all, w.row_seq, w.out_all, s);
   if (st != EC_OK) return st;
 
-  const BatchRows b{n_seq, w.row_seq, w.tok_tab, w.k_tab, w.v_tab, row_off, caches};
+  BatchRows b{n_seq, w.row_seq, SeqPtrs{}, row_off, caches};
+  for (int q = 0; q < n_seq; ++q) b.tok.p[q] = states[q].tokens;
   if (model->dtype == EC_BF16) {
     const FusedEnt fe{(EntPart*)w.ent_ws, w.H, w.amax, w.conf};
     st = run_forward(model, &caches[0], nullptr, w.rows_all, M, w.out_all, C, nullptr, nullptr, w.fwd, s,

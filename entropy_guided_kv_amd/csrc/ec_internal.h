@@ -47,6 +47,16 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voffset, soffset, 0, 0);
 }
 
+// MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each with its
+// own L2: workgroup pid runs on XCD pid % 8. The remapped id gives each XCD a contiguous
+// range of the logical order (XCD x takes ids [x per, (x+1) per) when nblk = 8 per), so
+// neighbours in the logical order share an L2.
+__device__ __forceinline__ int xcd_remap(int pid, int nblk) {
+  const int per = nblk / 8, rem = nblk % 8;
+  const int x = pid % 8, local = pid / 8;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + local;
+}
+
 // ---------------------------------------------------------------- errors
 void set_error(const char* fmt, ...);
 ec_status hip_fail(hipError_t e, const char* what);
@@ -108,6 +118,12 @@ struct EntPart {
   int pad[3];
 };
 
+// one pointer per sequence of a batched forward, passed by value in kernel arguments
+// (no device table to upload per step)
+struct SeqPtrs {
+  const void* p[EC_MAX_SEQ];
+};
+
 struct EpiArgs {
   int kind;
   void* out;          // STORE: T[M, ldo]; SWIGLU: T[M, ldo]; QKV: q rows T[M, d]
@@ -132,11 +148,10 @@ struct EpiArgs {
   EntPart* parts;
   int ntiles;
   // QKV over rows of several sequences: row m writes its K / V row into the cache of
-  // sequence row_seq[m] (k_tab / v_tab hold this layer's cache of each sequence);
-  // row_seq == nullptr: every row uses k_cache / v_cache
+  // sequence row_seq[m] (k_seq / v_seq hold this layer's cache of each sequence, by
+  // value in the kernel arguments); row_seq == nullptr: every row uses k_cache / v_cache
   const int32_t* row_seq;
-  void* const* k_tab;
-  void* const* v_tab;
+  SeqPtrs k_seq, v_seq;
 };
 
 // K / V destination of row m for the QKV epilogues
@@ -147,7 +162,7 @@ __device__ __forceinline__ T* kv_dst(const EpiArgs& e, int m, bool v) {
   const uintptr_t kc = (uintptr_t)e.k_cache, vc = (uintptr_t)e.v_cache;
   if (e.row_seq) {
     const int q = e.row_seq[m];
-    const uintptr_t kt = (uintptr_t)e.k_tab[q], vt = (uintptr_t)e.v_tab[q];
+    const uintptr_t kt = (uintptr_t)e.k_seq.p[q], vt = (uintptr_t)e.v_seq.p[q];
     return (T*)(v ? vt : kt);
   }
   return (T*)(v ? vc : kc);
@@ -167,9 +182,23 @@ ec_status pack_weights(int elem_bytes, int d, int head_dim, int F, const void* w
                        void* gateup_packed, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
+// Sequences of one batched attention launch: sequence i owns query rows [row0, row0 + nr)
+// of the compact q / out arrays and attends over its own cache k, v (all L rows).
+struct AttnSeq {
+  int row0, nr;
+  const void* k;
+  const void* v;
+};
+struct AttnSeqs {
+  AttnSeq s[EC_MAX_SEQ];
+  int n;
+};
 size_t attn_ws_bytes(int r, int L, int H, int D);
 ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, int L, int H, int D,
                float scale, void* out, void* ws, size_t ws_bytes, hipStream_t s);
+// every sequence's rows in one launch (plus one merge launch when the keys are split)
+ec_status attn_batch(ec_dtype dt, const void* q, const AttnSeqs& seqs, int L, int H, int D, float scale, void* out,
+                     void* ws, size_t ws_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------- entropy
 size_t entropy_ws_bytes(int rows, int vocab);
@@ -186,10 +215,10 @@ ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t 
                   void* ws, size_t ws_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------- elementwise
-// h[i] = table[tokens[rows[i]]]; with row_seq, the token array of row i is tok_tab[row_seq[i]]
+// h[i] = table[tokens[rows[i]]]; with row_seq, the token array of row i is tok.p[row_seq[i]]
 ec_status embed(ec_dtype dt, const void* table, int vocab, const int32_t* tokens, int L,
                 const int32_t* rows, int n, int d, float* h, hipStream_t s,
-                const int32_t* const* tok_tab = nullptr, const int32_t* row_seq = nullptr);
+                const SeqPtrs* tok = nullptr, const int32_t* row_seq = nullptr);
 ec_status rmsnorm(ec_dtype dt, const float* h, int n_src, const int32_t* idx, int n, int d,
                   const void* gain, float eps, void* out, hipStream_t s);
 // h[m] += sum_s part[s][m] (s ascending), then out[m] = T(RMSNorm(h[m]) * gain), m < M: the

@@ -32,6 +32,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace ec {
 
 namespace {
@@ -112,11 +114,6 @@ __device__ __forceinline__ void epi_swiglu(const EpiArgs& e, int m, int col, flo
 
 // -------------------------------------------------------------------- block mapping
 constexpr int kGroupM = 4;  // row tiles per group of the tile order
-__device__ __forceinline__ int xcd_remap(int pid, int nblk) {
-  const int per = nblk / 8, rem = nblk % 8;
-  const int x = pid % 8, local = pid / 8;
-  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + local;
-}
 
 // -------------------------------------------------------------------- bf16 MFMA GEMM
 // Packed weight layouts (built once by ec_pack_weights) put the two operands of
@@ -212,8 +209,10 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
 
   // Direct-to-LDS loads through buffer resources (buffer_load_dwordx4 ... lds): the
   // per-lane byte offset of each load is fixed, the K-step advances the scalar
-  // offset. Rows past M / N clamp to the last row (their products land in rows /
-  // columns the epilogue skips); the resource's extent bounds every access.
+  // offset. A rows past M get the offset M*K*2, the end of A's resource: out of range,
+  // so the load returns zeros without a memory access (a skinny product's row tile
+  // then moves only its M real rows). B rows past N clamp to the last row. Products
+  // of such rows land in rows / columns the epilogue skips.
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(A, (int64_t)M * K * 2);
   const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(B, (int64_t)N * K * 2);
   int oa[LPA], ob[LPB];
@@ -221,7 +220,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   for (int i = 0; i < LPA; ++i) {
     const int q = (i * NW + wave) * 64 + lane;
     const int r = q / CPR, c = (q % CPR) ^ ((r >> SWS) & (CPR - 1));
-    oa[i] = (int)(((int64_t)min(m0 + r, M - 1) * K + kbeg + c * 8) * 2);
+    oa[i] = m0 + r < M ? (int)(((int64_t)(m0 + r) * K + kbeg + c * 8) * 2) : (int)((int64_t)M * K * 2);
   }
 #pragma unroll
   for (int i = 0; i < LPB; ++i) {
@@ -293,8 +292,8 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
       pre_pos[i] = epi.rows[m];
       if (epi.row_seq) {
         const int q = epi.row_seq[m];
-        pre_k[i] = (uintptr_t)epi.k_tab[q];
-        pre_v[i] = (uintptr_t)epi.v_tab[q];
+        pre_k[i] = (uintptr_t)epi.k_seq.p[q];
+        pre_v[i] = (uintptr_t)epi.v_seq.p[q];
       } else {
         pre_k[i] = (uintptr_t)epi.k_cache;
         pre_v[i] = (uintptr_t)epi.v_cache;
@@ -645,13 +644,14 @@ pack_rows_kernel(const unsigned char* __restrict__ a, const unsigned char* __res
 // -------------------------------------------------------------------- host-side planning
 constexpr int kCUs = 256;
 
-enum TileCfg { T256x192, T256x128, T128x128, T64x128, kNumTileCfg };
+enum TileCfg { T256x192, T256x128, T128x128, T64x128, T256x96, T128x96, T256x64, T128x64, T256x32, kNumTileCfg };
 struct TileInfo {
   int BM, BN;
   double eff;  // sustained MFMA rate relative to 4 TFLOP/s per CU, measured on MI355X
 };
 constexpr TileInfo kTile[kNumTileCfg] = {
-    {256, 192, 1.10}, {256, 128, 1.10}, {128, 128, 0.80}, {64, 128, 0.45}};
+    {256, 192, 1.10}, {256, 128, 1.10}, {128, 128, 0.80}, {64, 128, 0.45},
+    {256, 96, 0.90}, {128, 96, 0.786}, {256, 64, 0.80}, {128, 64, 0.55}, {256, 32, 0.50}};
 // Sustained global-to-LDS rate of one CU (bytes per microsecond) with the weights streamed
 // from HBM: a tile's staging time is (BM + BN) x K x 2 bytes at this rate.
 constexpr double kCuLoadBytesPerUs = 60e3;
@@ -665,15 +665,21 @@ struct Plan {
 // projection shapes (N x K = 12288 x 4096, 24576 x 4096, 4096 x 4096, 4096 x 12288; rows
 // 17 .. 4096, weights streamed from HBM): time = waves x per-tile time, waves =
 // ceil(tiles * S / 256), per-tile time = the larger of the MFMA time
-// 2 BM BN (K / S) / (eff x 4 TFLOP/s) and the staging time (BM + BN) (K / S) 2 bytes
-// at kCuLoadBytesPerUs, plus, for split K, the partials' round trip (S M N x 8 bytes at
+// 2 BM BN (K / S) / (eff x 4 TFLOP/s) and the staging time (Mr + BN) (K / S) 2 bytes
+// at kCuLoadBytesPerUs (Mr = the tile's rows that exist, min(BM, M rounded up to 32):
+// rows past M are not loaded), plus, for split K, the partials' round trip (S M N x 8 bytes at
 // 3 TB/s) and 6 us for the reduction launch (measured with the K rotation of skinny
 // tiles). Over the measured shapes the choice costs 0.2 % more than the best candidate
 // in total, at most 4 % on a shape but one (17 x 12288 x 4096: 26 %). Larger
 // tiles carry more MFMA work per staged byte; smaller ones
 // and split K fill the 256 CUs at skinny M (skip steps, the LM head over the
-// candidates). Every tile shape and split S in {1, 2, 4, 8} (K chunks of at least
-// 8 steps) is priced and the cheapest taken.
+// candidates). The all-rows tiles (four wavefronts stacked along M over one weight
+// slice of 96, 64 or 32 columns) are priced only at M <= 256: their efficiencies were
+// fitted, with the four older tiles' figures held fixed, to a sweep of every tile and
+// split at M = 17 .. 256 on the four projection shapes (the choices then cost 0.7 % more
+// than the fastest measured candidate in total, against 2.3 % without them). Every tile
+// shape and split S in {1, 2, 4, 8} (K chunks of at least 8 steps) is priced and the
+// cheapest taken.
 Plan plan_bf16(int M, int N, int K, int kind) {
   Plan best{};
   double best_us = 1e300;
@@ -685,6 +691,7 @@ Plan plan_bf16(int M, int N, int K, int kind) {
   const bool ent = kind == EPI_ENTROPY || kind == EPI_STORE;
   for (int c = 0; c < kNumTileCfg; ++c) {
     const TileInfo& t = kTile[c];
+    if (c >= T256x96 && M > 256) continue;  // all-rows tiles: measured at skinny M only
     if (M <= 64 && c != T64x128) continue;
     if ((M <= 128 || ent) && (c == T256x192 || c == T256x128)) continue;
     const int MT = (M + t.BM - 1) / t.BM, NT = (N + t.BN - 1) / t.BN;
@@ -694,7 +701,8 @@ Plan plan_bf16(int M, int N, int K, int kind) {
       const int64_t waves = (tiles * S + kCUs - 1) / kCUs;
       const double kc = (double)K / S;
       const double mfma_us = 2.0 * t.BM * t.BN * kc / (t.eff * 4e6);
-      const double load_us = (double)(t.BM + t.BN) * kc * 2.0 / kCuLoadBytesPerUs;
+      const int rows = std::min(t.BM, (M + 31) / 32 * 32);
+      const double load_us = (double)(rows + t.BN) * kc * 2.0 / kCuLoadBytesPerUs;
       double us = (double)waves * (mfma_us > load_us ? mfma_us : load_us);
       if (S > 1) us += (double)S * M * N * 8.0 / 3e6 + 6.0;
       if (us < best_us) {
@@ -744,6 +752,12 @@ ec_status launch_cfg(const Plan& p, const bf16* A, const bf16* B, int M, int N, 
       case T256x192: return launch_bf16<256, 192, 64, 96, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
       case T256x128: return launch_bf16<256, 128, 64, 64, 3, false, EPI>(p, A, B, M, N, K, epi, part, s);
       case T128x128: return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+      // all-rows tiles of skinny products: four wavefronts stacked along M share one weight slice
+      case T256x96: return launch_bf16<256, 96, 64, 96, 3, false, EPI>(p, A, B, M, N, K, epi, part, s);
+      case T128x96: return launch_bf16<128, 96, 32, 96, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+      case T256x64: return launch_bf16<256, 64, 64, 64, 3, false, EPI>(p, A, B, M, N, K, epi, part, s);
+      case T128x64: return launch_bf16<128, 64, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
+      case T256x32: return launch_bf16<256, 32, 64, 32, 3, false, EPI>(p, A, B, M, N, K, epi, part, s);
       default: return launch_bf16<64, 128, 32, 32, 6, true, EPI>(p, A, B, M, N, K, epi, part, s);
     }
   }

@@ -18,10 +18,10 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads)
 embed_kernel(const T* __restrict__ table, int vocab, const int32_t* __restrict__ tokens, int L,
              const int32_t* __restrict__ rows, int d, float* __restrict__ h,
-             const int32_t* const* __restrict__ tok_tab, const int32_t* __restrict__ row_seq) {
+             const SeqPtrs tok_of, const int32_t* __restrict__ row_seq) {
   const int i = blockIdx.x;
   const int p = rows[i];
-  const int32_t* tk = row_seq ? tok_tab[row_seq[i]] : tokens;
+  const int32_t* tk = row_seq ? (const int32_t*)tok_of.p[row_seq[i]] : tokens;
   const int tok = (p >= 0 && p < L) ? tk[p] : -1;
   float* dst = h + (int64_t)i * d;
   if (tok < 0 || tok >= vocab) {  // invalid position or id: zero row
@@ -229,12 +229,13 @@ ec_status resid_norm_t(const float* part, int S, int M, int d, float* h, const T
 
 ec_status embed(ec_dtype dt, const void* table, int vocab, const int32_t* tokens, int L,
                 const int32_t* rows, int n, int d, float* h, hipStream_t s,
-                const int32_t* const* tok_tab, const int32_t* row_seq) {
+                const SeqPtrs* tok, const int32_t* row_seq) {
+  const SeqPtrs tp = tok ? *tok : SeqPtrs{};
   if (n == 0) return EC_OK;
   if (dt == EC_BF16)
-    embed_kernel<bf16><<<n, kThreads, 0, s>>>((const bf16*)table, vocab, tokens, L, rows, d, h, tok_tab, row_seq);
+    embed_kernel<bf16><<<n, kThreads, 0, s>>>((const bf16*)table, vocab, tokens, L, rows, d, h, tp, row_seq);
   else
-    embed_kernel<float><<<n, kThreads, 0, s>>>((const float*)table, vocab, tokens, L, rows, d, h, tok_tab, row_seq);
+    embed_kernel<float><<<n, kThreads, 0, s>>>((const float*)table, vocab, tokens, L, rows, d, h, tp, row_seq);
   EC_CHECK_LAUNCH("embed_kernel");
   return EC_OK;
 }
