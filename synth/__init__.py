@@ -222,6 +222,24 @@ def make_model(m: ModelShape, seed: int = 0, n_layers: Optional[int] = None,
     return ModelWeights(m, embed, layers, make_final_norm(m), head)
 
 
+def make_hot_token_model(m: ModelShape, seed: int = 0, n_layers: Optional[int] = None, hot_tokens: int = 4,
+                         hot_scale: float = 12.0, hot_seed: int = 0) -> ModelWeights:
+    """A test fixture whose rows have clear top-1 tokens.
+
+    The model is make_model's, except that the LM-head rows of hot_tokens token ids (drawn
+    with hot_seed) are scaled by hot_scale (rounded to bf16 again for bf16 models): every
+    row's largest logits come from those few ids, and its top-1 leads its top-2 by a
+    sizeable fraction of the top-1 logit, far above the rounding of stored logits. The
+    layers are unchanged, so the forward keeps the sensitivity of the plain fixture.
+    """
+    w = make_model(m, seed, n_layers)
+    hot = np.random.default_rng(hot_seed).choice(m.vocab - 1, hot_tokens, replace=False)
+    h = bf16_bits_to_f32(w.lm_head[hot]) if m.dtype == "bf16" else w.lm_head[hot]
+    h = (h * np.float32(hot_scale)).astype(np.float32)
+    w.lm_head[hot] = f32_to_bf16_bits(h) if m.dtype == "bf16" else h
+    return w
+
+
 # --------------------------------------------------------------------------
 # sequences
 # --------------------------------------------------------------------------

@@ -52,8 +52,9 @@ def _check_vs_oracle(outs, recs, cfg, tau, e_tol):
         if not same:
             assert not _gate_ok(r, cfg.tokens_per_step, cfg.model.dtype), f"step {r.t}: decoded differs"
             break
-        assert abs(o.emax - r.emax) <= e_tol, f"step {r.t}: E {o.emax} vs {r.emax}"
-        if abs(float(np.float32(r.emax)) - tau) > e_tol:
+        tol = e_tol(r) if callable(e_tol) else e_tol
+        assert abs(o.emax - r.emax) <= tol, f"step {r.t}: E {o.emax} vs {r.emax}"
+        if abs(float(np.float32(r.emax)) - tau) > tol:
             assert o.refresh_next == r.refresh_next
         compared += 1
     return compared
@@ -90,20 +91,32 @@ def test_batch_tiny_peaked_matches_oracle_and_single():
 
 @pytest.mark.parametrize("tau", [1.0, math.inf])
 def test_batch_small_bf16_first_steps(tau):
-    """Two bf16 sequences of the small config (refresh-only at tau 1, skips at tau inf)."""
+    """Two bf16 sequences of the small model, whole blocks of 16 per step, on the hot-token
+    fixture (every row's top-1 clearly ahead), stepped together (one attention launch per
+    layer over both): each sequence must match its own oracle trajectory on every step up to
+    its first gated one (E within the first-order bound of the single-sequence test), and the
+    first sequence's oracle clears the gates on its first four steps, so at least four
+    steps' decoded positions and ids are compared."""
+    import dataclasses
     from entropy_guided_kv_amd import api
-    cfg = synth.CONFIGS["small"]
-    w = synth.make_model(cfg.model)
+    from tests.test_gpu_step import HOT, _e_tol_perturbation, _first_gated
+    cfg = dataclasses.replace(synth.CONFIGS["small"], tokens_per_step=16, block_len=16)
+    w = synth.make_hot_token_model(cfg.model, **HOT)
     dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
     prompts = _prompts(cfg, 2)
-    steps = 3 if tau == 1.0 else 5
+    steps = 5
     _, seq_outs = _batch_run(dm, cfg, tau, prompts, max_steps=steps)
+    total = 0
     for i, p in enumerate(prompts):
-        recs, _, _ = ol.run_entropycache(om.OracleModel(w), cfg, p, tau, max_steps=steps)
-        # the configs' flat logits leave near ties at the selection cut: the comparison
-        # runs up to the first gated divergence (as for ec_step alone)
-        _check_vs_oracle(seq_outs[i], recs, cfg, tau, 2e-2)
-        assert seq_outs[i][0].refreshed and abs(seq_outs[i][0].emax - recs[0].emax) <= 2e-2
+        recs, _, _ = ol.run_entropycache(om.OracleModel(w), cfg, p, tau, max_steps=steps, keep_logits=True)
+        first = _first_gated(recs, cfg.tokens_per_step, "bf16")
+        compared = _check_vs_oracle(seq_outs[i], recs, cfg, tau, _e_tol_perturbation)
+        assert compared >= first
+        if i == 0:
+            assert first >= 4
+        total += compared
+        assert seq_outs[i][0].refreshed
+    assert total >= 4
 
 
 def test_batch_sixteen_sequences_tiny():
