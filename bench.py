@@ -321,32 +321,7 @@ def _entropy_kernel_bench(iters=50):
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
-def cpu_baseline(cfg, host, prompt, n_layers_sample: int):
-    """Time the oracle's refresh step on the host cores with a bounded sample.
-
-    The sample: one refresh step (all L rows) of the model cut to its first
-    n_layers_sample layers, and the same step with no layers (embedding, final
-    norm, LM head over the candidates, entropy, selection). The per-step time
-    of the full model is estimated as T0 + (T1 - T0) * n_layers / n_sample.
-    """
-    import numpy as np
-    import synth
-    from oracle import loop as ol
-    from oracle import model as om
-
-    def run(nl):
-        w = synth.ModelWeights(cfg.model, host["embed"], host["layers"][:nl], host["final_norm"],
-                               host["lm_head"])
-        mdl = om.OracleModel(w, keep_f64=False)
-        st = ol.init_state(cfg, prompt)
-        cache = om.new_cache(mdl, cfg.seq_len)
-        t0 = time.perf_counter()
-        ol.step(mdl, cfg, st, cache, cfg.tau)
-        return time.perf_counter() - t0
-
-    t0 = run(0)
-    t1 = run(n_layers_sample)
-    per_step = t0 + (t1 - t0) * cfg.model.n_layers / n_layers_sample
+def _host_cores():
     threads = None
     try:
         import threadpoolctl
@@ -354,14 +329,128 @@ def cpu_baseline(cfg, host, prompt, n_layers_sample: int):
         threads = max((i.get("num_threads", 0) for i in info), default=None)
     except Exception:
         pass
-    cores = threads or len(os.sched_getaffinity(0))
+    return threads or len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, host, prompt):
+    """The oracle as it stands, on the host cores, over a bounded window of the 8B workload:
+    one refresh step (all L rows, 32 layers) and the two skip steps that follow it at
+    tau = +inf (r = 256 recomputed rows each), float64 numpy. `value` is the refresh-step
+    rate, the step the headline workload takes every time (its E exceeds tau); the skip
+    steps' times are reported beside it."""
+    import numpy as np
+    import synth
+    from oracle import loop as ol
+    from oracle import model as om
+
+    w = synth.ModelWeights(cfg.model, host["embed"], host["layers"], host["final_norm"], host["lm_head"])
+    mdl = om.OracleModel(w, keep_f64=False)
+    st = ol.init_state(cfg, prompt)
+    cache = om.new_cache(mdl, cfg.seq_len)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        r = ol.step(mdl, cfg, st, cache, math.inf)
+        times.append((time.perf_counter() - t0, len(r.rows), bool(r.refreshed)))
+        log(f"[bench] oracle step: {times[-1][0]:.1f}s, {times[-1][1]} rows, refresh={times[-1][2]}")
+    t_full = times[0][0]
+    t_skip = sum(t for t, _, _ in times[1:]) / 2
     return {
-        "value": 1.0 / per_step, "unit": "steps/s", "cores": cores, "kind": "oracle",
-        "sample": (f"one refresh step (L={cfg.seq_len}) with {n_layers_sample} of "
-                   f"{cfg.model.n_layers} layers ({t1:.1f}s) and with 0 layers ({t0:.1f}s); "
-                   f"per-step time scaled linearly in layers to {per_step:.1f}s; float64 numpy"),
+        "value": 1.0 / t_full, "unit": "steps/s", "cores": _host_cores(), "kind": "oracle",
+        "precision": "float64 (numpy, bf16 rounding points mirrored)",
+        "sample": (f"8B-shaped model, all 32 layers: 1 refresh step (L={cfg.seq_len} rows, {t_full:.1f}s) "
+                   f"and the 2 skip steps after it at tau=+inf ({times[1][1]} and {times[2][1]} rows, "
+                   f"{times[1][0]:.1f}s and {times[2][0]:.1f}s); value = refresh steps/s"),
+        "refresh_step_s": t_full, "skip_step_s": t_skip, "skip_steps_per_s": 1.0 / t_skip,
         "host_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+# ------------------------------------------------------------------ small configurations
+def small_configs_bench(with_oracle: bool):
+    """The tiny (fp32) and small (bf16) configurations: one whole decode each at the
+    configured tau (after a warmup decode), and the oracle's whole decode of the same
+    inputs timed on the host beside it."""
+    import torch
+    import synth
+    from entropy_guided_kv_amd import api
+    from oracle import loop as ol
+    from oracle import model as om
+    res = {}
+    for name in ("tiny", "small"):
+        cfg = synth.CONFIGS[name]
+        w = synth.make_model(cfg.model)
+        dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+        dec = api.Decoder(dm, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len,
+                          cfg.k_recent, cfg.tau)
+        prompt_np = synth.make_prompt(cfg)
+        prompt = torch.from_numpy(prompt_np)
+        run_trajectory(dec, prompt)
+        outs, wall, _ = run_trajectory(dec, prompt)
+        r = {"workload": f"{name}: {cfg.model.n_layers} layers, d={cfg.model.d_model}, V={cfg.model.vocab}, "
+                         f"{cfg.model.dtype}, L={cfg.seq_len} = {cfg.prompt_len} + {cfg.n_masked}, "
+                         f"{cfg.tokens_per_step} token(s)/step, k={cfg.k_recent}, tau={cfg.tau}",
+             "steps": len(outs), "steps_per_s": len(outs) / wall,
+             "gen_tokens_per_s": sum(len(o.positions) for o in outs) / wall,
+             "refresh_rate": sum(o.refreshed for o in outs) / len(outs)}
+        if with_oracle:
+            t0 = time.perf_counter()
+            recs, _, _ = ol.run_entropycache(om.OracleModel(w), cfg, prompt_np, cfg.tau)
+            t = time.perf_counter() - t0
+            r["oracle"] = {"steps": len(recs), "seconds": t, "steps_per_s": len(recs) / t,
+                           "cores": _host_cores(), "precision": "float64 numpy"}
+        log(f"[bench] {name}: {r['steps_per_s']:.1f} steps/s" +
+            (f", oracle {r['oracle']['steps_per_s']:.2f} steps/s" if with_oracle else ""))
+        res[name] = r
+        del dec, dm
+        torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ mixed refresh rate
+def _model_with_head(dm, head):
+    """The same device model with another LM head (the layers are shared)."""
+    import ctypes as C
+    from types import SimpleNamespace
+    desc = type(dm.desc).from_buffer_copy(dm.desc)
+    desc.lm_head = head.data_ptr()
+    return SimpleNamespace(desc=desc, device=dm.device, shape=dm.shape, layers=dm.layers,
+                           torch_dtype=dm.torch_dtype, _keep=(dm, head, C))
+
+
+def mixed_refresh_bench(dm, cfg, host, prompt, t_full_s, t_skip_s, taus=(1.0, 2.0)):
+    """The 8B workload on the hot-token LM head (synth.make_hot_token_model's head: a few
+    token ids' rows scaled up, every other weight as configured): decoded rows' entropies
+    then spread from near 0 to near ln V, so at tau = 1 and 2 the refresh rate rho lies
+    strictly between 0 and 1. Reported with the rate the refresh and skip step times of the
+    plain runs predict, 1 / (rho T_full + (1 - rho) T_skip)."""
+    import numpy as np
+    import torch
+    import synth
+    from entropy_guided_kv_amd import api
+    m = cfg.model
+    hot = np.random.default_rng(0).choice(m.vocab - 1, 8, replace=False)
+    head_np = host["lm_head"].copy()
+    head_np[hot] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(head_np[hot]) * np.float32(10.0))
+    head = api._to_device(head_np, m.dtype, "cuda")
+    view = _model_with_head(dm, head)
+    res = {"workload": "8B-shaped bf16, L=1024 = 768 + 256, blocks of 32, 1 token/step, k=16; LM head with "
+                       "8 hot token rows x10 (other weights as configured)"}
+    for tau in taus:
+        dec = api.Decoder(view, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len, cfg.k_recent, tau)
+        run_trajectory(dec, prompt, steps=8)
+        outs, wall, _ = run_trajectory(dec, prompt)
+        rho = sum(o.refreshed for o in outs) / len(outs)
+        pred = 1.0 / (rho * t_full_s + (1 - rho) * t_skip_s)
+        res[f"tau={tau}"] = {"steps": len(outs), "steps_per_s": len(outs) / wall, "refresh_rate": rho,
+                             "mean_rows": sum(o.rows for o in outs) / len(outs),
+                             "predicted_steps_per_s": pred, "T_full_ms": t_full_s * 1e3, "T_skip_ms": t_skip_s * 1e3}
+        log(f"[bench] hot-token head tau={tau}: {len(outs) / wall:.1f} steps/s at refresh rate {rho:.3f} "
+            f"(predicted {pred:.1f})")
+        del dec
+    del view, head
+    torch.cuda.empty_cache()
+    return res
 
 
 # ------------------------------------------------------------------ main
@@ -372,7 +461,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=16, help="untimed steps before timing")
     ap.add_argument("--no-sweep", action="store_true", help="skip the tau sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-layers", type=int, default=2, help="layers in the CPU oracle sample")
+    ap.add_argument("--no-small", action="store_true", help="skip the tiny / small configuration runs")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel event timing (and the roofline object)")
     ap.add_argument("--breakdown", choices=("refresh", "both"), default="both",
@@ -419,7 +508,7 @@ def main():
     tau = 1.0
     prompt_np = synth.make_prompt(cfg)
     prompt = torch.from_numpy(prompt_np)
-    keep = 0 if args.no_cpu else args.cpu_layers
+    keep = 0 if args.no_cpu else m.n_layers
     dm, host = upload_model(cfg, keep)
     dec = api.Decoder(dm, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len,
                       cfg.k_recent, tau)
@@ -504,13 +593,25 @@ def main():
         log(f"[bench] entropy kernel 64x126464: warm {ent['warm']['us_per_call']:.1f} us, "
             f"cold {ent['cold']['us_per_call']:.1f} us")
 
+    mixed = None
+    if not args.no_sweep and "inf" in sweep:
+        t_full = wall / args.steps  # every headline step refreshes
+        inf = sweep["inf"]
+        t_skip = (inf["steps"] / inf["steps_per_s"] - t_full) / max(inf["steps"] - 1, 1)
+        mixed = mixed_refresh_bench(dm, cfg, host, prompt, t_full, t_skip)
+
+    small = None
+    if not args.no_small:
+        small = small_configs_bench(with_oracle=not args.no_cpu)
+
     cpu = None
     if not args.no_cpu:
-        log("[bench] CPU oracle baseline ...")
-        cpu = cpu_baseline(cfg, host, prompt_np, args.cpu_layers)
-        log(f"[bench] CPU oracle: {cpu['value']:.4f} steps/s on {cpu['cores']} threads")
+        log("[bench] CPU oracle baseline (1 refresh + 2 skip steps of the 8B model) ...")
+        cpu = cpu_baseline(cfg, host, prompt_np)
+        log(f"[bench] CPU oracle: {cpu['value']:.4f} refresh steps/s, {cpu['skip_steps_per_s']:.4f} skip steps/s "
+            f"on {cpu['cores']} threads")
     emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, sweep, roofline, kernels,
-         ent, cpu, long_res, drift_res)
+         ent, cpu, long_res, drift_res, mixed, small)
 
 
 def roofline_object(dom, dk):
@@ -563,7 +664,7 @@ def breakdown_report(dec, prompt, with_skip=True):
 
 
 def emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, sweep, roofline,
-         kernels, ent, cpu, long_res=None, drift_res=None):
+         kernels, ent, cpu, long_res=None, drift_res=None, mixed=None, small=None):
     res = {
         "metric": METRIC,
         "value": steps_s,
@@ -591,6 +692,8 @@ def emit(args, cfg, tau, steps_s, wall, tokens, refresh_rate, roof_s, ev_ms, swe
         "entropy_kernel_64x126464": ent,
         "long_context_batch4": long_res,
         "kv_drift_probe": drift_res,
+        "mixed_refresh_rate": mixed,
+        "small_configs": small,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
