@@ -644,14 +644,17 @@ pack_rows_kernel(const unsigned char* __restrict__ a, const unsigned char* __res
 // -------------------------------------------------------------------- host-side planning
 constexpr int kCUs = 256;
 
-enum TileCfg { T256x192, T256x128, T128x128, T64x128, T256x96, T128x96, T256x64, T128x64, T256x32, kNumTileCfg };
+enum TileCfg {
+  T256x192, T256x128, T128x128, T64x128, T256x96, T128x96, T256x64, T128x64, T256x32, T64x96, T64x64, kNumTileCfg
+};
 struct TileInfo {
   int BM, BN;
   double eff;  // sustained MFMA rate relative to 4 TFLOP/s per CU, measured on MI355X
 };
 constexpr TileInfo kTile[kNumTileCfg] = {
     {256, 192, 1.10}, {256, 128, 1.10}, {128, 128, 0.80}, {64, 128, 0.45},
-    {256, 96, 0.90}, {128, 96, 0.786}, {256, 64, 0.80}, {128, 64, 0.55}, {256, 32, 0.50}};
+    {256, 96, 0.90}, {128, 96, 0.786}, {256, 64, 0.80}, {128, 64, 0.55}, {256, 32, 0.50},
+    {64, 96, 0.377}, {64, 64, 0.311}};
 // Sustained global-to-LDS rate of one CU (bytes per microsecond) with the weights streamed
 // from HBM: a tile's staging time is (BM + BN) x K x 2 bytes at this rate.
 constexpr double kCuLoadBytesPerUs = 60e3;
@@ -677,7 +680,9 @@ struct Plan {
 // slice of 96, 64 or 32 columns) are priced only at M <= 256: their efficiencies were
 // fitted, with the four older tiles' figures held fixed, to a sweep of every tile and
 // split at M = 17 .. 256 on the four projection shapes (the choices then cost 0.7 % more
-// than the fastest measured candidate in total, against 2.3 % without them). Every tile
+// than the fastest measured candidate in total, against 2.3 % without them). The 64-row
+// tiles with 96 or 64 columns cut the projections into about 256 workgroups at M <= 64;
+// their efficiencies were fitted the same way to a second sweep at M = 17 .. 128. Every tile
 // shape and split S in {1, 2, 4, 8} (K chunks of at least 8 steps) is priced and the
 // cheapest taken.
 Plan plan_bf16(int M, int N, int K, int kind) {
@@ -691,9 +696,10 @@ Plan plan_bf16(int M, int N, int K, int kind) {
   const bool ent = kind == EPI_ENTROPY || kind == EPI_STORE;
   for (int c = 0; c < kNumTileCfg; ++c) {
     const TileInfo& t = kTile[c];
+    if (ent && c != T128x128 && c != T64x128) continue;  // the only tiles launch_cfg has for them
     if (c >= T256x96 && M > 256) continue;  // all-rows tiles: measured at skinny M only
-    if (M <= 64 && c != T64x128) continue;
-    if ((M <= 128 || ent) && (c == T256x192 || c == T256x128)) continue;
+    if (M <= 64 && c != T64x128 && c != T64x96 && c != T64x64) continue;
+    if (M <= 128 && (c == T256x192 || c == T256x128)) continue;
     const int MT = (M + t.BM - 1) / t.BM, NT = (N + t.BN - 1) / t.BN;
     const int64_t tiles = (int64_t)MT * NT;
     for (int S = 1; S <= (ent ? 1 : 8); S *= 2) {
@@ -758,6 +764,9 @@ ec_status launch_cfg(const Plan& p, const bf16* A, const bf16* B, int M, int N, 
       case T256x64: return launch_bf16<256, 64, 64, 64, 3, false, EPI>(p, A, B, M, N, K, epi, part, s);
       case T128x64: return launch_bf16<128, 64, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
       case T256x32: return launch_bf16<256, 32, 64, 32, 3, false, EPI>(p, A, B, M, N, K, epi, part, s);
+      // skinny tiles that cut the projections into 256 workgroups at small M
+      case T64x96: return launch_bf16<64, 96, 32, 96, 6, true, EPI>(p, A, B, M, N, K, epi, part, s);
+      case T64x64: return launch_bf16<64, 64, 32, 32, 6, true, EPI>(p, A, B, M, N, K, epi, part, s);
       default: return launch_bf16<64, 128, 32, 32, 6, true, EPI>(p, A, B, M, N, K, epi, part, s);
     }
   }

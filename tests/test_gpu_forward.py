@@ -102,12 +102,18 @@ def test_forward_tiny_f32(kind):
     _compare(shape, omm, dm, cache, oc, tokens, rows, rows[-5:] if kind == "partial" else np.arange(96, 128))
 
 
-@pytest.mark.parametrize("kind", ["full", "partial", "single"])
+@pytest.mark.parametrize("kind", ["full", "partial", "single", "many_out"])
 def test_forward_mini_bf16(kind):
+    """"many_out": logits of 200 rows, an LM head product (200 x 1024 x 256) that the GEMM
+    planner must not give a tile without the stored-logits epilogue."""
     shape, L = MINI_BF16, 320
-    w, omm, dm, cache, oc = _setup(shape, L, seed=2, stale=(kind != "full"))
+    w, omm, dm, cache, oc = _setup(shape, L, seed=2, stale=(kind not in ("full", "many_out")))
     rng = np.random.default_rng(4)
     tokens = rng.integers(0, shape.vocab - 1, L).astype(np.int32)
+    if kind == "many_out":
+        rows = np.arange(L)
+        _compare(shape, omm, dm, cache, oc, tokens, rows, np.sort(rng.choice(L, 200, replace=False)))
+        return
     if kind == "full":
         rows = np.arange(L)
     elif kind == "partial":

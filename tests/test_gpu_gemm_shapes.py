@@ -6,10 +6,12 @@ stays fast. The row counts pick every tile configuration and split width the
 GEMM planner uses on these shapes: 1024 rows (a refresh: 256x192 tiles for
 q|k|v and gate/up, 128x128 for the output projection, 256x128 with two K
 splits for down, reduced together with the next RMSNorm), 300 rows (256x128
-q|k|v, 64x128 output projection, down in four splits), 144 rows (128x128 q|k|v,
-output projection in four splits, down in eight), 40 and 17 rows (64x128 tiles,
-q|k|v in two and eight splits) and 1 row (gate/up in four splits: the split-K
-SwiGLU epilogue). Bars as in the other forward tests: 2e-2 relative per row for
+q|k|v, output projection in two splits, down in four), 144 rows (all-rows
+128x96 q|k|v and 256x96 gate/up, output projection in four splits, down in
+eight), 48 rows (64x96 q|k|v in two splits, 64x64 output projection in four,
+64x96 gate/up), 40 and 17 rows (64x128 output projection and down in eight
+splits) and 1 row (q|k|v in eight splits as well).
+Bars as in the other forward tests: 2e-2 relative per row for
 hidden states, logits and the recomputed K/V rows, every other cache row
 bit-identical, argmax exact where the logit margin clears the id gate.
 
@@ -28,7 +30,7 @@ pytestmark = pytest.mark.gpu
 WIDE = synth.ModelShape("wide", "bf16", 1, 4096, 32, 128, 12288, 1024)
 
 
-@pytest.mark.parametrize("n_rows", [1024, 300, 144, 40, 17, 1])
+@pytest.mark.parametrize("n_rows", [1024, 300, 144, 48, 40, 17, 1])
 def test_forward_at_8b_layer_width(n_rows):
     L = 1024
     w, omm, dm, cache, oc = _setup(WIDE, L, seed=11, stale=n_rows < L)

@@ -271,13 +271,20 @@ def test_determinism_two_runs_bit_identical():
     assert all(torch.equal(a, b) for a, b in zip(res[0][2], res[1][2]))
 
 
-@pytest.mark.parametrize("n_cand_rows", ["small"])
+MINI256 = synth.DecodeConfig("mini256", synth.ModelShape("mini", "bf16", 2, 256, 2, 128, 512, 1024),
+                             64, 256, 8, 256, 8, (math.inf,))
+
+
+@pytest.mark.parametrize("n_cand_rows", ["small", "mini256"])
 def test_fused_lm_head_entropy_matches_stored_logits(n_cand_rows):
     """bf16 ec_step reduces the LM head's logits in the GEMM epilogue (no logits tensor).
     Its first step must match ec_forward's stored logits reduced by ec_entropy_max: same
-    picked positions and ids, entropy within 1e-5 nats, confidence within 1e-5 relative."""
+    picked positions and ids, entropy within 1e-5 nats, confidence within 1e-5 relative.
+    "small": 128 candidate rows of the small model; "mini256": 256 candidate rows of a
+    d = 256, V = 1024 model, a product the GEMM planner would price for tiles that have no
+    entropy epilogue (it must plan only the 128x128 or 64x128 tile for these)."""
     from entropy_guided_kv_amd import api
-    cfg = synth.CONFIGS["small"]
+    cfg = synth.CONFIGS["small"] if n_cand_rows == "small" else MINI256
     w = synth.make_model(cfg.model, n_layers=2)
     dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
     prompt = synth.make_prompt(cfg)
