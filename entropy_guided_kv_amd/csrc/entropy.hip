@@ -24,6 +24,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 namespace ec {
 
@@ -125,30 +126,31 @@ entropy_merge_kernel(const Part* __restrict__ parts, int splits, float* __restri
 }
 
 // ---------------------------------------------------------------- single-launch reduction
-// ec_entropy_max in one launch. Workgroup b handles slice split = b / rows of row
-// row = b % rows (S slices per row), so the slices of every row are dispatched in
-// split order and the last slice of each row comes after every other workgroup but
-// the last slices of other rows. A workgroup reduces its slice (every element read
-// once, loads of a pass issued before their use, one exp2 per element against the
-// running maximum of its lane, lanes and wavefronts merged along a fixed order).
-// Slices 0 .. S-2 publish their partial state as four 64-bit words {call tag, value}
-// written with device-scope atomic stores; the last slice of the row (the merger)
-// polls them with device-scope atomic loads until every word carries the call's tag,
-// merges the S states in slice order and writes the row's entropy, argmax and
-// confidence. No word can be read before it is written in this call (the tag is new
-// for every call) and no fence is needed (each word carries its own tag). The merger
-// clears the tags it consumed, so a replay of the same launch with the same tag (a
-// captured graph) cannot read last replay's words. When E is requested every merger
-// publishes its row's entropy the same way and the last workgroup of the grid (the
-// merger of the last row) waits for all of them, takes the maximum over the selected
-// rows and clears those tags. Every workgroup a wait depends on was dispatched
-// before the waiting one and never waits itself; each wait is also bounded (after
-// kSpinLimit polls the row reads as NaN).
+// ec_entropy_max in one launch. Workgroup b reduces slice split = b / rows of row
+// row = b % rows (S slices per row, S = 1 when there are enough rows to cover the CUs):
+// every element is read once, the loads of a pass are issued before their use, each
+// element takes one exp2 against its lane's running maximum, and lanes and wavefronts
+// merge along a fixed order.
+//
+// S > 1: every workgroup but the last publishes its state as four 64-bit words
+// {call tag, value} (device-scope atomic stores). The last workgroup of the grid polls
+// all of them with device-scope atomic loads until every word carries the call's tag,
+// merges each row's states in slice order, writes the rows' entropy, argmax and
+// confidence, and takes E over the selected rows: one cross-workgroup hop per call.
+// S = 1: each workgroup writes its own row; with E requested it publishes the row's
+// entropy as one tagged word and the last workgroup waits for all of them.
+// No word can be read before it is written in this call (the tag is new for every
+// call) and no fence is needed (each word carries its own tag). The last workgroup
+// clears every tag it consumed, so a replay of the same launch with the same tag (a
+// captured graph) cannot read last replay's words. It was dispatched after every
+// workgroup it waits for, which never wait themselves; each wait is also bounded
+// (after kSpinLimit polls the rows concerned read as NaN).
 constexpr int kFThreads = 512;
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kFU = 8;                 // 16-byte vectors per lane per pass
 constexpr int kSpinLimit = 1 << 22;    // polls before a wait gives up (far beyond any normal wait)
 constexpr int kMaxSplits = 256;
+constexpr int kMaxStates = 512;        // rows x S when S > 1 (S > 1 only below 256 rows)
 
 __device__ __forceinline__ void tag_store(uint64_t* p, uint32_t tag, uint32_t v) {
   __hip_atomic_store(p, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -174,23 +176,67 @@ __device__ __forceinline__ bool tag_wait(uint64_t* p, uint32_t tag, uint32_t* v)
   return false;
 }
 
-__device__ __forceinline__ Part shfl_part(const Part& a, int o) {
-  Part b;
-  b.m = __shfl_xor(a.m, o);
-  b.z = __shfl_xor(a.z, o);
-  b.s = __shfl_xor(a.s, o);
-  b.idx = __shfl_xor(a.idx, o);
-  b.nan = __shfl_xor(a.nan, o);
-  return b;
+// Wavefront reductions: a butterfly inside each row of 16 lanes (DPP quad permutes, then
+// the half-row and row mirrors: every lane of a row ends with the row's total), then the
+// four row totals read from lanes 0, 16, 32, 48 and combined in that order. Results are
+// uniform over the wavefront and independent of timing.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  if constexpr (sizeof(T) == 4 && std::is_same<T, float>::value) {
+    v = op(v, dpp_f<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+    v = op(v, dpp_f<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+    v = op(v, dpp_f<0x141>(v));  // row_half_mirror
+    v = op(v, dpp_f<0x140>(v));  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return op(op(r0, r1), op(r2, r3));
+  } else {
+    v = op(v, dpp_i<0xB1>(v));
+    v = op(v, dpp_i<0x4E>(v));
+    v = op(v, dpp_i<0x141>(v));
+    v = op(v, dpp_i<0x140>(v));
+    const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return op(op(r0, r1), op(r2, r3));
+  }
 }
 
-// online update of a lane's state (m, z, s2, idx) by the values x[0..NV) at indices
-// j0[k] + e (increasing in k then e); -inf entries are empty. A NaN value is skipped by
-// the maximum and turns z into NaN through its exponential; only a pass with no finite
-// value is scanned for NaN explicitly.
+// The wavefront's lane states (m, z, s2 in log2 units against the lane's own m, first
+// index of m, NaN flag) -> one state: the largest m, z and s2 rescaled to it and summed,
+// the smallest index among the lanes holding that m. Empty lanes have m = -inf.
+__device__ __forceinline__ void wave_state(float m, float z, float s2, int idx, int nan, float& M, float& Z,
+                                           float& S2, int& I, int& N) {
+  M = wave_reduce(m, [](float a, float b) { return fmaxf(a, b); });
+  float zz = 0.f, ss = 0.f;
+  if (m != kNegInf) {  // then M is finite too
+    const float d = (m - M) * kLog2e, f = __builtin_amdgcn_exp2f(d);
+    zz = z * f;
+    ss = (s2 + d * z) * f;
+  }
+  const auto add = [](float a, float b) { return a + b; };
+  Z = wave_reduce(zz, add);
+  S2 = wave_reduce(ss, add);
+  I = wave_reduce(m == M ? idx : 0x7fffffff, [](int a, int b) { return a < b ? a : b; });
+  N = wave_reduce(nan, [](int a, int b) { return a | b; });
+}
+
+// online update of a lane's state (m, z, s2, idx) by one pass of NV values: x[q] is
+// element blk + ((q / E) kFThreads + tid) E + q % E (increasing in q); -inf entries are
+// empty. A NaN value is skipped by the maximum and turns z into NaN through its
+// exponential; only a pass with no finite value is scanned for NaN explicitly.
 template <int NV, int E>
-__device__ __forceinline__ void lane_update(const float* x, const int* j0, float& m, float& z, float& s2, int& idx,
-                                            int& has_nan) {
+__device__ __forceinline__ void lane_update(const float* x, int blk, int tid, float& m, float& z, float& s2,
+                                            int& idx, int& has_nan) {
   float cm = kNegInf;
 #pragma unroll
   for (int q = 0; q < NV; ++q) cm = fmaxf(cm, x[q]);
@@ -199,9 +245,10 @@ __device__ __forceinline__ void lane_update(const float* x, const int* j0, float
     for (int q = 0; q < NV; ++q) has_nan |= x[q] != x[q];
   }
   if (cm > m) {  // a strictly larger maximum moves idx to its first occurrence in this pass
+    int qi = 0;
 #pragma unroll
-    for (int q = NV - 1; q >= 0; --q)
-      if (x[q] == cm) idx = j0[q / E] + q % E;
+    for (int q = NV - 1; q >= 0; --q) qi = x[q] == cm ? q : qi;
+    idx = blk + ((qi / E) * kFThreads + tid) * E + qi % E;
     if (m != kNegInf) {  // rescale the sums to the new maximum
       const float dl = (m - cm) * kLog2e, f = __builtin_amdgcn_exp2f(dl);
       s2 = (s2 + dl * z) * f;
@@ -211,88 +258,134 @@ __device__ __forceinline__ void lane_update(const float* x, const int* j0, float
   }
   if (m != kNegInf) {
     const float mb = m * kLog2e;
+    float t[NV], e[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) t[q] = fmaf(x[q], kLog2e, -mb);
+#pragma unroll
+    for (int q = 0; q < NV; ++q) e[q] = __builtin_amdgcn_exp2f(t[q]);
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
-      const float t = fmaf(x[q], kLog2e, -mb);
-      const float e = __builtin_amdgcn_exp2f(t);
-      z += e;
-      s2 = fmaf(fmaxf(t, -1000.f), e, s2);  // -inf logit: -1000 * 0 = 0
+      z += e[q];
+      s2 = fmaf(fmaxf(t[q], -1000.f), e[q], s2);  // -inf logit: -1000 * 0 = 0
     }
   }
 }
 
+// one pass of whole vectors at blk: FULL = every vector of the pass lies below hiv (no
+// masking); otherwise vectors at or past hiv re-read the slice's first vector (so every
+// load is issued unconditionally) and are masked to -inf
+template <typename T, bool FULL>
+__device__ __forceinline__ void vec_pass(const T* __restrict__ base, int blk, int lo, int hiv, int tid, float& m,
+                                         float& z, float& s2, int& idx, int& has_nan) {
+  constexpr int E = Vec<T>::E;
+  v4u u[kFU];
+#pragma unroll
+  for (int k = 0; k < kFU; ++k) {
+    const int j = blk + (k * kFThreads + tid) * E;
+    u[k] = *reinterpret_cast<const v4u*>(base + (FULL || j < hiv ? j : lo));
+  }
+  float x[kFU * E];
+#pragma unroll
+  for (int k = 0; k < kFU; ++k) {
+    Vec<T>::unpack(u[k], x + k * E);
+    if (!FULL && blk + (k * kFThreads + tid) * E >= hiv) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[k * E + e] = kNegInf;
+    }
+  }
+  // two halves, so that the first half's arithmetic runs while the second half's loads
+  // are still in flight
+  constexpr int H = kFU / 2;
+  lane_update<H * E, E>(x, blk, tid, m, z, s2, idx, has_nan);
+  lane_update<H * E, E>(x + H * E, blk + H * kFThreads * E, tid, m, z, s2, idx, has_nan);
+}
+
 // partial state of elements [lo, hi) of one row over the workgroup (valid in thread 0).
-// Whole vectors [lo, hiv): every load of a pass is issued unconditionally (vectors past
-// hiv re-read the slice's first vector and are masked to -inf), so the loads of a pass
-// are in flight together; the < E elements of a ragged end [hiv, hi) follow one per
-// thread.
+// Whole vectors [lo, hiv) go through vec_pass; the < E elements of a ragged end [hiv, hi)
+// (or every element, when the row is not 16-byte aligned) follow one per thread.
 template <typename T, bool VEC>
 __device__ Part slice_state(const T* __restrict__ base, int lo, int hi, Part* red) {
   constexpr int E = Vec<T>::E;
-  constexpr int NV = kFU * E;
+  constexpr int P = kFThreads * kFU * E;  // elements per pass
   const int tid = threadIdx.x;
   float m = kNegInf, z = 0.f, s2 = 0.f;  // s2 = sum (x - m) log2(e) e^(x - m), against this lane's m
   int idx = 0x7fffffff, has_nan = 0;
-  const int hiv = VEC ? lo + ((hi - lo) / E) * E : hi;
-  for (int blk = lo; blk < hiv; blk += kFThreads * NV) {
-    float x[NV];
-    int j0[kFU];
-#pragma unroll
-    for (int k = 0; k < kFU; ++k) j0[k] = blk + (k * kFThreads + tid) * E;
-    if (VEC) {
-      v4u u[kFU];
-#pragma unroll
-      for (int k = 0; k < kFU; ++k) u[k] = *reinterpret_cast<const v4u*>(base + (j0[k] < hiv ? j0[k] : lo));
-#pragma unroll
-      for (int k = 0; k < kFU; ++k) {
-        Vec<T>::unpack(u[k], x + k * E);
-        if (j0[k] >= hiv) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) x[k * E + e] = kNegInf;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kFU; ++k)
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int j = j0[k] + e;
-          const float v = to_f(base[j < hiv ? j : lo]);
-          x[k * E + e] = j < hiv ? v : kNegInf;
-        }
+  int hiv = lo;
+  if (VEC) {
+    hiv = lo + ((hi - lo) / E) * E;
+    for (int blk = lo; blk < hiv; blk += P) {
+      if (blk + P <= hiv) vec_pass<T, true>(base, blk, lo, hiv, tid, m, z, s2, idx, has_nan);
+      else vec_pass<T, false>(base, blk, lo, hiv, tid, m, z, s2, idx, has_nan);
     }
-    // two halves, so that the first half's arithmetic runs while the second half's loads
-    // are still in flight
-    lane_update<NV / 2, E>(x, j0, m, z, s2, idx, has_nan);
-    lane_update<NV / 2, E>(x + NV / 2, j0 + kFU / 2, m, z, s2, idx, has_nan);
   }
-  if (VEC && hiv < hi && tid < hi - hiv) {  // ragged end: one element per thread
-    const int j0t[1] = {hiv + tid};
-    const float xt[1] = {to_f(base[hiv + tid])};
-    lane_update<1, 1>(xt, j0t, m, z, s2, idx, has_nan);
+  for (int j = hiv + tid; j < hi; j += kFThreads) {  // one element per thread
+    const float xt[1] = {to_f(base[j])};
+    lane_update<1, 1>(xt, j, 0, m, z, s2, idx, has_nan);
   }
+  // lanes, then wavefronts (wavefront 0 reduces the kFWaves wavefront states the same way);
   // a NaN among finite values has reached z through its exponential
-  Part p{m, z, s2 * kLn2, idx, has_nan | (z != z), {0, 0, 0}};
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {  // symmetric merge: every lane ends with the same state
-    const Part q = shfl_part(p, o);
-    part_merge(p, q);
-  }
-  if ((tid & 63) == 0) red[tid >> 6] = p;
+  float M, Z, S2;
+  int I, N;
+  wave_state(m, z, s2, idx, has_nan | (z != z), M, Z, S2, I, N);
+  if ((tid & 63) == 0) red[tid >> 6] = Part{M, Z, S2, I, N, {0, 0, 0}};
   __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < kFWaves; ++w) part_merge(p, red[w]);
+  Part p{kNegInf, 0.f, 0.f, 0x7fffffff, 0, {0, 0, 0}};
+  if (tid < 64) {
+    const Part w = tid < kFWaves ? red[tid] : Part{kNegInf, 0.f, 0.f, 0x7fffffff, 0, {0, 0, 0}};
+    wave_state(w.m, w.z, w.s, w.idx, w.nan, M, Z, S2, I, N);
+    p = Part{M, Z, S2 * kLn2, I, N, {0, 0, 0}};
   }
   return p;
 }
 
-__device__ __forceinline__ void write_row(const Part& a, int row, float* H, int32_t* amax, float* conf, float* h_out) {
-  const bool bad = a.nan || a.m == kNegInf;
-  const float h = bad ? NAN : __logf(a.z) - a.s / a.z;
+__device__ __forceinline__ float row_entropy(const Part& a) {
+  return a.nan || a.m == kNegInf ? NAN : __logf(a.z) - a.s / a.z;
+}
+
+__device__ __forceinline__ float write_row(const Part& a, int row, float* H, int32_t* amax, float* conf) {
+  const float h = row_entropy(a);
   H[row] = h;
-  conf[row] = bad ? NAN : 1.0f / a.z;
+  conf[row] = a.nan || a.m == kNegInf ? NAN : 1.0f / a.z;
   amax[row] = a.idx == 0x7fffffff ? 0 : a.idx;
-  *h_out = h;
+  return h;
+}
+
+// E = max over the selected rows of h_of(row) (NaN if any is NaN, a selection is out of
+// range, or `fail`); every thread of the workgroup calls it, thread 0 writes *emax.
+// sel_pre is the row thread tid selects (loaded at the kernel's start, so that no global
+// load sits on the path after the states arrive); threads past the first kFThreads
+// selections read theirs here.
+template <typename HOf>
+__device__ void emax_over(const int32_t* __restrict__ sel, int n_sel, int sel_pre, int rows, int fail, HOf h_of,
+                          float* emax_sh, int* enan_sh, float* __restrict__ emax) {
+  const int tid = threadIdx.x;
+  float mx = kNegInf;
+  int nan = fail;
+  const int n = sel ? n_sel : rows;
+  for (int i = tid; i < n; i += kFThreads) {
+    const int r = i == tid ? sel_pre : (sel ? sel[i] : i);
+    if (r < 0 || r >= rows) {
+      nan = 1;
+      continue;
+    }
+    const float h = h_of(r);
+    if (h != h) nan = 1;
+    else mx = fmaxf(mx, h);
+  }
+  mx = wave_reduce(mx, [](float a, float b) { return fmaxf(a, b); });
+  nan = wave_reduce(nan, [](int a, int b) { return a | b; });
+  if ((tid & 63) == 0) {
+    emax_sh[tid >> 6] = mx;
+    enan_sh[tid >> 6] = nan;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kFWaves; ++w) {
+      mx = fmaxf(mx, emax_sh[w]);
+      nan |= enan_sh[w];
+    }
+    *emax = nan ? NAN : mx;
+  }
 }
 
 template <typename T, bool VEC>
@@ -302,17 +395,48 @@ entropy_fused_kernel(const T* __restrict__ logits, int rows, int V, int64_t stri
                      int32_t* __restrict__ amax, float* __restrict__ conf, float* __restrict__ emax,
                      uint64_t* __restrict__ parts, uint64_t* __restrict__ hpub, uint32_t tag) {
   __shared__ Part red[kFWaves];
-  __shared__ Part got[kMaxSplits];
+  __shared__ Part got[kMaxStates];
+  __shared__ float h_sh[kMaxStates];
   __shared__ int fail_sh;
   __shared__ float emax_sh[kFWaves];
   __shared__ int enan_sh[kFWaves];
-  const int split = blockIdx.x / rows, row = blockIdx.x % rows, tid = threadIdx.x;
+  const int b = blockIdx.x, split = b / rows, row = b % rows, tid = threadIdx.x;
+  const bool last = b == (int)gridDim.x - 1;
+  int sel_pre = -1;
+  if (last && emax && tid < (sel ? n_sel : rows)) sel_pre = sel ? sel[tid] : tid;
   const int lo = min(V, split * chunk), hi = min(V, lo + chunk);
   Part p = slice_state<T, VEC>(logits + (int64_t)row * stride, lo, hi, red);
-  uint64_t* pr = parts + (int64_t)row * S * 4;
-  if (split < S - 1) {  // publish this slice's state for the row's merger
+
+  if (S == 1) {  // the workgroup holds its whole row
     if (tid == 0) {
-      uint64_t* q = pr + split * 4;
+      const float h = write_row(p, row, H, amax, conf);
+      if (emax && !last) tag_store(hpub + row, tag, __float_as_uint(h));
+      if (last) h_sh[0] = h;
+    }
+    if (!emax || !last) return;
+    // the last workgroup: E once every other row has published its entropy
+    if (tid == 0) fail_sh = 0;
+    __syncthreads();
+    for (int r = tid; r < rows - 1; r += kFThreads) {
+      uint32_t w = 0;
+      if (!tag_wait<1>(hpub + r, tag, &w)) atomicOr(&fail_sh, 1);
+    }
+    __syncthreads();
+    const float h_last = h_sh[0];
+    emax_over(sel, n_sel, sel_pre, rows, fail_sh, [&](int r) {
+      return r == rows - 1 ? h_last
+                           : __uint_as_float((uint32_t)__hip_atomic_load(hpub + r, __ATOMIC_RELAXED,
+                                                                        __HIP_MEMORY_SCOPE_AGENT));
+    }, emax_sh, enan_sh, emax);
+    __syncthreads();
+    for (int r = tid; r < rows - 1; r += kFThreads) tag_store(hpub + r, 0u, 0u);  // consumed
+    return;
+  }
+
+  // S > 1: state b of the grid is published at parts[4 b .. 4 b + 3]
+  if (!last) {
+    if (tid == 0) {
+      uint64_t* q = parts + (int64_t)b * 4;
       tag_store(q + 0, tag, __float_as_uint(p.m));
       tag_store(q + 1, tag, __float_as_uint(p.z));
       tag_store(q + 2, tag, __float_as_uint(p.s));
@@ -320,68 +444,37 @@ entropy_fused_kernel(const T* __restrict__ logits, int rows, int V, int64_t stri
     }
     return;
   }
-  // ---- merger of this row: thread j < S - 1 collects slice j
-  if (tid == 0) fail_sh = 0;
-  __syncthreads();
-  if (tid < S - 1) {
-    uint64_t* q = pr + tid * 4;
-    uint32_t w[4] = {0x7fc00000u, 0u, 0u, 0x80000000u};  // read as a NaN row if the wait gives up
-    if (!tag_wait<4>(q, tag, w)) atomicOr(&fail_sh, 1);
-    got[tid] = Part{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), (int)(w[3] & 0x7fffffffu),
-                    (int)(w[3] >> 31), {0, 0, 0}};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tag_store(q + i, 0u, 0u);  // consumed
+  // ---- the last workgroup: collect every other state, merge each row in slice order.
+  // Its global stores (the rows' results, E, the cleared tags) are issued only after its
+  // last barrier, so no barrier waits for them.
+  const int ns = rows * S;
+  if (tid == 0) {
+    fail_sh = 0;
+    got[ns - 1] = p;
   }
   __syncthreads();
-  float h_row = NAN;
-  if (tid == 0) {
-    Part a = S > 1 ? got[0] : p;
-    for (int j = 1; j < S - 1; ++j) part_merge(a, got[j]);
-    if (S > 1) part_merge(a, p);
+  for (int j = tid; j < ns - 1; j += kFThreads) {
+    uint32_t w[4] = {0x7fc00000u, 0u, 0u, 0x80000000u};  // read as a NaN state if the wait gives up
+    if (!tag_wait<4>(parts + (int64_t)j * 4, tag, w)) atomicOr(&fail_sh, 1);
+    got[j] = Part{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), (int)(w[3] & 0x7fffffffu),
+                  (int)(w[3] >> 31), {0, 0, 0}};
+  }
+  __syncthreads();
+  Part a{kNegInf, 0.f, 0.f, 0x7fffffff, 0, {0, 0, 0}};
+  if (tid < rows) {  // rows < kFThreads whenever S > 1
+    a = got[tid];
+    for (int k = 1; k < S; ++k) part_merge(a, got[k * rows + tid]);
     if (fail_sh) a.nan = 1;
-    write_row(a, row, H, amax, conf, &h_row);
-    if (emax) tag_store(hpub + row, tag, __float_as_uint(h_row));
+    h_sh[tid] = row_entropy(a);
   }
-  if (!emax || blockIdx.x != gridDim.x - 1) return;
-  // ---- the last workgroup: E over the selected rows once every row has published
-  // (all rows' words are awaited and cleared, also rows outside the selection)
-  if (tid == 0) fail_sh = 0;
-  __syncthreads();
-  for (int r = tid; r < rows; r += kFThreads) {
-    uint32_t w = 0;
-    if (!tag_wait<1>(hpub + r, tag, &w)) atomicOr(&fail_sh, 1);
+  if (emax) {
+    __syncthreads();
+    emax_over(sel, n_sel, sel_pre, rows, fail_sh, [&](int r) { return h_sh[r]; }, emax_sh, enan_sh, emax);
   }
-  __syncthreads();
-  float mx = kNegInf;
-  int nan = fail_sh;
-  const int n = sel ? n_sel : rows;
-  for (int i = tid; i < n; i += kFThreads) {
-    const int r = sel ? sel[i] : i;
-    if (r < 0 || r >= rows) {
-      nan = 1;
-      continue;
-    }
-    const float h = __uint_as_float((uint32_t)__hip_atomic_load(hpub + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    if (h != h) nan = 1;
-    else mx = fmaxf(mx, h);
-  }
+  if (tid < rows) write_row(a, tid, H, amax, conf);
+  for (int j = tid; j < ns - 1; j += kFThreads) {
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-    nan |= __shfl_xor(nan, o);
-  }
-  if ((tid & 63) == 0) {
-    emax_sh[tid >> 6] = mx;
-    enan_sh[tid >> 6] = nan;
-  }
-  __syncthreads();
-  for (int r = tid; r < rows; r += kFThreads) tag_store(hpub + r, 0u, 0u);  // consumed
-  if (tid == 0) {
-    for (int w = 1; w < kFWaves; ++w) {
-      mx = fmaxf(mx, emax_sh[w]);
-      nan |= enan_sh[w];
-    }
-    *emax = nan ? NAN : mx;
+    for (int i = 0; i < 4; ++i) tag_store(parts + (int64_t)j * 4 + i, 0u, 0u);  // consumed
   }
 }
 
@@ -416,7 +509,7 @@ uint32_t next_tag() {
 
 size_t entropy_ws_bytes(int rows, int vocab) {
   if (rows <= 0 || vocab <= 0) return 0;
-  // tagged slice states [rows][S][4] and published row entropies [rows], 64-bit words
+  // tagged slice states [S][rows][4] and published row entropies [rows], 64-bit words
   return ((size_t)rows * splits_for(rows, vocab) * 4 + (size_t)rows) * sizeof(uint64_t) + 256;
 }
 
@@ -430,9 +523,17 @@ ec_status entropy(ec_dtype dt, const void* logits, int rows, int vocab, int64_t 
     }
     return EC_OK;
   }
-  const int S = splits_for(rows, vocab);
   const int E = dt == EC_BF16 ? 8 : 4;
-  const int chunk = ((vocab + S - 1) / S + E - 1) / E * E;  // slice starts stay 16-byte aligned
+  const int P = kFThreads * kFU * E;  // elements per pass of a workgroup
+  int S = splits_for(rows, vocab);
+  // slice starts stay 16-byte aligned; where rounding the slice length up to whole passes
+  // keeps the number of slices, it is rounded, so that only the last slice of a row has a
+  // partial (masked) pass
+  int chunk = ((vocab + S - 1) / S + E - 1) / E * E;
+  const int whole = (chunk + P - 1) / P * P;
+  if (S > 1 && (vocab + whole - 1) / whole == S) chunk = whole;
+  EC_REQUIRE(S == 1 || (int64_t)rows * S <= kMaxStates, EC_ERR_UNSUPPORTED,
+             "ec_entropy_max: %d rows x %d slices exceed %d slice states", rows, S, kMaxStates);
   uint64_t* parts = (uint64_t*)ws;
   uint64_t* hpub = parts + (size_t)rows * S * 4;
   const uint32_t tag = next_tag();

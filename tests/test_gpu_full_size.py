@@ -113,6 +113,24 @@ def test_8b_refresh_and_skip_steps_match_oracle():
         assert errs.max() <= BAR and el <= BAR and bad.size == 0
 
 
+def test_8b_width_bf16_trajectory_hot_token_fixture():
+    """The device's own bf16 trajectory (not lock-step) at the 8B layer width against the
+    oracle's: two layers of the 8B shape (d=4096, 32 heads of 128, SwiGLU 12288,
+    V=126464), L=1024 = 768 + 256, whole blocks of 8 decoded per step, k=16, tau = +inf
+    (every step after the first is a skip step over the still-masked rows and the recent
+    ones), on the hot-token fixture (4 LM-head rows scaled by 12). The fixture was sized
+    on the oracle alone so that its first four steps clear the id and cut gates; decoded
+    positions and ids must then be identical on at least those four steps, |R| and the
+    path on every step compared, E within the first-order bar of the other bf16
+    trajectory tests."""
+    import dataclasses
+    from tests.test_gpu_step import _compare_run, _e_tol_perturbation
+    cfg = dataclasses.replace(synth.CONFIGS["8b"], tokens_per_step=8, block_len=8)
+    w = synth.make_hot_token_model(cfg.model, n_layers=2, hot_tokens=4, hot_scale=12.0)
+    _compare_run(cfg, w, math.inf, max_steps=8, e_tol=_e_tol_perturbation, expect_full_compare=False,
+                 min_compared=4)
+
+
 def test_long_context_batch_full_size():
     """The long-context workload at full size: four sequences of L=4096 (3584 prompt + 512
     masked), k=32, tau=1.0, stepped together by ec_step_batch as the bench launches them.
