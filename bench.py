@@ -208,7 +208,10 @@ def long_batch_bench(dm, steps: int, warmup: int = 2):
             ntok += sum(len(o.positions) for o in live)
             nref += sum(o.refreshed for o in live)
             nseq += len(live)
-        res[f"tau={tau}"] = {"steps": steps, "steps_per_s": steps / wall,
+        first = n_warm if tau == 1.0 else 1
+        res[f"tau={tau}"] = {"window": f"steps {first}..{first + steps - 1} of the {cfg.steps}-step trajectory "
+                                       f"(not a whole trajectory)",
+                             "steps": steps, "steps_per_s": steps / wall,
                              "gen_tokens_per_s": ntok / wall, "ms_per_step": wall * 1e3 / steps,
                              "refresh_rate": nref / max(nseq, 1),
                              "mean_rows_per_seq": sum(o.rows for st in outs for o in st if o) / max(nseq, 1),
