@@ -223,3 +223,21 @@ def test_decode_ring_slot_rule_keeps_the_last_k_entries(n, k):
         assert held == set(log[-k:])
         R = sorted(set(np.flatnonzero(masked).tolist()) | held)
         np.testing.assert_array_equal(R, ol.recompute_set(masked, log, k))
+
+
+def test_top2_margin_pins():
+    """The top-1/top-2 logit margin the id gate uses: a worked row, a tied maximum (margin 0),
+    shift invariance, and against a brute force written differently (the smallest gap between
+    the row maximum and any other entry, over every index but the first argmax)."""
+    np.testing.assert_array_equal(ol._top2_margin(np.array([[1.0, 5.0, 3.0]])), [2.0])
+    np.testing.assert_array_equal(ol._top2_margin(np.array([[4.0, 1.0, 4.0]])), [0.0])
+    assert ol._top2_margin(np.array([[7.0]]))[0] == np.inf
+    rng = np.random.default_rng(5)
+    x = np.round(rng.standard_normal((50, 37)) * 4) / 4  # quarter steps: ties happen
+    m = ol._top2_margin(x)
+    np.testing.assert_allclose(ol._top2_margin(x + 3.25), m, rtol=0, atol=1e-12)
+    for row, got in zip(x, m):
+        a = int(np.argmax(row))
+        brute = min(row[a] - row[j] for j in range(len(row)) if j != a)
+        assert got == brute
+    assert (m >= 0).all()
