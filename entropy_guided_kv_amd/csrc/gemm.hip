@@ -672,19 +672,16 @@ struct Plan {
 // at kCuLoadBytesPerUs (Mr = the tile's rows that exist, min(BM, M rounded up to 32):
 // rows past M are not loaded), plus, for split K, the partials' round trip (S M N x 8 bytes at
 // 3 TB/s) and 6 us for the reduction launch (measured with the K rotation of skinny
-// tiles). Over the measured shapes the choice costs 0.2 % more than the best candidate
-// in total, at most 4 % on a shape but one (17 x 12288 x 4096: 26 %). Larger
-// tiles carry more MFMA work per staged byte; smaller ones
-// and split K fill the 256 CUs at skinny M (skip steps, the LM head over the
-// candidates). The all-rows tiles (four wavefronts stacked along M over one weight
-// slice of 96, 64 or 32 columns) are priced only at M <= 256: their efficiencies were
-// fitted, with the four older tiles' figures held fixed, to a sweep of every tile and
-// split at M = 17 .. 256 on the four projection shapes (the choices then cost 0.7 % more
-// than the fastest measured candidate in total, against 2.3 % without them). The 64-row
-// tiles with 96 or 64 columns cut the projections into about 256 workgroups at M <= 64;
-// their efficiencies were fitted the same way to a second sweep at M = 17 .. 128. Every tile
-// shape and split S in {1, 2, 4, 8} (K chunks of at least 8 steps) is priced and the
-// cheapest taken.
+// tiles). Larger tiles carry more MFMA work per staged byte; smaller ones and split K
+// fill the 256 CUs at skinny M (skip steps, the LM head over the candidates). The
+// all-rows tiles (four wavefronts stacked along M over one weight slice of 96, 64 or 32
+// columns) are priced only at M <= 256, and the 64-row tiles with 96 or 64 columns, which
+// cut the projections into about 256 workgroups, also at M <= 64; their efficiencies were
+// fitted, with the four older tiles' figures held fixed, to sweeps of every tile and split
+// at M = 17 .. 256 on the four projection shapes. Over those sweeps the choices cost 1.2 %
+// more than the fastest measured candidate in total, at most 11 % on one shape (17 rows of
+// the 4096 x 4096 product). Every tile shape and split S in {1, 2, 4, 8} (K chunks of at
+// least 8 steps) is priced and the cheapest taken.
 Plan plan_bf16(int M, int N, int K, int kind) {
   Plan best{};
   double best_us = 1e300;

@@ -41,6 +41,23 @@ def test_forward_at_8b_layer_width(n_rows):
     _compare(WIDE, omm, dm, cache, oc, tokens, rows, out)
 
 
+NARROW_FFN = synth.ModelShape("narrowffn", "bf16", 1, 2048, 16, 128, 512, 1024)
+
+
+@pytest.mark.parametrize("n_rows", [40, 1])
+def test_forward_split_k_swiglu(n_rows):
+    """A layer whose packed gate/up matrix is short (2F = 1024 rows) against a deep K
+    (d = 2048): the GEMM planner splits K four ways over 64x64 tiles, so the SwiGLU runs in
+    the split-K reduction instead of the GEMM epilogue. Same bars as the other forward
+    tests."""
+    L = 256
+    w, omm, dm, cache, oc = _setup(NARROW_FFN, L, seed=31, stale=True)
+    rng = np.random.default_rng(32)
+    tokens = rng.integers(0, NARROW_FFN.vocab - 1, L).astype(np.int32)
+    rows = np.sort(rng.choice(L, n_rows, replace=False))
+    _compare(NARROW_FFN, omm, dm, cache, oc, tokens, rows, rows[: min(n_rows, 16)])
+
+
 WIDE13 = synth.ModelShape("wide13", "bf16", 1, 5120, 40, 128, 13824, 1024)
 
 
