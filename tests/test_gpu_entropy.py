@@ -65,9 +65,13 @@ def test_entropy_edge_rows(dtype):
 
 
 @pytest.mark.parametrize("rows,V,stride_pad", [(1, 1, 0), (3, 7, 1), (5, 1000, 24), (17, 12345, 3),
-                                               (2, 126464, 0), (128, 32000, 0), (0, 10, 0)])
+                                               (2, 126464, 0), (128, 32000, 0), (0, 10, 0),
+                                               (300, 2000, 0), (1000, 4096, 8)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_entropy_ragged_and_strided(rows, V, stride_pad, dtype):
+    """Fewer than 256 rows split each row into slices that the last workgroup merges; 256
+    rows or more take one workgroup per row, whose entropies the last workgroup gathers for
+    E; a row pitch that is not a multiple of 16 bytes takes the element-wise path."""
     rng = np.random.default_rng(rows * 7 + V)
     z = (rng.standard_normal((rows, V + stride_pad)) * rng.uniform(0.1, 6, (rows, 1))).astype(np.float32)
     if dtype == "bf16":
