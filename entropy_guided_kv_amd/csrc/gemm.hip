@@ -572,8 +572,9 @@ splitk_epilogue_kernel(const float* __restrict__ part, int S, int M, int N, int 
 }
 
 // -------------------------------------------------------------------- fp32 SIMT GEMM
-// Plain fp32 path (fp32 models): one thread per output unit (an element, or
-// the pair the rotary / SwiGLU epilogue needs), dot products over K.
+// fp32 path for shapes the matrix-unit kernel below does not take (K not a multiple of
+// 4, or rotary halves narrower than 32 columns): one thread per output unit (an element,
+// or the pair the rotary / SwiGLU epilogue needs), dot products over K.
 __global__ void __launch_bounds__(kThreads)
 gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
                 const float* __restrict__ B2, int M, int N, int K, EpiArgs epi) {
@@ -613,6 +614,79 @@ gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
     float x = 0.f;
     for (int k = 0; k < K; ++k) x = fmaf(a[k], b[k], x);
     epi_single<float>(epi, m, col, x);
+  }
+}
+
+// fp32 models on the matrix unit (v_mfma_f32_32x32x2_f32): one wavefront per 32 output
+// rows and two 32-column blocks that its epilogue pairs: the rotary partners half a head
+// away (q/k/v), the up rows of the same columns (SwiGLU, from B2), or the next 32
+// columns. Lane l loads four consecutive K elements at offset 4 (l / 32) of each 8-wide K
+// step from row l % 32 of A and of each B block, so MFMA j of the step takes K positions
+// k + j (lanes 0-31) and k + 4 + j (lanes 32-63). Every output sums its K positions in the
+// same order whatever M and whichever rows share its launch.
+constexpr int kF32Waves = 4;
+__global__ void __launch_bounds__(kF32Waves * 64)
+gemm_f32_mfma_kernel(const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ B2,
+                     int M, int N, int K, int units, EpiArgs epi) {
+  const int lane = threadIdx.x % 64;
+  const int64_t w = (int64_t)blockIdx.x * kF32Waves + threadIdx.x / 64;
+  const int mb = (M + 31) / 32;
+  if (w >= (int64_t)mb * units) return;  // a whole wavefront
+  const int mt = (int)(w % mb), u = (int)(w / mb);
+  const int kind = epi.kind;
+  int c1, c2;
+  const float* Bs = B;
+  if (kind == EPI_QKV) {
+    const int half = epi.head_dim / 2, per_head = half / 32;
+    c1 = (u / per_head) * epi.head_dim + (u % per_head) * 32;
+    c2 = c1 + half;
+  } else if (kind == EPI_SWIGLU) {
+    c1 = c2 = u * 32;
+    Bs = B2;
+  } else {
+    c1 = u * 64;
+    c2 = c1 + 32;
+  }
+  const int r = lane % 32, kq = 4 * (lane / 32), m0 = mt * 32;
+  const float* a = A + (int64_t)min(m0 + r, M - 1) * K + kq;
+  const float* b1 = B + (int64_t)min(c1 + r, N - 1) * K + kq;
+  const float* b2 = Bs + (int64_t)min(c2 + r, N - 1) * K + kq;
+  f32x16 acc1, acc2;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc1[v] = acc2[v] = 0.f;
+  auto step = [&](const float4& x, const float4& y1, const float4& y2) __attribute__((always_inline)) {
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y1.x, acc1, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y2.x, acc2, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y1.y, acc1, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y2.y, acc2, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y1.z, acc1, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y2.z, acc2, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y1.w, acc1, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y2.w, acc2, 0, 0, 0);
+  };
+  int k = 0;
+  for (; k + 8 <= K; k += 8)
+    step(*reinterpret_cast<const float4*>(a + k), *reinterpret_cast<const float4*>(b1 + k),
+         *reinterpret_cast<const float4*>(b2 + k));
+  if (k < K) {  // K % 8 == 4: the upper half-wavefront's elements lie past K and count as zero
+    const bool in = k + kq < K;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    step(in ? *reinterpret_cast<const float4*>(a + k) : z, in ? *reinterpret_cast<const float4*>(b1 + k) : z,
+         in ? *reinterpret_cast<const float4*>(b2 + k) : z);
+  }
+  // accumulator element v of lane l: row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int m = m0 + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+    if (m >= M) continue;
+    if (kind == EPI_QKV) {
+      epi_qkv_pair<float>(epi, m, c1 + r, acc1[v], acc2[v]);
+    } else if (kind == EPI_SWIGLU) {
+      if (c1 + r < N) epi_swiglu<float>(epi, m, c1 + r, acc1[v], acc2[v]);
+    } else {
+      if (c1 + r < N) epi_single<float>(epi, m, c1 + r, acc1[v]);
+      if (c2 + r < N) epi_single<float>(epi, m, c2 + r, acc2[v]);
+    }
   }
 }
 
@@ -798,6 +872,16 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
   const int kind = epi.kind;
   if (dt == EC_F32) {
     EC_REQUIRE(kind != EPI_ENTROPY, EC_ERR_UNSUPPORTED, "gemm: the fused entropy epilogue is bf16 only");
+    if (K % 4 == 0 && (kind != EPI_QKV || epi.head_dim % 64 == 0)) {
+      // matrix-unit path: 16-byte rows, rotary halves of whole 32-column blocks
+      const int units = kind == EPI_QKV ? N / 64 : kind == EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64;
+      const int64_t waves = (int64_t)((M + 31) / 32) * units;
+      const int blocks = (int)((waves + kF32Waves - 1) / kF32Waves);
+      gemm_f32_mfma_kernel<<<blocks, kF32Waves * 64, 0, s>>>((const float*)A, (const float*)B, (const float*)B2, M,
+                                                             N, K, units, epi);
+      EC_CHECK_LAUNCH("gemm_f32_mfma_kernel");
+      return EC_OK;
+    }
     const int64_t units = (kind == EPI_QKV) ? (int64_t)M * (N / 2) : (int64_t)M * N;
     const int blocks = (int)((units + kThreads - 1) / kThreads);
     gemm_f32_kernel<<<blocks, kThreads, 0, s>>>((const float*)A, (const float*)B,
