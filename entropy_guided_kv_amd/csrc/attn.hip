@@ -441,7 +441,7 @@ ec_status launch_merge(const float* po, const float* pml, int S, int r, int H, i
   return EC_OK;
 }
 
-// fp32 path: one workgroup per (query, head); scores in LDS, exact softmax.
+// fp32 path for other head sizes: one workgroup per (query, head); scores in LDS, exact softmax.
 __global__ void __launch_bounds__(kThreads)
 attn_f32_kernel(const float* __restrict__ q, const AttnSeqs seqs, int L, int H, int Dh, float scale,
                 float* __restrict__ out) {
@@ -490,6 +490,107 @@ attn_f32_kernel(const float* __restrict__ q, const AttnSeqs seqs, int L, int H, 
     float acc = 0.f;
     for (int j = 0; j < L; ++j) acc = fmaf(sc[j], vc[(int64_t)j * HD + h * Dh + d], acc);
     out[(int64_t)i * HD + h * Dh + d] = acc * inv;
+  }
+}
+
+// fp32 path on the matrix unit (v_mfma_f32_32x32x2_f32): one wavefront per 32 queries of
+// one sequence and one head, transposed like the bf16 kernel so that the probabilities
+// feed the second product from the registers that hold the scores:
+//   S^T[32 keys, 32 queries] = K Q^T   (lane l: query l % 32; keys 8 (v / 4) + 4 (l / 32) + v % 4)
+//   O^T[Dh, 32 queries]     += V^T P^T (register v of a lane is the B operand of one MFMA
+//                                       over the key pair {8 (v / 4) + v % 4, + 4})
+// over blocks of 32 keys with an online softmax (running max and sum per query, kept by
+// the two lanes l and l ^ 32 that share a query). The K and Q operands use four
+// consecutive head dimensions per lane, 4 (l / 32) into each 8-wide step (MFMA j takes
+// dimensions d + j and d + 4 + j). Q stays in registers; K and V come from the cache.
+template <int DH>
+__global__ void __launch_bounds__(256)
+attn_f32_mfma_kernel(const float* __restrict__ q_all, const AttnSeqs seqs, int L, int H, float scale,
+                     float* __restrict__ out_all, int waves_total) {
+  const int lane = threadIdx.x % 64;
+  int w = blockIdx.x * 4 + threadIdx.x / 64;
+  if (w >= waves_total) return;  // a whole wavefront
+  int si = 0, qtiles = 0;
+  for (;;) {
+    qtiles = (seqs.s[si].nr + 31) / 32;
+    if (w < qtiles * H || si + 1 >= seqs.n) break;
+    w -= qtiles * H;
+    ++si;
+  }
+  if (qtiles == 0) return;  // (not reached: the grid counts only sequences with rows)
+  const int qt = w % qtiles, h = w / qtiles;
+  const int r = seqs.s[si].nr;
+  const int64_t HD = (int64_t)H * DH;
+  const float* __restrict__ q = q_all + (int64_t)seqs.s[si].row0 * HD + h * DH;
+  const float* __restrict__ kc = (const float*)seqs.s[si].k + h * DH;
+  const float* __restrict__ vc = (const float*)seqs.s[si].v + h * DH;
+  float* __restrict__ out = out_all + (int64_t)seqs.s[si].row0 * HD + h * DH;
+  const int c = lane % 32, hf = lane / 32;
+  const int qrow = qt * 32 + c;
+  float4 fq[DH / 8];
+  {
+    const float* qr = q + (int64_t)min(qrow, r - 1) * HD + 4 * hf;
+#pragma unroll
+    for (int j = 0; j < DH / 8; ++j) fq[j] = *reinterpret_cast<const float4*>(qr + 8 * j);
+  }
+  f32x16 o[DH / 32];
+#pragma unroll
+  for (int i = 0; i < DH / 32; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int kb = 0; kb < L; kb += 32) {
+    f32x16 st;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) st[v] = 0.f;
+    const float* kr = kc + (int64_t)min(kb + c, L - 1) * HD + 4 * hf;
+#pragma unroll
+    for (int j = 0; j < DH / 8; ++j) {
+      const float4 k4 = *reinterpret_cast<const float4*>(kr + 8 * j);
+      st = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.x, fq[j].x, st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.y, fq[j].y, st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.z, fq[j].z, st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.w, fq[j].w, st, 0, 0, 0);
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = kb + 8 * (v / 4) + 4 * hf + (v % 4);
+      st[v] = key < L ? st[v] * scale : -INFINITY;
+      tmax = fmaxf(tmax, st[v]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);  // finite: every block holds a key below L
+    const float alpha = __expf(m_run - m_new);  // 0 on the first block
+#pragma unroll
+    for (int i = 0; i < DH / 32; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+    float psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      st[v] = __expf(st[v] - m_new);
+      psum += st[v];
+    }
+    l_run = l_run * alpha + psum + __shfl_xor(psum, 32);
+    m_run = m_new;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = min(kb + 8 * (v / 4) + 4 * hf + (v % 4), L - 1);  // past L: weight 0
+      const float* vr = vc + (int64_t)key * HD + c;
+#pragma unroll
+      for (int i = 0; i < DH / 32; ++i)
+        o[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32 * i], st[v], o[i], 0, 0, 0);
+    }
+  }
+  // O^T element v of lane l: dimension 8 (v / 4) + 4 (l / 32) + v % 4 of block i, query l % 32
+  if (qrow < r) {
+    const float inv = 1.0f / l_run;
+    float* orow = out + (int64_t)qrow * HD;
+#pragma unroll
+    for (int i = 0; i < DH / 32; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) orow[32 * i + 8 * (v / 4) + 4 * hf + (v % 4)] = o[i][v] * inv;
   }
 }
 
@@ -556,6 +657,18 @@ ec_status attn_batch(ec_dtype dt, const void* q, const AttnSeqs& seqs, int L, in
   if (r == 0) return EC_OK;
   EC_REQUIRE(L >= 1, EC_ERR_ARG, "attn: seq_len must be >= 1");
   if (dt == EC_F32) {
+    if (Dh == 32 || Dh == 64 || Dh == 128) {  // matrix-unit path
+      int waves = 0;
+      for (int i = 0; i < seqs.n; ++i) waves += (seqs.s[i].nr + 31) / 32 * H;
+      const int blocks = (waves + 3) / 4;
+#define EC_F32_ATTN(DHV)                                                                                     attn_f32_mfma_kernel<DHV><<<blocks, 256, 0, s>>>((const float*)q, seqs, L, H, scale, (float*)out, waves)
+      if (Dh == 32) EC_F32_ATTN(32);
+      else if (Dh == 64) EC_F32_ATTN(64);
+      else EC_F32_ATTN(128);
+#undef EC_F32_ATTN
+      EC_CHECK_LAUNCH("attn_f32_mfma_kernel");
+      return EC_OK;
+    }
     EC_REQUIRE(Dh <= 1024 && (size_t)(L + Dh) * 4 <= 64 * 1024, EC_ERR_UNSUPPORTED,
                "attn: f32 path supports L + head_dim <= 16384");
     dim3 grid(r, H);

@@ -81,8 +81,11 @@ def test_partial_attn_bf16(r, L, H):
     assert err < 2e-2
 
 
-@pytest.mark.parametrize("r,L,H,D", [(32, 128, 4, 64), (5, 300, 2, 16), (1, 1, 1, 8)])
+@pytest.mark.parametrize("r,L,H,D", [(32, 128, 4, 64), (45, 300, 3, 64), (70, 1000, 2, 128), (1, 33, 1, 32),
+                                     (5, 300, 2, 16), (1, 1, 1, 8)])
 def test_partial_attn_f32(r, L, H, D):
+    """head_dim 32, 64 and 128 run on the matrix unit (ragged query tiles and key blocks
+    past L masked), other head sizes on the one-workgroup-per-query kernel."""
     got, want = _attn_case(r, L, H, D, torch.float32, seed=3)
     assert row_rel_err(got.reshape(r * H, D), want.reshape(r * H, D)) < 1e-5
 
