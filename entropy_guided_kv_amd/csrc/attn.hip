@@ -657,7 +657,9 @@ ec_status attn_batch(ec_dtype dt, const void* q, const AttnSeqs& seqs, int L, in
   if (r == 0) return EC_OK;
   EC_REQUIRE(L >= 1, EC_ERR_ARG, "attn: seq_len must be >= 1");
   if (dt == EC_F32) {
-    if (Dh == 32 || Dh == 64 || Dh == 128) {  // matrix-unit path
+    uintptr_t align = (uintptr_t)q | (uintptr_t)out;
+    for (int i = 0; i < seqs.n; ++i) align |= (uintptr_t)seqs.s[i].k | (uintptr_t)seqs.s[i].v;
+    if ((Dh == 32 || Dh == 64 || Dh == 128) && align % 16 == 0) {  // matrix-unit path (16-byte row loads)
       int waves = 0;
       for (int i = 0; i < seqs.n; ++i) waves += (seqs.s[i].nr + 31) / 32 * H;
       const int blocks = (waves + 3) / 4;

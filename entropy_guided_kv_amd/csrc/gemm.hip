@@ -572,9 +572,10 @@ splitk_epilogue_kernel(const float* __restrict__ part, int S, int M, int N, int 
 }
 
 // -------------------------------------------------------------------- fp32 SIMT GEMM
-// fp32 path for shapes the matrix-unit kernel below does not take (K not a multiple of
-// 4, or rotary halves narrower than 32 columns): one thread per output unit (an element,
-// or the pair the rotary / SwiGLU epilogue needs), dot products over K.
+// fp32 path for what the matrix-unit kernel below does not take (K not a multiple of 4,
+// operands not 16-byte aligned, or rotary halves narrower than 32 columns): one thread per
+// output unit (an element, or the pair the rotary / SwiGLU epilogue needs), dot products
+// over K.
 __global__ void __launch_bounds__(kThreads)
 gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
                 const float* __restrict__ B2, int M, int N, int K, EpiArgs epi) {
@@ -872,8 +873,9 @@ ec_status gemm(ec_dtype dt, const void* A, const void* B, const void* B2, int M,
   const int kind = epi.kind;
   if (dt == EC_F32) {
     EC_REQUIRE(kind != EPI_ENTROPY, EC_ERR_UNSUPPORTED, "gemm: the fused entropy epilogue is bf16 only");
-    if (K % 4 == 0 && (kind != EPI_QKV || epi.head_dim % 64 == 0)) {
-      // matrix-unit path: 16-byte rows, rotary halves of whole 32-column blocks
+    const bool a16 = (((uintptr_t)A | (uintptr_t)B | (uintptr_t)(B2 ? B2 : B)) & 15) == 0;
+    if (K % 4 == 0 && a16 && (kind != EPI_QKV || epi.head_dim % 64 == 0)) {
+      // matrix-unit path: 16-byte row loads, rotary halves of whole 32-column blocks
       const int units = kind == EPI_QKV ? N / 64 : kind == EPI_SWIGLU ? (N + 31) / 32 : (N + 63) / 64;
       const int64_t waves = (int64_t)((M + 31) / 32) * units;
       const int blocks = (int)((waves + kF32Waves - 1) / kF32Waves);

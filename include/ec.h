@@ -136,7 +136,9 @@ ec_status ec_cache_scatter(void* k_cache, void* v_cache, int64_t seq_len, int32_
  * unrounded, out = sum_j bf16(w_j) v_j / sum_j w_j (bf16 rounding commutes with
  * powers of two, so the result does not depend on M).
  * Supported: head_dim == 128 for bf16, with max(r, seq_len) * n_heads * 256
- * bytes below 2 GiB (32-bit buffer offsets); head_dim <= 256 for f32.
+ * bytes below 2 GiB (32-bit buffer offsets). f32: head_dim 32, 64 or 128 with
+ * 16-byte aligned q, caches and out runs on the matrix unit at any seq_len;
+ * otherwise head_dim <= 1024 with (seq_len + head_dim) * 4 <= 65536.
  * EC_ERR_UNSUPPORTED otherwise.
  * workspace: >= ec_partial_attn_workspace_size(...) bytes (may be 0 -> NULL ok).
  * ---------------------------------------------------------------------- */

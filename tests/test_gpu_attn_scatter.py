@@ -48,7 +48,7 @@ def test_cache_scatter_skips_out_of_range_rows():
     assert kc[2].float().sum().item() == 256 and kc.float().sum().item() == 256
 
 
-def _attn_case(r, L, H, D, dtype, seed=0, scale=1.0):
+def _attn_case(r, L, H, D, dtype, seed=0, scale=1.0, misalign=False):
     import entropy_guided_kv_amd as ek
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((r, H * D)) * scale
@@ -57,6 +57,13 @@ def _attn_case(r, L, H, D, dtype, seed=0, scale=1.0):
     if dtype == torch.bfloat16:
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
     dev = [torch.from_numpy(a.astype(np.float32)).to(dtype).cuda() for a in (q, k, v)]
+    if misalign:  # the same values one element past a 16-byte boundary
+        def shift(t):
+            buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+            view = buf[1:].view(t.shape)
+            view.copy_(t)
+            return view
+        dev = [shift(t) for t in dev]
     out = ek.ec_partial_attn(dev[0], dev[1], dev[2], H, D)
     torch.cuda.synchronize()
     want = attention(q.reshape(r, H, D), k.reshape(L, H, D), v.reshape(L, H, D)).reshape(r, H * D)
@@ -87,6 +94,14 @@ def test_partial_attn_f32(r, L, H, D):
     """head_dim 32, 64 and 128 run on the matrix unit (ragged query tiles and key blocks
     past L masked), other head sizes on the one-workgroup-per-query kernel."""
     got, want = _attn_case(r, L, H, D, torch.float32, seed=3)
+    assert row_rel_err(got.reshape(r * H, D), want.reshape(r * H, D)) < 1e-5
+
+
+def test_partial_attn_f32_unaligned_rows():
+    """Operands 4 bytes off a 16-byte boundary take the one-workgroup-per-query kernel
+    (the matrix-unit kernel reads 16-byte row pieces)."""
+    r, L, H, D = 32, 128, 4, 64
+    got, want = _attn_case(r, L, H, D, torch.float32, seed=3, misalign=True)
     assert row_rel_err(got.reshape(r * H, D), want.reshape(r * H, D)) < 1e-5
 
 
