@@ -461,13 +461,31 @@ entropy_fused_kernel(const T* __restrict__ logits, int rows, int V, int64_t stri
   }
   __syncthreads();
   Part a{kNegInf, 0.f, 0.f, 0x7fffffff, 0, {0, 0, 0}};
+  float h = NAN;
   if (tid < rows) {  // rows < kFThreads whenever S > 1
     a = got[tid];
     for (int k = 1; k < S; ++k) part_merge(a, got[k * rows + tid]);
     if (fail_sh) a.nan = 1;
-    h_sh[tid] = row_entropy(a);
+    h = row_entropy(a);
   }
-  if (emax) {
+  const int n = sel ? n_sel : rows;
+  if (rows <= 64 && n <= 64) {
+    // wavefront 0 holds every row's entropy: E from its registers, no further barrier
+    if (emax && tid < 64) {
+      const int r = sel_pre;
+      const float hr = __shfl(h, r & 63);
+      float mx = kNegInf;
+      int nan = fail_sh;
+      if (tid < n) {
+        if (r < 0 || r >= rows || hr != hr) nan = 1;
+        else mx = hr;
+      }
+      mx = wave_reduce(mx, [](float x, float y) { return fmaxf(x, y); });
+      nan = wave_reduce(nan, [](int x, int y) { return x | y; });
+      if (tid == 0) *emax = nan ? NAN : mx;
+    }
+  } else if (emax) {
+    if (tid < rows) h_sh[tid] = h;
     __syncthreads();
     emax_over(sel, n_sel, sel_pre, rows, fail_sh, [&](int r) { return h_sh[r]; }, emax_sh, enan_sh, emax);
   }
