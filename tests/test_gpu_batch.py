@@ -33,10 +33,10 @@ def _prompts(cfg, n):
     return out
 
 
-def _batch_run(dm, cfg, tau, prompts, max_steps=None):
+def _batch_run(dm, cfg, tau, prompts, max_steps=None, window=False):
     from entropy_guided_kv_amd import api
     bd = api.BatchDecoder(dm, len(prompts), cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step,
-                          cfg.block_len, cfg.k_recent, tau)
+                          cfg.block_len, cfg.k_recent, tau, window=window)
     bd.reset([torch.from_numpy(p) for p in prompts])
     steps = bd.run(max_steps=max_steps)
     return bd, [[st[i] for st in steps] for i in range(len(prompts))]
@@ -134,3 +134,27 @@ def test_batch_sixteen_sequences_tiny():
         single = dec.run(max_steps=6)
         assert [(o.refreshed, o.positions, o.ids, o.emax) for o in single] == \
                [(o.refreshed, o.positions, o.ids, o.emax) for o in seq_outs[i]]
+
+
+def test_batch_sliding_window_tiny():
+    """Sliding-window candidates (candidates from the window at each sequence's lowest masked
+    position) in a batch of three fp32 sequences, blocks of 8 and two tokens per step, on the
+    peaked head (refresh and skip steps mix): each sequence equals its single-sequence run
+    bit for bit over its whole decode."""
+    import dataclasses
+    from entropy_guided_kv_amd import api
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], tokens_per_step=2, block_len=8)
+    w = synth.make_model(cfg.model, lm_head_scale=PEAKED_SCALE)
+    dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+    prompts = _prompts(cfg, 3)
+    _, seq_outs = _batch_run(dm, cfg, PEAKED_TAU, prompts, window=True)
+    for i in range(3):
+        dec = api.Decoder(dm, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len,
+                          cfg.k_recent, PEAKED_TAU, window=True)
+        dec.reset(torch.from_numpy(prompts[i]))
+        single = dec.run()
+        got = [o for o in seq_outs[i] if o is not None]
+        assert len(got) == len(single) == cfg.steps
+        assert [(o.refreshed, o.rows, o.positions, o.ids, o.emax) for o in single] == \
+               [(o.refreshed, o.rows, o.positions, o.ids, o.emax) for o in got]
+    assert any(o.refreshed for o in seq_outs[0][1:]) and not all(o.refreshed for o in seq_outs[0])
