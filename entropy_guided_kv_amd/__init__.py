@@ -7,7 +7,8 @@ call loads libec.so and raises if it has not been built.
 from ._lib import ECError, load  # noqa: F401
 
 __all__ = [
-    "ECError", "load", "ec_entropy_max", "ec_entropy_max_noalloc", "ec_cache_scatter", "ec_partial_attn", "ec_rope_table",
+    "ECError", "load", "ec_entropy_max", "ec_entropy_max_noalloc", "ec_cache_scatter", "ec_partial_attn",
+    "ec_partial_attn_plan", "ec_rope_table",
     "ec_forward", "DeviceModel", "KVCache", "Decoder", "StepOut", "ec_timing_enable",
     "ec_timing_read",
 ]

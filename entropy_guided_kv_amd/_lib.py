@@ -22,7 +22,7 @@ STATUS_NAMES = {
 
 EXPORTS = (
     "ec_entropy_max_workspace_size", "ec_entropy_max", "ec_entropy_max_noalloc", "ec_cache_scatter",
-    "ec_partial_attn_workspace_size", "ec_partial_attn", "ec_rope_table",
+    "ec_partial_attn_workspace_size", "ec_partial_attn_plan", "ec_partial_attn", "ec_rope_table",
     "ec_forward_workspace_size", "ec_forward", "ec_state_plan_words", "ec_state_reset",
     "ec_step_workspace_size", "ec_step", "ec_timing_enable", "ec_timing_select", "ec_timing_read",
     "ec_last_error",
@@ -112,6 +112,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ec_entropy_max_noalloc": (C.c_int, [vp, C.c_int, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp]),
         "ec_cache_scatter": (C.c_int, [vp, vp, i64, i32, C.c_int, vp, vp, vp, i32, vp]),
         "ec_partial_attn_workspace_size": (sz, [i32, i32, i32, i32]),
+        "ec_partial_attn_plan": (C.c_int, [i32, i32, i32, i32, C.POINTER(i32), C.POINTER(i32)]),
         "ec_partial_attn": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, f32, C.c_int, vp, vp, sz, vp]),
         "ec_rope_table": (C.c_int, [vp, vp, i32, i32, C.c_double, vp]),
         "ec_forward_workspace_size": (sz, [C.POINTER(ec_model_desc), i32, i32, i32]),

@@ -10,7 +10,7 @@ from __future__ import annotations
 import ctypes as C
 import math
 from dataclasses import dataclass, field
-from typing import List, Optional, Sequence
+from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
@@ -152,6 +152,16 @@ def ec_partial_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                               float(scale), _dtype(q), _ptr(out), _ptr(ws), ws.numel(),
                               _stream(stream)), "ec_partial_attn")
     return out
+
+
+def ec_partial_attn_plan(r: int, seq_len: int, n_heads: int, head_dim: int = 128) -> Tuple[int, int]:
+    """(queries per workgroup, key splits) that the bf16 ec_partial_attn launches for
+    these sizes (host only)."""
+    lib = load()
+    qt, sp = C.c_int32(0), C.c_int32(0)
+    check(lib.ec_partial_attn_plan(r, seq_len, n_heads, head_dim, C.byref(qt), C.byref(sp)),
+          "ec_partial_attn_plan")
+    return qt.value, sp.value
 
 
 def ec_rope_table(max_pos: int, head_dim: int, base: float = 10000.0, device="cuda", stream=None):

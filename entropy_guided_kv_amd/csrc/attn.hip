@@ -26,17 +26,20 @@
 // rounded to bf16 for an integer M: the same rounded values for any tiling (the
 // row sum l takes the unrounded weights). All global
 // loads go straight into LDS (buffer_load_dwordx4 ... lds, no staging registers):
-// the 128-query Q tile once, issued with the first K/V tiles and then read into
-// registers for the whole loop, and the K and V tiles of 64 keys through a ring
-// of kStages LDS stages, so that the loads of the next kStages - 1 tiles are in
-// flight during the current tile's MFMAs (a split of up to kStages tiles issues
-// all of its loads at once). The tiles are shared by the
-// 8 wavefronts of a workgroup: 4 groups of 32 queries (128 queries), the two
-// wavefronts of a group taking the lower and the upper 32 keys of every tile
-// (two wavefronts per SIMD: one's softmax and LDS reads overlap the other's
-// MFMAs) and combining their (m, l, o) through LDS at the end. When heads x query tiles
-// under-fill the 256 CUs, the key range is split over workgroups and a merge
-// kernel combines (m, l, o) exactly.
+// the workgroup's Q tile once, issued with the first K/V tiles and then read into
+// registers for the whole loop, and the K and V tiles through a ring of LDS
+// stages, so that the loads of the next tiles are in flight during the current
+// tile's MFMAs (a split of no more tiles than stages issues all of its loads at
+// once). The tiles are shared by the 8 wavefronts of a workgroup (two per SIMD:
+// one's softmax and LDS reads overlap the other's MFMAs), in one of two shapes:
+//   wide:   4 groups of 32 queries (128 queries), 64-key tiles, 4 stages; the two
+//           wavefronts of a group take the lower and the upper 32 keys of a tile;
+//   narrow: 2 groups of 32 queries (64 queries), 128-key tiles, 2 stages; the four
+//           wavefronts of a group take one 32-key quarter of a tile each.
+// The wavefronts of a query group combine their (m, l, o) through LDS at the end.
+// A skip step's few hundred rows fill the 256 CUs with narrow workgroups and
+// whole key ranges; when heads x query tiles still under-fill them, the key range
+// is split over workgroups and a merge kernel combines (m, l, o) exactly.
 #include "ec_internal.h"
 
 #include <math.h>
@@ -46,10 +49,7 @@ namespace ec {
 namespace {
 
 constexpr int kThreads = 256;      // merge and fp32 kernels
-constexpr int kAttnThreads = 512;  // MFMA kernel: 8 wavefronts
 constexpr int D = 128;       // head_dim of the MFMA kernel
-constexpr int BQ = 128;      // queries per workgroup (32 per wavefront)
-constexpr int BKV = 64;      // keys per LDS stage
 constexpr int KS = D;        // LDS row stride (bf16): unpadded 256-byte rows, swizzled (below)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxFloor = -1e30f;  // below every reachable score in log2 units
@@ -59,14 +59,51 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) bf16 lds_bf16;
 
-constexpr int kStages = 4;                            // LDS ring of K/V tiles
-constexpr int kTileBytes = BKV * KS * 2;                // K (or V) of one tile
-constexpr int kVOff = kStages * kTileBytes;             // V stages after the K stages
-constexpr int kQOff = 2 * kStages * kTileBytes;         // Q tile (BQ rows of 256 bytes) after the ring
-constexpr int kHandBytes = 4 * 64 * (D / 2 + 2) * 4;    // (m, l, o) hand-over after the loop, over the ring
-constexpr int kAttnLds = kQOff + BQ * D * 2;
-static_assert(kHandBytes <= kQOff, "hand-over fits in the ring");
-static_assert(kAttnLds <= 160 * 1024, "LDS budget");
+// Workgroup shape of the MFMA kernel: QG groups of 32 queries x KG wavefronts per group, each
+// wavefront taking 32 keys of every K/V tile (BKV = 32 KG keys), over a ring of NSTG tiles.
+//   wide   (4 x 2, 4 stages): 128 queries, 64-key tiles; refresh-sized and long query sets
+//   narrow (2 x 4, 2 stages): 64 queries, 128-key tiles; the few hundred rows of a skip step,
+//          where 128-query tiles leave most CUs idle unless the keys are split (and merged)
+template <int QG_, int KG_, int NSTG_>
+struct AttnShape {
+  static constexpr int QG = QG_, KG = KG_, NSTG = NSTG_;
+  static constexpr int NW = QG * KG, NT = NW * 64;
+  static constexpr int BQ = 32 * QG;                        // queries per workgroup
+  static constexpr int BKV = 32 * KG;                       // keys per LDS stage
+  static constexpr int kTileBytes = BKV * KS * 2;           // K (or V) of one tile
+  static constexpr int kVOff = NSTG * kTileBytes;           // V stages after the K stages
+  static constexpr int kQOff = 2 * NSTG * kTileBytes;       // Q tile (BQ rows of 256 bytes) after the ring
+  static constexpr int kHandBytes = (KG - 1) * QG * 64 * (D / 2 + 2) * 4;  // (m, l, o) hand-over, over the ring
+  static constexpr int kLds = kQOff + BQ * D * 2;
+  static constexpr int SL = BKV / 4 / NW;                   // 1 KB slices of K (and of V) per wavefront per tile
+  static constexpr int kLoadsPerTile = 2 * SL;              // per wavefront
+  static constexpr int kQLoads = BQ * D * 2 / 1024 / NW;    // per wavefront
+  static_assert(kHandBytes <= kQOff, "hand-over fits in the ring");
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+  static_assert(SL >= 1 && SL * NW * 4 == BKV && kQLoads >= 1 && kQLoads * NW * 4 == BQ, "load split");
+  static_assert(kQLoads <= kLoadsPerTile && NSTG * kLoadsPerTile < 64, "the waits cover the Q loads and the ring");
+  static_assert((NSTG - 1) * kTileBytes < 65536, "stage offsets are 16-bit immediates");
+};
+using AttnWide = AttnShape<4, 2, 4>;
+using AttnNarrow = AttnShape<2, 4, 2>;
+// planning figures fitted to MI355X measurements: time per K/V tile of one wave of
+// workgroups, and the cost of a key split beyond its tiles (the merge launch, plus the
+// partials' round trip per split and query at 32 heads)
+constexpr double kWideTileUs = 0.9;
+constexpr double kNarrowTileUs = 1.14;
+constexpr double kMergeUs = 4.0;
+constexpr double kPartialUs = 0.008;
+
+// s_waitcnt vmcnt(min(n, K) * PER) for a wave-uniform run-time n >= 0
+template <int PER, int K>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if constexpr (K == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= K) wait_vmcnt<K * PER>();
+    else wait_tiles<PER, K - 1>(n);
+  }
+}
 
 // {x[l % 32], x[l % 32 + 32]} on every lane l: a lane's value and its partner's in the
 // other half of the wavefront, lower half first (v_permlane32_swap_b32, no LDS round trip)
@@ -76,17 +113,19 @@ __device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
   hi = __uint_as_float(r[1]);
 }
 
-// grid: (query tiles, heads, splits); dynamic LDS of kAttnLds bytes
-template <bool SPLIT>
-__global__ void __launch_bounds__(kAttnThreads)
+// grid: query tiles x heads x splits; dynamic LDS of SH::kLds bytes
+template <typename SH, bool SPLIT>
+__global__ void __launch_bounds__(SH::NT)
 attn_bf16_kernel(const bf16* __restrict__ q_all, const AttnSeqs seqs, int L, int H, float scale_log2,
                  int kv_chunk, int nsplit, int r_all, bf16* __restrict__ out_all, float* __restrict__ po,
                  float* __restrict__ pml) {
-  // K and V tiles in natural [key][dim] layout, one stage per tile of the ring: the four
-  // K stages in the first 64 KB, the four V stages in the next, so that with the tile loop
-  // unrolled over the stages every fragment read is a per-lane base register (computed
-  // once) plus an immediate offset below 64 KB. After the loop the LDS holds the
-  // (m, l, o) hand-over.
+  // K and V tiles in natural [key][dim] layout, one stage per tile of the ring: the K
+  // stages first, then the V stages, so that with the tile loop unrolled over the stages
+  // every fragment read is a per-lane base register (computed once) plus an immediate
+  // offset below 64 KB. After the loop the LDS holds the (m, l, o) hand-over.
+  constexpr int QG = SH::QG, KG = SH::KG, NW = SH::NW, BQ = SH::BQ, BKV = SH::BKV, SL = SH::SL;
+  constexpr int kStages = SH::NSTG, kTileBytes = SH::kTileBytes, kVOff = SH::kVOff, kQOff = SH::kQOff;
+  constexpr int kLoadsPerTile = SH::kLoadsPerTile, kQLoads = SH::kQLoads;
   // LDS layout (64 banks of 4 bytes): a K row keeps its 16-byte chunk c at c ^ (row % 16), so the
   // 16 rows one b128 fragment read serves per cycle hit 16 distinct bank groups; a V row keeps
   // its 64-byte quarter q (dims 32q .. 32q+31) at q ^ (row % 4), so the four consecutive keys of
@@ -113,7 +152,7 @@ attn_bf16_kernel(const bf16* __restrict__ q_all, const AttnSeqs seqs, int L, int
   bf16* __restrict__ out = SPLIT ? nullptr : out_all + (int64_t)row0 * H * D;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int qw = wave % 4, kh = wave / 4;   // query group, key half of every tile
+  const int qw = wave % QG, kh = wave / QG;  // query group, 32-key part of every tile
   const int lq = lane % 32, g = lane / 32;
   const int64_t HD = (int64_t)H * D;
   const int qrow = qt * BQ + qw * 32 + lq;  // this lane's query (column of S^T)
@@ -123,14 +162,13 @@ attn_bf16_kernel(const bf16* __restrict__ q_all, const AttnSeqs seqs, int L, int
   {
     const __amdgpu_buffer_rsrc_t rQ = buffer_rsrc(q, (int64_t)r * HD * 2);
 #pragma unroll
-    for (int i = 0; i < BQ * D * 2 / 1024 / 8; ++i) {
-      const int sl = i * 8 + wave, row = 4 * sl + lane / 16, pos = lane % 16;
+    for (int i = 0; i < kQLoads; ++i) {
+      const int sl = i * NW + wave, row = 4 * sl + lane / 16, pos = lane % 16;
       const int qr = min(qt * BQ + row, r - 1);
       buffer_load_lds16(rQ, lds_raw + kQOff + sl * 1024,
                         (int)(((int64_t)qr * HD + h * D) * 2) + (pos ^ (row & 15)) * 16, 0);
     }
   }
-  constexpr int kQLoads = BQ * D * 2 / 1024 / 8;  // per wavefront
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -147,17 +185,17 @@ attn_bf16_kernel(const bf16* __restrict__ q_all, const AttnSeqs seqs, int L, int
   const int kv_hi = min(L, kv_lo + kv_chunk);
   const int ntiles = (kv_hi - kv_lo + BKV - 1) / BKV;
 
-  // a tile is 16 KB of K and 16 KB of V: 16 slices of 1 KB (4 rows of 256 bytes) each;
-  // wavefront w loads slices w and 8 + w of both. Lane l of a slice load fills bytes
+  // a tile is BKV / 4 slices of 1 KB (4 rows of 256 bytes) of K and as many of V;
+  // wavefront w loads slices w, NW + w, ... of both. Lane l of a slice load fills bytes
   // 16 l of the slice, i.e. tile row 4 s + l / 16 at position l % 16, and fetches the
   // 16-byte chunk that the swizzle puts there. Keys past the cache end re-read row L - 1
   // (masked below).
   const __amdgpu_buffer_rsrc_t rK = buffer_rsrc(kc, (int64_t)L * HD * 2);
   const __amdgpu_buffer_rsrc_t rV = buffer_rsrc(vc, (int64_t)L * HD * 2);
-  int lrow[2], ok_[2], ov_[2];
+  int lrow[SL], ok_[SL], ov_[SL];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int sl = i * 8 + wave, row = 4 * sl + lane / 16, pos = lane % 16;
+  for (int i = 0; i < SL; ++i) {
+    const int sl = i * NW + wave, row = 4 * sl + lane / 16, pos = lane % 16;
     lrow[i] = row;
     const int ck = (pos ^ (row & 15)) * 16;  // bytes within the row
     const int cv = ((((pos >> 2) ^ (row & 3)) << 2) | (pos & 3)) * 16;
@@ -174,21 +212,20 @@ attn_bf16_kernel(const bf16* __restrict__ q_all, const AttnSeqs seqs, int L, int
     if (kv0 + BKV <= L) {
       const int so = (int)((int64_t)kv0 * HD * 2);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        buffer_load_lds16(rK, sk + (i * 8 + wave) * 1024, ok_[i], so);
-        buffer_load_lds16(rV, sv + (i * 8 + wave) * 1024, ov_[i], so);
+      for (int i = 0; i < SL; ++i) {
+        buffer_load_lds16(rK, sk + (i * NW + wave) * 1024, ok_[i], so);
+        buffer_load_lds16(rV, sv + (i * NW + wave) * 1024, ov_[i], so);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < SL; ++i) {
         const int key = min(kv0 + lrow[i], L - 1);
         const int d0 = (int)(((int64_t)(key - lrow[i]) * HD) * 2);
-        buffer_load_lds16(rK, sk + (i * 8 + wave) * 1024, ok_[i] + d0, 0);
-        buffer_load_lds16(rV, sv + (i * 8 + wave) * 1024, ov_[i] + d0, 0);
+        buffer_load_lds16(rK, sk + (i * NW + wave) * 1024, ok_[i] + d0, 0);
+        buffer_load_lds16(rV, sv + (i * NW + wave) * 1024, ov_[i] + d0, 0);
       }
     }
   };
-  constexpr int kLoadsPerTile = 4;  // per wavefront
 
   // transpose-read coordinates for the V^T operand: within each 16-lane group, source lane
   // s points at (key base + s/4, dim base + 4 (s%4)); ds_read_tr16_b64 then hands lane j the
@@ -201,13 +238,7 @@ attn_bf16_kernel(const bf16* __restrict__ q_all, const AttnSeqs seqs, int L, int
     if (t < issued) issue(t, t);
   // Q fragments (B operand of S^T): Q[qrow][16kk + 8g .. +7], read once the Q loads (older
   // than every tile's) have landed in every wavefront
-  switch (issued) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<kLoadsPerTile>(); break;
-    case 2: wait_vmcnt<2 * kLoadsPerTile>(); break;
-    case 3: wait_vmcnt<3 * kLoadsPerTile>(); break;
-    default: wait_vmcnt<4 * kLoadsPerTile>(); break;
-  }
+  wait_tiles<kLoadsPerTile, kStages>(issued);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -237,13 +268,7 @@ attn_bf16_kernel(const bf16* __restrict__ q_all, const AttnSeqs seqs, int L, int
     // the tiles issued after t are outstanding; the barrier then publishes every
     // wavefront's share, and tells that all have finished tile t - 1, whose stage is
     // refilled with tile t - 1 + kStages
-    switch (issued - t - 1) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<kLoadsPerTile>(); break;
-      case 2: wait_vmcnt<2 * kLoadsPerTile>(); break;
-      default: wait_vmcnt<3 * kLoadsPerTile>(); break;
-    }
-    static_assert(kStages == 4 && kQLoads <= kLoadsPerTile, "the waits cover up to four tiles in flight");
+    wait_tiles<kLoadsPerTile, kStages - 1>(issued - t - 1);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -338,30 +363,36 @@ attn_bf16_kernel(const bf16* __restrict__ q_all, const AttnSeqs seqs, int L, int
   }
   __syncthreads();  // every wavefront is done with the last tile; no loads are outstanding
 
-  // the upper-key wavefront of each query group hands (m, l, o) to the lower one through
-  // LDS
-  {
-    float* xb = reinterpret_cast<float*>(lds_raw) + (qw * 64 + lane) * (D / 2 + 2);
-    if (kh == 1) {
+  // the wavefronts of each query group that took keys 32 .. BKV - 1 of the tiles hand their
+  // (m, l, o) to the one that took keys 0 .. 31 through LDS, which merges them in key order
+  if constexpr (KG > 1) {
+    constexpr int XS = D / 2 + 2;  // floats per lane: 64 of o, m, l
+    float* xb = reinterpret_cast<float*>(lds_raw);
+    if (kh > 0) {
+      float* x = xb + (((kh - 1) * QG + qw) * 64 + lane) * XS;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) xb[16 * i + v] = o[i][v];
-      xb[D / 2] = m_ref;
-      xb[D / 2 + 1] = l_run;
+        for (int v = 0; v < 16; ++v) x[16 * i + v] = o[i][v];
+      x[D / 2] = m_ref;
+      x[D / 2 + 1] = l_run;
     }
     __syncthreads();
-    if (kh == 1) return;
-    const float m2 = xb[D / 2], l2 = xb[D / 2 + 1];
-    const float mm = fmaxf(m_ref, m2);
-    const float a1 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
-    const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+    if (kh > 0) return;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
+    for (int k = 1; k < KG; ++k) {
+      const float* x = xb + (((k - 1) * QG + qw) * 64 + lane) * XS;
+      const float m2 = x[D / 2], l2 = x[D / 2 + 1];
+      const float mm = fmaxf(m_ref, m2);
+      const float a1 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
+      const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][v] = o[i][v] * a1 + xb[16 * i + v] * a2;
-    l_run = l_run * a1 + l2 * a2;
-    m_ref = mm;
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] = o[i][v] * a1 + x[16 * i + v] * a2;
+      l_run = l_run * a1 + l2 * a2;
+      m_ref = mm;
+    }
   }
   if (!qok) return;
   // o[i][v]: dim = 32i + 8(v/4) + 4g + v%4 of query qrow
@@ -595,45 +626,89 @@ attn_f32_mfma_kernel(const float* __restrict__ q_all, const AttnSeqs seqs, int L
 }
 
 struct AttnPlan {
+  bool narrow;  // AttnNarrow workgroups (64 queries) instead of AttnWide (128)
   int splits, chunk;
 };
 
-// Key-range split by a cost model fitted to MI355X measurements of every split count
-// (r = 17 .. 4096 queries, L = 1024 and 4096, 32 heads; it picks the fastest on each):
-// waves of workgroups x tiles per workgroup x 0.9 us, plus, when split, 0.008 us per
-// (split x query) for the partials' round trip and merge (scaled by H / 32). r is the
-// number of query rows and qtiles the number of 128-query tiles over every sequence of
-// the launch; splits whose partials would not fit max_ws bytes are skipped.
-AttnPlan plan_attn(int r, int qtiles, int L, int H, size_t max_ws = (size_t)-1) {
-  AttnPlan p;
-  const int base = qtiles * H;
+// Workgroup shape and key-range split by a cost model fitted to MI355X measurements of
+// every shape and split count (r = 17 .. 4096 queries, L = 1024 and 4096, 32 heads; the
+// fastest candidate or one within 5 % of it on each): waves of workgroups x tiles per
+// workgroup x the shape's time per tile, plus, when split, the merge launch and the
+// partials' round trip per (split x query), scaled by H / 32. The narrow shape wins from
+// 17 to about 600 query rows (skip steps), the wide one above. r is the number of query
+// rows over every sequence of the launch and qt_wide / qt_narrow its number of query tiles
+// for each shape; splits whose partials would not fit max_ws bytes are skipped.
+AttnPlan plan_attn(int r, int qt_wide, int qt_narrow, int L, int H, size_t max_ws = (size_t)-1) {
+  AttnPlan best_p{false, 1, 0};
   double best = 1e300;
-  int s_best = 1;
-  for (int s : {1, 2, 3, 4, 6, 8, 12, 16}) {
-    if (s > 1 && L / s < BKV) break;
-    const int chunk = ((L + s - 1) / s + BKV - 1) / BKV * BKV;
-    const int splits = (L + chunk - 1) / chunk;
-    if (splits > 1 && (size_t)splits * r * H * (D + 2) * sizeof(float) + 512 > max_ws) continue;
-    const double waves = (double)(((int64_t)base * splits + 255) / 256);
-    double us = waves * (chunk / BKV) * 0.9;
-    if (splits > 1) us += 0.008 * splits * r * (H / 32.0);
-    if (us < best) {
-      best = us;
-      s_best = s;
+  for (int nar = 0; nar < 2; ++nar) {
+    const int bkv = nar ? AttnNarrow::BKV : AttnWide::BKV;
+    const int base = (nar ? qt_narrow : qt_wide) * H;
+    const double tile_us = nar ? kNarrowTileUs : kWideTileUs;
+    for (int s : {1, 2, 3, 4, 6, 8, 12, 16}) {
+      if (s > 1 && L / s < bkv) break;
+      const int chunk = ((L + s - 1) / s + bkv - 1) / bkv * bkv;
+      const int splits = (L + chunk - 1) / chunk;
+      if (splits > 1 && (size_t)splits * r * H * (D + 2) * sizeof(float) + 512 > max_ws) continue;
+      const double waves = (double)(((int64_t)base * splits + 255) / 256);
+      double us = waves * (chunk / bkv) * tile_us;
+      if (splits > 1) us += kMergeUs + kPartialUs * splits * r * (H / 32.0);
+      if (us < best) {
+        best = us;
+        best_p = AttnPlan{nar != 0, splits, chunk};
+      }
     }
   }
-  p.chunk = ((L + s_best - 1) / s_best + BKV - 1) / BKV * BKV;
-  p.splits = (L + p.chunk - 1) / p.chunk;
-  return p;
+  return best_p;
+}
+
+template <typename SH>
+ec_status launch_attn(const AttnPlan& p, const bf16* q, const AttnSeqs& seqs, int L, int H, float sl, int r,
+                      int qtiles, void* out, void* ws, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)qtiles * H * p.splits);
+  // one limit record per kernel (the two instantiations share a function type)
+  static LdsLimit whole, split;
+  const ec_status st = p.splits == 1 ? whole.ensure((const void*)attn_bf16_kernel<SH, false>, SH::kLds)
+                                     : split.ensure((const void*)attn_bf16_kernel<SH, true>, SH::kLds);
+  if (st != EC_OK) return st;
+  if (p.splits == 1) {
+    attn_bf16_kernel<SH, false><<<grid, SH::NT, SH::kLds, s>>>(q, seqs, L, H, sl, p.chunk, 1, r, (bf16*)out,
+                                                              nullptr, nullptr);
+    EC_CHECK_LAUNCH("attn_bf16_kernel");
+    return EC_OK;
+  }
+  float* po = (float*)ws;
+  float* pml = po + (size_t)p.splits * r * H * D;
+  attn_bf16_kernel<SH, true><<<grid, SH::NT, SH::kLds, s>>>(q, seqs, L, H, sl, p.chunk, p.splits, r, nullptr, po,
+                                                           pml);
+  EC_CHECK_LAUNCH("attn_bf16_kernel");
+  bf16* o = (bf16*)out;
+  switch (p.splits) {
+#define EC_MERGE_CASE(n) \
+  case n: return launch_merge<n>(po, pml, p.splits, r, H, D, o, s);
+    EC_MERGE_CASE(2) EC_MERGE_CASE(3) EC_MERGE_CASE(4) EC_MERGE_CASE(5) EC_MERGE_CASE(6) EC_MERGE_CASE(7)
+    EC_MERGE_CASE(8) EC_MERGE_CASE(9) EC_MERGE_CASE(10) EC_MERGE_CASE(11) EC_MERGE_CASE(12)
+    EC_MERGE_CASE(13) EC_MERGE_CASE(14) EC_MERGE_CASE(15) EC_MERGE_CASE(16)
+#undef EC_MERGE_CASE
+    default: return launch_merge<-1>(po, pml, p.splits, r, H, D, o, s);
+  }
 }
 
 }  // namespace
 
 size_t attn_ws_bytes(int r, int L, int H, int Dh) {
   if (r <= 0 || Dh != D) return 0;
-  AttnPlan p = plan_attn(r, (r + BQ - 1) / BQ, L, H);
+  const AttnPlan p = plan_attn(r, (r + AttnWide::BQ - 1) / AttnWide::BQ, (r + AttnNarrow::BQ - 1) / AttnNarrow::BQ,
+                               L, H);
   if (p.splits <= 1) return 0;
   return (size_t)p.splits * r * H * (Dh + 2) * sizeof(float) + 512;
+}
+
+void attn_plan_query(int r, int L, int H, int* query_tile, int* splits) {
+  const AttnPlan p = plan_attn(r, (r + AttnWide::BQ - 1) / AttnWide::BQ, (r + AttnNarrow::BQ - 1) / AttnNarrow::BQ,
+                               L, H);
+  *query_tile = p.narrow ? AttnNarrow::BQ : AttnWide::BQ;
+  *splits = p.splits;
 }
 
 ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, int L, int H,
@@ -647,12 +722,13 @@ ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, 
 ec_status attn_batch(ec_dtype dt, const void* q, const AttnSeqs& seqs, int L, int H, int Dh, float scale, void* out,
                      void* ws, size_t ws_bytes, hipStream_t s) {
   EC_REQUIRE(seqs.n >= 1 && seqs.n <= EC_MAX_SEQ, EC_ERR_ARG, "attn: %d sequences", seqs.n);
-  int r = 0, qtiles = 0;
+  int r = 0, qt_wide = 0, qt_narrow = 0;
   for (int i = 0; i < seqs.n; ++i) {
     EC_REQUIRE(seqs.s[i].nr >= 0 && seqs.s[i].row0 == r, EC_ERR_ARG, "attn: sequence %d rows not contiguous", i);
     EC_REQUIRE(seqs.s[i].nr == 0 || (seqs.s[i].k && seqs.s[i].v), EC_ERR_ARG, "attn: null cache of sequence %d", i);
     r += seqs.s[i].nr;
-    qtiles += (seqs.s[i].nr + BQ - 1) / BQ;
+    qt_wide += (seqs.s[i].nr + AttnWide::BQ - 1) / AttnWide::BQ;
+    qt_narrow += (seqs.s[i].nr + AttnNarrow::BQ - 1) / AttnNarrow::BQ;
   }
   if (r == 0) return EC_OK;
   EC_REQUIRE(L >= 1, EC_ERR_ARG, "attn: seq_len must be >= 1");
@@ -683,34 +759,10 @@ ec_status attn_batch(ec_dtype dt, const void* q, const AttnSeqs& seqs, int L, in
   // q and the caches are addressed through buffer resources with 32-bit byte offsets
   EC_REQUIRE((int64_t)(L > r ? L : r) * H * Dh * 2 <= 0x7fffffff, EC_ERR_UNSUPPORTED,
              "attn: %d rows of %d x %d bf16 exceed the 2 GiB buffer range", L > r ? L : r, H, Dh);
-  const AttnPlan p = plan_attn(r, qtiles, L, H, ws ? ws_bytes : 0);
+  const AttnPlan p = plan_attn(r, qt_wide, qt_narrow, L, H, ws ? ws_bytes : 0);
   const float sl = scale * kLog2e;
-  const unsigned grid = (unsigned)((int64_t)qtiles * H * p.splits);
-  static LdsLimit whole, split;
-  ec_status st = p.splits == 1 ? whole.ensure((const void*)attn_bf16_kernel<false>, kAttnLds)
-                               : split.ensure((const void*)attn_bf16_kernel<true>, kAttnLds);
-  if (st != EC_OK) return st;
-  if (p.splits == 1) {
-    attn_bf16_kernel<false><<<grid, kAttnThreads, kAttnLds, s>>>((const bf16*)q, seqs, L, H, sl, p.chunk, 1, r,
-                                                                (bf16*)out, nullptr, nullptr);
-    EC_CHECK_LAUNCH("attn_bf16_kernel");
-    return EC_OK;
-  }
-  float* po = (float*)ws;
-  float* pml = po + (size_t)p.splits * r * H * Dh;
-  attn_bf16_kernel<true><<<grid, kAttnThreads, kAttnLds, s>>>((const bf16*)q, seqs, L, H, sl, p.chunk, p.splits, r,
-                                                             nullptr, po, pml);
-  EC_CHECK_LAUNCH("attn_bf16_kernel");
-  bf16* o = (bf16*)out;
-  switch (p.splits) {
-#define EC_MERGE_CASE(n) \
-  case n: return launch_merge<n>(po, pml, p.splits, r, H, Dh, o, s);
-    EC_MERGE_CASE(2) EC_MERGE_CASE(3) EC_MERGE_CASE(4) EC_MERGE_CASE(5) EC_MERGE_CASE(6) EC_MERGE_CASE(7)
-    EC_MERGE_CASE(8) EC_MERGE_CASE(9) EC_MERGE_CASE(10) EC_MERGE_CASE(11) EC_MERGE_CASE(12)
-    EC_MERGE_CASE(13) EC_MERGE_CASE(14) EC_MERGE_CASE(15) EC_MERGE_CASE(16)
-#undef EC_MERGE_CASE
-    default: return launch_merge<-1>(po, pml, p.splits, r, H, Dh, o, s);
-  }
+  if (p.narrow) return launch_attn<AttnNarrow>(p, (const bf16*)q, seqs, L, H, sl, r, qt_narrow, out, ws, s);
+  return launch_attn<AttnWide>(p, (const bf16*)q, seqs, L, H, sl, r, qt_wide, out, ws, s);
 }
 
 }  // namespace ec

@@ -678,6 +678,18 @@ size_t ec_partial_attn_workspace_size(int32_t r, int32_t seq_len, int32_t n_head
   return attn_ws_bytes(r, seq_len, n_heads, head_dim);
 }
 
+ec_status ec_partial_attn_plan(int32_t r, int32_t seq_len, int32_t n_heads, int32_t head_dim,
+                               int32_t* query_tile, int32_t* splits) {
+  EC_REQUIRE(query_tile && splits, EC_ERR_ARG, "ec_partial_attn_plan: null output");
+  EC_REQUIRE(r >= 1 && seq_len >= 1 && n_heads >= 1, EC_ERR_ARG, "ec_partial_attn_plan: bad sizes");
+  EC_REQUIRE(head_dim == 128, EC_ERR_UNSUPPORTED, "ec_partial_attn_plan: the bf16 path needs head_dim 128");
+  int qt = 0, sp = 0;
+  attn_plan_query(r, seq_len, n_heads, &qt, &sp);
+  *query_tile = qt;
+  *splits = sp;
+  return EC_OK;
+}
+
 ec_status ec_partial_attn(const void* q, const void* k_cache, const void* v_cache, int32_t r,
                           int32_t seq_len, int32_t n_heads, int32_t head_dim, float scale,
                           ec_dtype dtype, void* out, void* workspace, size_t workspace_bytes,

@@ -194,6 +194,8 @@ struct AttnSeqs {
   int n;
 };
 size_t attn_ws_bytes(int r, int L, int H, int D);
+// bf16 launch plan of one sequence's attention: queries per workgroup and key splits
+void attn_plan_query(int r, int L, int H, int* query_tile, int* splits);
 ec_status attn(ec_dtype dt, const void* q, const void* k, const void* v, int r, int L, int H, int D,
                float scale, void* out, void* ws, size_t ws_bytes, hipStream_t s);
 // every sequence's rows in one launch (plus one merge launch when the keys are split)

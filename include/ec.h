@@ -149,6 +149,17 @@ ec_status ec_partial_attn(const void* q, const void* k_cache, const void* v_cach
                           ec_dtype dtype, void* out, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* ec_partial_attn_plan -- the launch plan of the bf16 path of ec_partial_attn for
+ * these sizes (host only, no device work): *query_tile = queries per workgroup
+ * (64 for the skip-step shape, 128 for the refresh-sized one), *splits = key-range
+ * splits merged after the launch (1 = none). Workgroups = ceil(r / query_tile) *
+ * n_heads * splits. For diagnostics and tests; ec_partial_attn takes the same plan
+ * with its workspace at least ec_partial_attn_workspace_size(...) bytes.
+ * Errors: EC_ERR_ARG for null outputs or sizes < 1, EC_ERR_UNSUPPORTED for
+ * head_dim != 128. */
+ec_status ec_partial_attn_plan(int32_t r, int32_t seq_len, int32_t n_heads, int32_t head_dim,
+                               int32_t* query_tile, int32_t* splits);
+
 /* ------------------------------------------------------------------------
  * Model, cache and decoding descriptors (plain structs; struct_size must be
  * set to sizeof(the struct) by the caller).

@@ -55,6 +55,48 @@ def test_workspace_queries_are_host_only(lib):
     assert lib.ec_state_plan_words(0, 16) == 0
 
 
+def test_attention_plan_query(lib):
+    """Host-only launch plan of the bf16 attention: the 64-query shape over whole key ranges
+    for the few hundred rows of a skip step at 32 heads, the 128-query shape at refresh size,
+    key splits only where the query tiles leave CUs idle, and the workspace query agreeing."""
+    def plan(r, L, H):
+        qt, sp = C.c_int32(0), C.c_int32(0)
+        assert lib.ec_partial_attn_plan(r, L, H, 128, C.byref(qt), C.byref(sp)) == _lib.EC_OK
+        return qt.value, sp.value
+    for r in (96, 128, 147, 256, 384, 512):
+        assert plan(r, 1024, 32) == (64, 1)
+    assert plan(1024, 1024, 32) == (128, 1)
+    assert plan(4096, 4096, 32)[0] == 128
+    qt, sp = plan(17, 1024, 32)
+    assert qt == 64 and sp > 1  # one query tile per head: the keys are split to fill the CUs
+    for r, L, H in ((1, 1024, 32), (17, 1024, 32), (256, 1024, 32), (1024, 1024, 32), (40, 700, 8),
+                    (3, 1250, 2), (1, 33, 1)):
+        qt, sp = plan(r, L, H)
+        ws = lib.ec_partial_attn_workspace_size(r, L, H, 128)
+        assert (ws > 0) == (sp > 1)
+        if sp > 1:
+            assert ws >= sp * r * H * 130 * 4
+    qt, sp = C.c_int32(0), C.c_int32(0)
+    assert lib.ec_partial_attn_plan(16, 1024, 32, 64, C.byref(qt), C.byref(sp)) == _lib.EC_ERR_UNSUPPORTED
+    assert lib.ec_partial_attn_plan(0, 1024, 32, 128, C.byref(qt), C.byref(sp)) == _lib.EC_ERR_ARG
+    assert lib.ec_partial_attn_plan(16, 1024, 32, 128, None, C.byref(sp)) == _lib.EC_ERR_ARG
+
+
+def test_bf16_attention_cases_cover_both_shapes():
+    """Host only: the bf16 cases of the attention parity test reach both workgroup shapes, with and without key
+    splits, every merge width from 2 to 16, and caches shorter than one tile."""
+    import entropy_guided_kv_amd as ek
+    from tests.test_gpu_attn_scatter import BF16_ATTN_CASES
+    plans = {c: ek.ec_partial_attn_plan(*c) for c in BF16_ATTN_CASES}
+    narrow = {sp for (qt, sp) in plans.values() if qt == 64}
+    wide = {sp for (qt, sp) in plans.values() if qt == 128}
+    assert 1 in narrow and len(narrow - {1}) >= 4, plans
+    assert 1 in wide and len(wide - {1}) >= 8, plans
+    assert set(range(2, 17)) <= (narrow | wide), plans
+    assert plans[(150, 65, 4)] == (64, 1) and plans[(100, 97, 8)] == (64, 1)
+    assert plans[(7, 29, 3)] == (128, 1) and plans[(1024, 1024, 32)] == (128, 1)
+
+
 def _model_desc(dtype=_lib.EC_BF16, d=4096, H=32, Dh=128, F=12288, V=126464, n_layers=32):
     lw = (_lib.ec_layer_weights * n_layers)()
     for i in range(n_layers):

@@ -70,17 +70,31 @@ def _attn_case(r, L, H, D, dtype, seed=0, scale=1.0, misalign=False):
     return to_f64(out), want
 
 
-@pytest.mark.parametrize("r,L,H", [(143, 1024, 4), (1, 1024, 2), (257, 512, 3), (128, 128, 1),
-                                   (17, 1000, 2), (1024, 1024, 2), (33, 4096, 2),
-                                   (40, 700, 8), (96, 900, 24),
-                                   # with the split cost model of the kernel these take 3, 7, 9,
-                                   # 10, 11, 12, 13, 14 and 15 key splits (most with a ragged last
-                                   # tile), so that every merge width is compared with the oracle
-                                   (1, 192, 1), (1, 769, 1), (1, 1025, 1), (3, 1250, 2), (5, 1400, 3),
-                                   (2, 768, 1), (1, 1600, 1), (1, 1700, 1), (1, 1800, 1),
-                                   # caches of 1, 29 and 33 rows: the upper-key wavefront of the
-                                   # only tile sees no key (or one), whose softmax terms must be 0
-                                   (4, 1, 2), (7, 29, 3), (1, 33, 1)])
+# bf16 cases; with the launch planner of the library (ec_partial_attn_plan) they take:
+#   64-query workgroups, whole key range: (147, 1024, 32), (256, 1024, 32), (257, 512, 3),
+#     (128, 128, 1), (100, 97, 8) and (150, 65, 4) (a 128-key tile over a cache of 97 or 65
+#     rows: its last 32-key quarter, or last two, see one key or none, whose softmax terms
+#     must be 0);
+#   64-query workgroups with 2 .. 16 key splits: (200, 1800, 24), (17, 1024, 32), (64, 1024, 32),
+#     (143, 1024, 4), (1024, 1024, 2), (96, 900, 24), (65, 1025, 32), (1, 1025, 32) and
+#     (70, 2500, 2) (ragged last tiles), (33, 4096, 2);
+#   128-query workgroups, whole key range: (1024, 1024, 32), (4, 1, 2), (7, 29, 3), (1, 33, 1)
+#     (caches of 1, 29 and 33 rows: the upper-key wavefront of the only tile sees no key or
+#     one);
+#   128-query workgroups with 4 .. 15 key splits: (200, 4096, 32), (17, 1000, 2), (40, 700, 8)
+#     and, one per merge width, (1, 769, 1), (1, 1025, 1), (3, 1250, 2), (5, 1400, 3),
+#     (2, 768, 1), (1, 1600, 1), (1, 1700, 1), (1, 1800, 1) (most with a ragged last tile).
+# test_abi.py::test_bf16_attention_cases_cover_both_shapes checks this coverage on the host.
+BF16_ATTN_CASES = [(147, 1024, 32), (256, 1024, 32), (257, 512, 3), (128, 128, 1), (100, 97, 8), (150, 65, 4),
+                   (200, 1800, 24), (17, 1024, 32), (64, 1024, 32), (143, 1024, 4), (1024, 1024, 2),
+                   (96, 900, 24), (65, 1025, 32), (1, 1025, 32), (70, 2500, 2), (33, 4096, 2),
+                   (1024, 1024, 32), (4, 1, 2), (7, 29, 3), (1, 33, 1),
+                   (200, 4096, 32), (17, 1000, 2), (40, 700, 8), (1, 1024, 2),
+                   (1, 769, 1), (1, 1025, 1), (3, 1250, 2), (5, 1400, 3), (2, 768, 1), (1, 1600, 1),
+                   (1, 1700, 1), (1, 1800, 1)]
+
+
+@pytest.mark.parametrize("r,L,H", BF16_ATTN_CASES)
 def test_partial_attn_bf16(r, L, H):
     got, want = _attn_case(r, L, H, 128, torch.bfloat16, seed=r + L, scale=0.35)
     err = row_rel_err(got.reshape(r * H, 128), want.reshape(r * H, 128))
