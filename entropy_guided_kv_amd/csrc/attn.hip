@@ -631,11 +631,11 @@ struct AttnPlan {
 };
 
 // Workgroup shape and key-range split by a cost model fitted to MI355X measurements of
-// every shape and split count (r = 17 .. 4096 queries, L = 1024 and 4096, 32 heads; the
-// fastest candidate or one within 5 % of it on each): waves of workgroups x tiles per
-// workgroup x the shape's time per tile, plus, when split, the merge launch and the
-// partials' round trip per (split x query), scaled by H / 32. The narrow shape wins from
-// 17 to about 600 query rows (skip steps), the wide one above. r is the number of query
+// every shape and split count (r = 17 .. 4096 queries, L = 1024 and 4096, 32 heads, K/V
+// warm and cold; it picks the fastest candidate or one within 6 % of it on each): waves of
+// workgroups x tiles per workgroup x the shape's time per tile, plus, when split, the
+// merge launch and the partials' round trip per (split x query), scaled by H / 32. The
+// narrow shape wins from 17 to about 600 query rows (skip steps), the wide one above. r is the number of query
 // rows over every sequence of the launch and qt_wide / qt_narrow its number of query tiles
 // for each shape; splits whose partials would not fit max_ws bytes are skipped.
 AttnPlan plan_attn(int r, int qt_wide, int qt_narrow, int L, int H, size_t max_ws = (size_t)-1) {
