@@ -248,8 +248,9 @@ attn_bf16_kernel(const bf16* __restrict__ q_all, const AttnSeqs seqs, int L, int
     fq[kk] = *reinterpret_cast<const bf16x8*>(lds_raw + kQOff + (qw * 32 + lq) * (D * 2) +
                                                (((2 * kk + g) ^ (lq & 15)) * 16));
   // per-lane LDS offsets of the fragment reads (the stage adds an immediate): the V ones
-  // carry the V region's 64 KB themselves, passed through an empty asm so that the
-  // compiler keeps it in the register and the stage offset stays a 16-bit immediate
+  // carry the V region's offset (64 KB in both shapes) themselves, passed through an empty
+  // asm so that the compiler keeps it in the register and the stage offset stays a 16-bit
+  // immediate
   int koff[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) koff[kk] = ((kh * 32 + lq) * KS + (((2 * kk + g) ^ (lq & 15)) * 8)) * 2;
