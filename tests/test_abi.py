@@ -187,6 +187,14 @@ def test_argument_errors_return_before_any_gpu_work(lib):
     assert lib.ec_cache_scatter(None, None, 10, 8, E.EC_F32, None, None, None, 3, None) == E.EC_ERR_ARG
     assert lib.ec_cache_scatter(None, None, 10, 8, E.EC_F32, None, None, None, 0, None) == E.EC_OK
     assert lib.ec_partial_attn(None, None, None, 4, 16, 2, 128, 1.0, E.EC_BF16, None, None, 0, None) == E.EC_ERR_ARG
+    # sizes past the kernels' 32-bit buffer offsets (2 GiB per cache) and head sizes the bf16
+    # kernel does not take: refused before anything is enqueued (fake pointers, never read)
+    big = lib.ec_partial_attn_workspace_size(1, 1 << 17, 128, 128)
+    assert lib.ec_partial_attn(0x1000, 0x1000, 0x1000, 1, 1 << 17, 128, 128, 1.0, E.EC_BF16, 0x1000, 0x1000,
+                               big, None) == E.EC_ERR_UNSUPPORTED
+    assert b"2 GiB" in lib.ec_last_error()
+    assert lib.ec_partial_attn(0x1000, 0x1000, 0x1000, 4, 16, 2, 64, 1.0, E.EC_BF16, 0x1000, None, 0,
+                               None) == E.EC_ERR_UNSUPPORTED
     assert lib.ec_step(None, None, None, None, None, 0, None, None) == E.EC_ERR_ARG
     assert b"model" in lib.ec_last_error()
     m, _keep = _model_desc()
