@@ -181,6 +181,33 @@ def new_cache(model: OracleModel, seq_len: int) -> List[List[np.ndarray]]:
     return [[np.zeros((seq_len, d)), np.zeros((seq_len, d))] for _ in range(model.n_layers)]
 
 
+def layer_forward(model: OracleModel, li: int, h: np.ndarray, rows: np.ndarray, kv) -> np.ndarray:
+    """One transformer block (EntropyCache explainer, Italian summary section 1: bidirectional
+    attention, no mask) for the residual rows ``h`` [r, d] at positions ``rows``: RMSNorm, q/k/v
+    with RoPE at the rows' positions, the rows' K/V written into the layer's cache ``kv`` = [K, V]
+    ([L, d] each) before the queries attend over all L rows, O-projection and residual, RMSNorm,
+    SwiGLU MLP and residual. Returns the residual stream after the block."""
+    m = model.shape
+    d, H, D = m.d_model, m.n_heads, m.head_dim
+    r = len(rows)
+    rnd = model.rnd
+    lw = model.layer(li)
+    K, V = kv
+    a = rnd(rmsnorm(h, lw["attn_norm"], m.rms_eps))
+    qkv = a @ lw["wqkv"].T
+    q = rnd(rope(qkv[:, :d].reshape(r, H, D), rows, m.rope_base))
+    k = rnd(rope(qkv[:, d:2 * d].reshape(r, H, D), rows, m.rope_base))
+    v = rnd(qkv[:, 2 * d:])
+    K[rows] = k.reshape(r, d)
+    V[rows] = v
+    o = rnd(attention(q, K.reshape(-1, H, D), V.reshape(-1, H, D),
+                      round_weights=rnd if model.mirror else None).reshape(r, d))
+    h = h + o @ lw["wo"].T
+    b = rnd(rmsnorm(h, lw["mlp_norm"], m.rms_eps))
+    s = rnd(silu(b @ lw["w_gate"].T) * (b @ lw["w_up"].T))
+    return h + s @ lw["w_down"].T
+
+
 def forward(model: OracleModel, tokens: np.ndarray, rows: Sequence[int], cache,
             out_rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """Forward pass over the positions ``rows`` against the per-layer cache.
@@ -199,28 +226,12 @@ def forward(model: OracleModel, tokens: np.ndarray, rows: Sequence[int], cache,
     m = model.shape
     rows = np.asarray(rows, dtype=np.int64)
     assert len(np.unique(rows)) == len(rows), "recomputed rows must be distinct"
-    d, H, D = m.d_model, m.n_heads, m.head_dim
-    r = len(rows)
     rnd = model.rnd
     h = model.embed(np.asarray(tokens)[rows])
     for li in range(model.n_layers):
-        lw = model.layer(li)
-        K, V = cache[li]
-        a = rnd(rmsnorm(h, lw["attn_norm"], m.rms_eps))
-        qkv = a @ lw["wqkv"].T
-        q = rnd(rope(qkv[:, :d].reshape(r, H, D), rows, m.rope_base))
-        k = rnd(rope(qkv[:, d:2 * d].reshape(r, H, D), rows, m.rope_base))
-        v = rnd(qkv[:, 2 * d:])
-        K[rows] = k.reshape(r, d)
-        V[rows] = v
-        o = rnd(attention(q, K.reshape(-1, H, D), V.reshape(-1, H, D),
-                          round_weights=rnd if model.mirror else None).reshape(r, d))
-        h = h + o @ lw["wo"].T
-        b = rnd(rmsnorm(h, lw["mlp_norm"], m.rms_eps))
-        s = rnd(silu(b @ lw["w_gate"].T) * (b @ lw["w_up"].T))
-        h = h + s @ lw["w_down"].T
+        h = layer_forward(model, li, h, rows, cache[li])
     if out_rows is None:
-        sel = np.arange(r)
+        sel = np.arange(len(rows))
     else:
         where = {int(p): i for i, p in enumerate(rows)}
         sel = np.array([where[int(p)] for p in out_rows], dtype=np.int64)
