@@ -102,6 +102,28 @@ def test_partial_attn_bf16(r, L, H):
     assert err < 2e-2
 
 
+def _random_bf16_cases(n=24, seed=2024, max_work=2.5e7):
+    """(r, L, H) drawn from a fixed seed: r in [1, 700), L in [1, 3000), H among 1 .. 32, with
+    r L H bounded so that the oracle stays fast."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        r, L = int(rng.integers(1, 700)), int(rng.integers(1, 3000))
+        H = int(rng.choice([1, 2, 3, 5, 8, 12, 16, 32]))
+        if r * L * H <= max_work:
+            cases.append((r, L, H))
+    return cases
+
+
+@pytest.mark.parametrize("r,L,H", _random_bf16_cases())
+def test_partial_attn_bf16_seeded_random_shapes(r, L, H):
+    """Shapes off the hand-picked list: both workgroup shapes, 1 .. 16 key splits, ragged query
+    tiles and key tiles (the plans they take: 64 or 128 queries per workgroup with 1, 3 .. 11
+    splits, and 128 with 7, 8, 11 and 16)."""
+    got, want = _attn_case(r, L, H, 128, torch.bfloat16, seed=7 * r + L, scale=0.35)
+    assert row_rel_err(got.reshape(r * H, 128), want.reshape(r * H, 128)) < 2e-2
+
+
 @pytest.mark.parametrize("r,L,H,D", [(32, 128, 4, 64), (45, 300, 3, 64), (70, 1000, 2, 128), (1, 33, 1, 32),
                                      (5, 300, 2, 16), (1, 1, 1, 8)])
 def test_partial_attn_f32(r, L, H, D):
