@@ -90,6 +90,38 @@ def test_entropy_ragged_and_strided(rows, V, stride_pad, dtype):
     _check(x, ref)
 
 
+def _random_entropy_cases(n=16, seed=77, max_elems=3e7):
+    """(rows, V, row-pitch padding, dtype, with a selection) drawn from a fixed seed."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        rows, V = int(rng.integers(1, 700)), int(rng.integers(1, 150000))
+        if rows * V > max_elems:
+            continue
+        pad = int(rng.choice([0, 0, 1, 3, 8, 24]))
+        cases.append((rows, V, pad, ("bf16", "f32")[len(cases) % 2], bool(len(cases) % 4 >= 2)))
+    return cases
+
+
+@pytest.mark.parametrize("rows,V,pad,dtype,with_sel", _random_entropy_cases())
+def test_entropy_seeded_random_shapes(rows, V, pad, dtype, with_sel):
+    """Shapes off the hand-picked list (1 to 256 slices per row, one workgroup per row past 256
+    rows, aligned and element-wise row pitches), with per-row temperatures and, for half of
+    them, E over a random subset of the rows."""
+    rng = np.random.default_rng(rows * 131 + V)
+    z = (rng.standard_normal((rows, V + pad)) * rng.uniform(0.05, 6, (rows, 1))).astype(np.float32)
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(z)
+        full, ref = bf16_tensor(bits), bf16_bits_to_f64(bits)[:, :V]
+    else:
+        full, ref = torch.from_numpy(z).cuda(), z.astype(np.float64)[:, :V]
+    sel = None
+    if with_sel:
+        k = int(rng.integers(1, rows + 1))
+        sel = torch.from_numpy(np.sort(rng.choice(rows, k, replace=False)).astype(np.int32)).cuda()
+    _check(full[:, :V], ref, sel=sel)
+
+
 def test_entropy_selected_rows_and_nan():
     rng = np.random.default_rng(3)
     z = (rng.standard_normal((6, 5000)) * 2).astype(np.float32)
