@@ -41,6 +41,24 @@ def test_forward_at_8b_layer_width(n_rows):
     _compare(WIDE, omm, dm, cache, oc, tokens, rows, out)
 
 
+def _random_rows(n=10, seed=5150):
+    """Row counts drawn from a fixed seed over [2, 1023]: other tile and split choices of the
+    planner than the hand-picked counts above."""
+    rng = np.random.default_rng(seed)
+    return sorted(int(x) for x in rng.choice(np.arange(2, 1024), n, replace=False))
+
+
+@pytest.mark.parametrize("n_rows", _random_rows())
+def test_forward_at_8b_layer_width_seeded_rows(n_rows):
+    L = 1024
+    w, omm, dm, cache, oc = _setup(WIDE, L, seed=13, stale=True)
+    rng = np.random.default_rng(n_rows)
+    tokens = rng.integers(0, WIDE.vocab - 1, L).astype(np.int32)
+    rows = np.sort(rng.choice(L, n_rows, replace=False))
+    out = rows[np.sort(rng.choice(len(rows), min(len(rows), 32), replace=False))]
+    _compare(WIDE, omm, dm, cache, oc, tokens, rows, out)
+
+
 NARROW_FFN = synth.ModelShape("narrowffn", "bf16", 1, 2048, 16, 128, 512, 1024)
 
 
