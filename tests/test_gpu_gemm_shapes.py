@@ -41,14 +41,14 @@ def test_forward_at_8b_layer_width(n_rows):
     _compare(WIDE, omm, dm, cache, oc, tokens, rows, out)
 
 
-def _random_rows(n=10, seed=5150):
-    """Row counts drawn from a fixed seed over [2, 1023]: other tile and split choices of the
+def _random_rows(n, lo, hi, seed):
+    """Row counts drawn from a fixed seed over [lo, hi): other tile and split choices of the
     planner than the hand-picked counts above."""
     rng = np.random.default_rng(seed)
-    return sorted(int(x) for x in rng.choice(np.arange(2, 1024), n, replace=False))
+    return sorted(int(x) for x in rng.choice(np.arange(lo, hi), n, replace=False))
 
 
-@pytest.mark.parametrize("n_rows", _random_rows())
+@pytest.mark.parametrize("n_rows", _random_rows(10, 2, 1024, 5150) + _random_rows(8, 2, 257, 5151))
 def test_forward_at_8b_layer_width_seeded_rows(n_rows):
     L = 1024
     w, omm, dm, cache, oc = _setup(WIDE, L, seed=13, stale=True)
