@@ -190,6 +190,38 @@ def test_tiny_degenerate_budgets(name, P, M, n, B, k):
         assert abs(o.emax - r.emax) <= 1e-3
 
 
+def _random_tiny_configs(n=12, seed=4242):
+    """Tiny fp32 decodes drawn from a fixed seed: prompt length, masked count (L <= 128),
+    tokens per step, block length, recent budget k, weight and prompt seeds, fixed blocks or a
+    sliding window, and either the peaked LM head with its mixing threshold or tau = +inf."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.integers(1, 65))
+        P = int(rng.integers(1, 129 - M))
+        nt = int(rng.integers(1, 5))
+        B = int(rng.choice([2, 4, 8, 16, 32, M]))
+        k = int(rng.integers(0, 9))
+        peaked = bool(rng.integers(0, 2))
+        window = bool(rng.integers(0, 2))
+        cfg = synth.DecodeConfig(f"r{i}", synth.TINY, P, M, nt, B, k, (math.inf,), seed=int(rng.integers(0, 1000)),
+                                 window=window)
+        out.append(pytest.param(cfg, peaked, id=f"P{P}-M{M}-n{nt}-B{B}-k{k}-{'peaked' if peaked else 'inf'}"
+                                                f"{'-win' if window else ''}-s{cfg.seed}"))
+    return out
+
+
+@pytest.mark.parametrize("cfg,peaked", _random_tiny_configs())
+def test_tiny_seeded_random_decodes(cfg, peaked):
+    """Whole tiny fp32 trajectories over configurations off the hand-picked list (ragged last
+    blocks, n > k and n <= k, k = 0, sliding windows, mixed and all-skip paths): path, |R|,
+    positions, ids, E and the next flag on every step the gates decide."""
+    w = synth.make_model(cfg.model, seed=cfg.seed, lm_head_scale=PEAKED_SCALE if peaked else 1.0)
+    outs, recs = _compare_run(cfg, w, PEAKED_TAU if peaked else math.inf, expect_full_compare=False,
+                              min_compared=1)
+    print("paths", "".join("F" if o.refreshed else "." for o in outs))
+
+
 def test_tau_minus_inf_equals_vanilla_on_gpu():
     """tau = -inf refreshes every step; it must match a run that forces a refresh each step."""
     from entropy_guided_kv_amd import api
