@@ -158,3 +158,35 @@ def test_batch_sliding_window_tiny():
         assert [(o.refreshed, o.rows, o.positions, o.ids, o.emax) for o in single] == \
                [(o.refreshed, o.rows, o.positions, o.ids, o.emax) for o in got]
     assert any(o.refreshed for o in seq_outs[0][1:]) and not all(o.refreshed for o in seq_outs[0])
+
+
+def _random_batches():
+    from tests.test_gpu_step import _random_tiny_configs
+    rng = np.random.default_rng(99)
+    out = []
+    for p in _random_tiny_configs()[:6]:
+        cfg, peaked = p.values
+        out.append(pytest.param(cfg, peaked, int(rng.integers(2, 9)), id=p.id))
+    return out
+
+
+@pytest.mark.parametrize("cfg,peaked,n_seq", _random_batches())
+def test_batch_seeded_random_tiny(cfg, peaked, n_seq):
+    """Batches of 2 to 8 fp32 sequences over the seeded random tiny configurations (ragged
+    blocks, k = 0, n > k, sliding windows): each sequence equals its single-sequence run bit
+    for bit over its whole decode."""
+    from entropy_guided_kv_amd import api
+    w = synth.make_model(cfg.model, seed=cfg.seed, lm_head_scale=PEAKED_SCALE if peaked else 1.0)
+    tau = PEAKED_TAU if peaked else math.inf
+    dm = api.DeviceModel.from_host(w, rope_max_pos=cfg.seq_len)
+    prompts = _prompts(cfg, n_seq)
+    bd, seq_outs = _batch_run(dm, cfg, tau, prompts, window=cfg.window)
+    for i in range(n_seq):
+        dec = api.Decoder(dm, cfg.seq_len, cfg.prompt_len, cfg.tokens_per_step, cfg.block_len,
+                          cfg.k_recent, tau, window=cfg.window)
+        dec.reset(torch.from_numpy(prompts[i]))
+        single = dec.run()
+        got = [o for o in seq_outs[i] if o is not None]
+        assert [(o.refreshed, o.rows, o.positions, o.ids, o.emax) for o in single] == \
+               [(o.refreshed, o.rows, o.positions, o.ids, o.emax) for o in got]
+        assert torch.equal(dec.tokens, bd.tokens[i])
