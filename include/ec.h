@@ -149,8 +149,9 @@ ec_status ec_partial_attn(const void* q, const void* k_cache, const void* v_cach
                           ec_dtype dtype, void* out, void* workspace, size_t workspace_bytes,
                           void* stream);
 
-/* ec_partial_attn_plan -- the launch plan of the bf16 path of ec_partial_attn for
- * these sizes (host only, no device work): *query_tile = queries per workgroup
+/* ec_partial_attn_plan -- the launch plan of the bf16 path of ec_partial_attn (the
+ * attention above, Italian summary section 1) for these sizes (host only, no device
+ * work): *query_tile = queries per workgroup
  * (64 for the skip-step shape, 128 for the refresh-sized one), *splits = key-range
  * splits merged after the launch (1 = none). Workgroups = ceil(r / query_tile) *
  * n_heads * splits. For diagnostics and tests; ec_partial_attn takes the same plan
