@@ -44,13 +44,17 @@ def step_work(m, L: int, r: int, n_cand: int):
     """(flops, bytes) the method must do for one step that recomputes r rows.
 
     flops: every projection over the r rows, attention of r queries over L keys,
-    the LM head over the candidate rows. bytes: every weight once, the K/V cache
-    read once (L rows) and the r recomputed rows written, the candidate logits
-    written and read by the reduction.
+    except in the last layer, whose K/V projection covers the r rows and whose
+    attention, O-proj and MLP only the candidate rows (the only final states the LM
+    head reads); the LM head over the candidate rows. bytes: every weight once, the
+    K/V cache read once (L rows) and the r recomputed rows written, the candidate
+    logits written and read by the reduction.
     """
     d, F, V, nl = m.d_model, m.ffn_dim, m.vocab, m.n_layers
     per_layer_w = 4 * d * d + 3 * d * F
-    flops = nl * (2 * r * per_layer_w + 4 * r * L * d) + 2 * n_cand * V * d
+    c = min(n_cand, r)
+    last = 2 * r * 3 * d * d + 2 * c * (d * d + 3 * d * F) + 4 * c * L * d
+    flops = (nl - 1) * (2 * r * per_layer_w + 4 * r * L * d) + last + 2 * n_cand * V * d
     bytes_ = 2 * (nl * per_layer_w + V * d) + nl * (2 * L * d * 2 + 2 * r * d * 2) + 2 * 2 * n_cand * V
     return float(flops), float(bytes_)
 

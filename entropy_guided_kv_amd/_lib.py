@@ -29,9 +29,9 @@ EXPORTS = (
     "ec_version", "ec_pack_weights", "ec_step_batch_workspace_size", "ec_step_batch", "ec_step_probe",
 )
 
-EC_T_KINDS = 10
+EC_T_KINDS = 11
 TIMING_KINDS = ("embed", "norm", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "entropy",
-                "select")
+                "select", "last")
 
 
 class ec_layer_weights(C.Structure):

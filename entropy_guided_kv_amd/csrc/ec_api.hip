@@ -157,6 +157,8 @@ struct FwdWs {
   void* o;
   void* s;
   void* xn;
+  float* hc;  // [max_out, d] fp32 residual rows of the outputs in the last layer
+  void* qc;   // [max_out, d] their queries
   float* splitk;
   size_t splitk_bytes;
   void* attn;
@@ -208,6 +210,8 @@ size_t carve_fwd(const ec_model_desc* m, int max_rows, int max_out, int L, void*
   x.o = c.take<char>((size_t)max_rows * d * es);
   x.s = c.take<char>((size_t)max_rows * F * es);
   x.xn = c.take<char>((size_t)std::max(max_out, 1) * d * es);
+  x.hc = c.take<float>((size_t)std::max(max_out, 1) * d);
+  x.qc = c.take<char>((size_t)std::max(max_out, 1) * d * es);
   x.splitk_bytes = splitk_max(m, max_rows, max_out);
   x.splitk = c.take<float>(x.splitk_bytes / sizeof(float) + 1);
   x.attn_bytes = attn_max(m, max_rows, L);
@@ -224,6 +228,7 @@ struct BatchRows {
   const int32_t* row_seq;          // device [rows]: sequence of each row
   SeqPtrs tok;                     // token array of each sequence (kernel arguments)
   const int* row_off;              // host [n_seq + 1]
+  const int* out_off;              // host [n_seq + 1]: sequence s owns outputs [out_off[s], out_off[s+1])
   const ec_cache_desc* caches;     // host [n_seq]
 };
 
@@ -269,6 +274,14 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
     // normed: w.a already holds this layer's attention-norm input (the previous layer's
     // down projection fused its split-K reduction with the norm)
     bool normed = false;
+    // Only the output rows' final hidden states are read (by the LM head), unless the
+    // caller asks for every row's. The last layer then computes K/V of every row (the
+    // cache update), but its attention, O-proj and MLP only for the output rows: their
+    // queries and residual rows are gathered after the QKV projection.
+    const bool prune = hidden == nullptr && n_out > 0 && n_out < n_rows && m->n_layers > 0;
+    float* hres = w.h;  // residual rows of the current layer
+    int Mr = n_rows;    // rows past the QKV projection
+    const void* qin = w.q;
     for (int l = 0; l < m->n_layers; ++l) {
       const ec_layer_weights& lw = m->layers[l];
       if (!normed) {
@@ -304,59 +317,72 @@ ec_status run_forward(const ec_model_desc* m, const ec_cache_desc* c, const int3
       if (probe)
         EC_TRY(drift_rows(dt, probe->old_k, probe->old_v, c->k[l], c->v[l], rows, n_rows, L, d,
                           probe->dist + (size_t)l * 2 * n_rows, s));
+      const bool outputs_only = prune && l + 1 == m->n_layers;
+      if (outputs_only) {
+        TScope t(EC_T_LAST, s, 0.0, (double)n_out * dd * (4 + es) * 2);
+        EC_TRY(gather_rows2(out_idx, n_out, w.q, w.qc, (size_t)d * esize(dt), w.h, w.hc, (size_t)d * 4, s));
+        hres = w.hc;
+        Mr = n_out;
+        qin = w.qc;
+      }
+      const double Ml = Mr;
+      const int* off = outputs_only ? (b ? b->out_off : nullptr) : (b ? b->row_off : nullptr);
       {
-        TScope t(EC_T_ATTN, s, 4 * M * Lq * dd, (2 * Lq * dd + 2 * M * dd) * es);
+        TScope t(outputs_only ? EC_T_LAST : EC_T_ATTN, s, 4 * Ml * Lq * dd, (2 * Lq * dd + 2 * Ml * dd) * es);
         if (b) {
           // one launch for every sequence: each sequence's rows attend to its own cache
           AttnSeqs as{};
           as.n = b->n_seq;
           for (int q = 0; q < b->n_seq; ++q)
-            as.s[q] = AttnSeq{b->row_off[q], b->row_off[q + 1] - b->row_off[q], b->caches[q].k[l], b->caches[q].v[l]};
-          EC_TRY(attn_batch(dt, w.q, as, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
+            as.s[q] = AttnSeq{off[q], off[q + 1] - off[q], b->caches[q].k[l], b->caches[q].v[l]};
+          EC_TRY(attn_batch(dt, qin, as, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
         } else {
-          EC_TRY(attn(dt, w.q, c->k[l], c->v[l], n_rows, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
+          EC_TRY(attn(dt, qin, c->k[l], c->v[l], Mr, L, H, Dh, scale, w.o, w.attn, w.attn_bytes, s));
         }
       }
       EpiArgs r{};
       r.kind = EPI_RESID;
-      r.resid = w.h;
+      r.resid = hres;
       r.ldo = d;
       r.norm_gain = lw.mlp_norm;
       r.norm_out = w.a;
       r.norm_eps = m->rms_eps;
       {
-        TScope t(EC_T_OPROJ, s, 2 * M * dd * dd, (dd * dd + M * dd) * es + 8 * M * dd);
-        EC_TRY(gemm(dt, w.o, lw.wo, nullptr, n_rows, d, d, r, w.splitk, w.splitk_bytes, s, &normed));
+        TScope t(outputs_only ? EC_T_LAST : EC_T_OPROJ, s, 2 * Ml * dd * dd, (dd * dd + Ml * dd) * es + 8 * Ml * dd);
+        EC_TRY(gemm(dt, w.o, lw.wo, nullptr, Mr, d, d, r, w.splitk, w.splitk_bytes, s, &normed));
       }
       if (!normed) {
-        TScope t(EC_T_NORM, s, 0.0, M * dd * (4 + es));
-        EC_TRY(rmsnorm(dt, w.h, n_rows, nullptr, n_rows, d, lw.mlp_norm, m->rms_eps, w.a, s));
+        TScope t(outputs_only ? EC_T_LAST : EC_T_NORM, s, 0.0, Ml * dd * (4 + es));
+        EC_TRY(rmsnorm(dt, hres, Mr, nullptr, Mr, d, lw.mlp_norm, m->rms_eps, w.a, s));
       }
       EpiArgs g{};
       g.kind = EPI_SWIGLU;
       g.out = w.s;
       g.ldo = F;
       {
-        TScope t(EC_T_GATEUP, s, 4 * M * FF * dd, (2 * FF * dd + M * dd + M * FF) * es);
-        EC_TRY(gemm(dt, w.a, lw.w_gate, lw.w_up, n_rows, F, d, g, w.splitk, w.splitk_bytes, s));
+        TScope t(outputs_only ? EC_T_LAST : EC_T_GATEUP, s, 4 * Ml * FF * dd, (2 * FF * dd + Ml * dd + Ml * FF) * es);
+        EC_TRY(gemm(dt, w.a, lw.w_gate, lw.w_up, Mr, F, d, g, w.splitk, w.splitk_bytes, s));
       }
       // the next layer's attention norm rides on the down projection's split-K reduction
       const bool has_next = l + 1 < m->n_layers;
       r.norm_gain = has_next ? m->layers[l + 1].attn_norm : nullptr;
       r.norm_out = has_next ? w.a : nullptr;
       {
-        TScope t(EC_T_DOWN, s, 2 * M * dd * FF, (dd * FF + M * FF) * es + 8 * M * dd);
-        EC_TRY(gemm(dt, w.s, lw.w_down, nullptr, n_rows, d, F, r, w.splitk, w.splitk_bytes, s, &normed));
+        TScope t(outputs_only ? EC_T_LAST : EC_T_DOWN, s, 2 * Ml * dd * FF, (dd * FF + Ml * FF) * es + 8 * Ml * dd);
+        EC_TRY(gemm(dt, w.s, lw.w_down, nullptr, Mr, d, F, r, w.splitk, w.splitk_bytes, s, &normed));
       }
     }
   }
+  // the last layer ran over the gathered output rows (w.hc) only
+  const bool pruned = hidden == nullptr && n_out > 0 && n_out < n_rows && m->n_layers > 0;
   if (probe && n_rows > 0) EC_TRY(drift_reduce(probe->dist, m->n_layers, n_rows, 2 * (int64_t)n_rows, probe->out, s));
   if (hidden && n_rows > 0)
     EC_CHECK_HIP(hipMemcpyAsync(hidden, w.h, (size_t)n_rows * d * sizeof(float),
                                 hipMemcpyDeviceToDevice, s));
   if (n_out > 0) {
     TScope t(EC_T_LMHEAD, s, 2 * NO * VV * dd, (VV * dd + NO * dd + (fe ? 0.0 : NO * VV)) * es + NO * dd * 4);
-    EC_TRY(rmsnorm(dt, w.h, n_rows, out_idx, n_out, d, m->final_norm, m->rms_eps, w.xn, s));
+    if (pruned) EC_TRY(rmsnorm(dt, w.hc, n_out, nullptr, n_out, d, m->final_norm, m->rms_eps, w.xn, s));
+    else EC_TRY(rmsnorm(dt, w.h, n_rows, out_idx, n_out, d, m->final_norm, m->rms_eps, w.xn, s));
     EpiArgs o{};
     if (fe) {
       // LM head with the entropy / argmax / confidence reduction in its epilogue: one
@@ -859,7 +885,7 @@ ec_status ec_step_batch(const ec_model_desc* model, int32_t n_seq, const ec_cach
   st = batch_gather(segs, L, w.rows_all, w.row_seq, w.out_all, s);
   if (st != EC_OK) return st;
 
-  BatchRows b{n_seq, w.row_seq, SeqPtrs{}, row_off, caches};
+  BatchRows b{n_seq, w.row_seq, SeqPtrs{}, row_off, cand_off, caches};
   for (int q = 0; q < n_seq; ++q) b.tok.p[q] = states[q].tokens;
   if (model->dtype == EC_BF16) {
     const FusedEnt fe{(EntPart*)w.ent_ws, w.H, w.amax, w.conf};

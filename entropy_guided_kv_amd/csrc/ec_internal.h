@@ -228,6 +228,10 @@ ec_status rmsnorm(ec_dtype dt, const float* h, int n_src, const int32_t* idx, in
 // float operations of the split-K residual epilogue followed by rmsnorm(), in their order.
 ec_status resid_norm(ec_dtype dt, const float* part, int S, int M, int d, float* h, const void* gain,
                      float eps, void* out, hipStream_t s);
+// ao[i] = a[idx[i]] and bo[i] = b[idx[i]] for i < n (rows of a_row_bytes / b_row_bytes,
+// multiples of 16, 16-byte aligned buffers), one launch
+ec_status gather_rows2(const int32_t* idx, int n, const void* a, void* ao, size_t a_row_bytes, const void* b,
+                       void* bo, size_t b_row_bytes, hipStream_t s);
 ec_status scatter(ec_dtype dt, void* kc, void* vc, int64_t L, int width, const void* kr,
                   const void* vr, const int32_t* idx, int n, hipStream_t s);
 

@@ -191,6 +191,19 @@ scatter_scalar_kernel(T* __restrict__ kc, T* __restrict__ vc, int64_t L, int wid
   }
 }
 
+// Row gather of two row-major buffers in one launch: blockIdx.y = 0 copies row idx[i]
+// of a (a_vecs 16-byte vectors per row) to row i of ao, blockIdx.y = 1 the same for b.
+__global__ void __launch_bounds__(kThreads)
+gather2_kernel(const int32_t* __restrict__ idx, const uint4* __restrict__ a, uint4* __restrict__ ao, int a_vecs,
+               const uint4* __restrict__ b, uint4* __restrict__ bo, int b_vecs) {
+  const int i = blockIdx.x;
+  const int src = idx[i];
+  const uint4* x = blockIdx.y == 0 ? a : b;
+  uint4* y = blockIdx.y == 0 ? ao : bo;
+  const int nv = blockIdx.y == 0 ? a_vecs : b_vecs;
+  for (int j = threadIdx.x; j < nv; j += kThreads) y[(int64_t)i * nv + j] = x[(int64_t)src * nv + j];
+}
+
 // cos/sin(pos * base^(-2i/D)) in fp64, stored fp32; one thread per (pos, i).
 __global__ void rope_table_kernel(float* c, float* sn, int max_pos, int half, int D, double base) {
   const int64_t n = (int64_t)max_pos * half;
@@ -277,6 +290,19 @@ ec_status scatter(ec_dtype dt, void* kc, void* vc, int64_t L, int width, const v
                                                         (const float*)kr, (const float*)vr, idx);
   }
   EC_CHECK_LAUNCH("scatter_kernel");
+  return EC_OK;
+}
+
+ec_status gather_rows2(const int32_t* idx, int n, const void* a, void* ao, size_t a_row_bytes, const void* b,
+                       void* bo, size_t b_row_bytes, hipStream_t s) {
+  if (n == 0) return EC_OK;
+  EC_REQUIRE(a_row_bytes % 16 == 0 && b_row_bytes % 16 == 0 &&
+                 (((uintptr_t)a | (uintptr_t)ao | (uintptr_t)b | (uintptr_t)bo) & 15) == 0,
+             EC_ERR_UNSUPPORTED, "gather_rows2: rows of %zu and %zu bytes need 16-byte alignment", a_row_bytes,
+             b_row_bytes);
+  gather2_kernel<<<dim3(n, 2), kThreads, 0, s>>>(idx, (const uint4*)a, (uint4*)ao, (int)(a_row_bytes / 16),
+                                                 (const uint4*)b, (uint4*)bo, (int)(b_row_bytes / 16));
+  EC_CHECK_LAUNCH("gather2_kernel");
   return EC_OK;
 }
 

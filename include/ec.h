@@ -251,6 +251,11 @@ ec_status ec_rope_table(float* cos_out, float* sin_out, int32_t max_pos, int32_t
  * out_idx: int32[n_out], indices INTO rows whose logits are produced;
  * logits: [n_out, V] of dtype; hidden: NULL or float[n_rows, d] receiving the
  * residual stream after the last layer.
+ * The logits need the last layer's output only at the out_idx rows: with hidden
+ * == NULL and n_out < n_rows, the last layer writes K/V of every row but runs
+ * its attention, O-projection and MLP over the out_idx rows alone (ec_step and
+ * ec_step_batch always take this path). The logits are those of the whole
+ * forward up to the summation order of the smaller launches.
  * Supported: bf16 needs head_dim == 128, d % 256 == 0, F % 128 == 0,
  * V % 256 == 0; f32 any even head_dim <= 256.
  * ---------------------------------------------------------------------- */
@@ -399,7 +404,9 @@ ec_status ec_step_batch(const ec_model_desc* model, int32_t n_seq, const ec_cach
  * ---------------------------------------------------------------------- */
 enum {
   EC_T_EMBED = 0, EC_T_NORM, EC_T_QKV, EC_T_ATTN, EC_T_OPROJ, EC_T_GATEUP, EC_T_DOWN,
-  EC_T_LMHEAD, EC_T_ENTROPY, EC_T_SELECT, EC_T_KINDS
+  EC_T_LMHEAD, EC_T_ENTROPY, EC_T_SELECT,
+  EC_T_LAST,  /* last layer past its QKV projection, over the output rows only (see ec_forward) */
+  EC_T_KINDS
 };
 typedef struct ec_timing {
   uint32_t struct_size;

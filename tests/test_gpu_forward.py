@@ -155,3 +155,60 @@ def test_partial_after_full_is_idempotent_bf16():
     for a, b in zip(cache.k, k0):
         assert row_rel_err(to_f64(a)[ri], to_f64(b)[ri]) < 2e-2
         assert torch.equal(a[outside], b[outside])
+
+
+@pytest.mark.parametrize("case", ["tiny_full", "tiny_partial", "mini_full", "mini_partial", "mini_one_out",
+                                  "small_partial"])
+def test_forward_last_layer_over_outputs(case):
+    """Without the hidden states, the last layer runs its attention, O-proj and MLP over the
+    output rows only (their final states are all the LM head reads); its K/V are still
+    written for every row. Against the whole forward on the same starting cache: every
+    cache row bit-identical (the QKV projections see the same inputs); fp32 logits
+    bit-identical (the fp32 kernels sum each output in a fixed order whatever the row
+    count); bf16 logits within the bf16 bar of the oracle's, ids where the gate allows."""
+    from entropy_guided_kv_amd import api
+    if case.startswith("tiny"):
+        cfg = synth.CONFIGS["tiny"]
+        shape, L = cfg.model, cfg.seq_len
+        tokens = synth.make_prompt(cfg)
+        seed, n_layers = 0, None
+    elif case.startswith("mini"):
+        shape, L = MINI_BF16, 320
+        tokens = np.random.default_rng(7).integers(0, shape.vocab - 1, L).astype(np.int32)
+        seed, n_layers = 3, None
+    else:
+        cfg = synth.CONFIGS["small"]
+        shape, L = cfg.model, cfg.seq_len
+        tokens = synth.make_prompt(cfg)
+        seed, n_layers = 0, 2
+    partial = case.endswith("partial") or case.endswith("one_out")
+    w, omm, dm, cache, oc = _setup(shape, L, seed=seed, n_layers=n_layers, stale=partial)
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(L, min(150, 3 * L // 4), replace=False)) if partial else np.arange(L)
+    if case.endswith("one_out"):
+        out_idx = np.array([77], np.int32)
+    else:
+        out_idx = np.sort(rng.choice(len(rows), 32, replace=False)).astype(np.int32)
+    # a second cache with the same starting rows for the whole forward
+    cache2 = api.KVCache(dm, L)
+    for a, b in zip(cache2.k + cache2.v, cache.k + cache.v):
+        a.copy_(b)
+    tk = torch.from_numpy(tokens).cuda()
+    rt = torch.from_numpy(rows.astype(np.int32)).cuda()
+    ot = torch.from_numpy(out_idx).cuda()
+    lg_out, h_none = api.ec_forward(dm, cache, tk, rt, ot, want_hidden=False)
+    lg_all, _ = api.ec_forward(dm, cache2, tk, rt, ot, want_hidden=True)
+    torch.cuda.synchronize()
+    assert h_none is None
+    for i, (a, b) in enumerate(zip(cache.k + cache.v, cache2.k + cache2.v)):
+        assert torch.equal(a, b), f"cache tensor {i} differs between the two paths"
+    if shape.dtype == "f32":
+        assert torch.equal(lg_out, lg_all)
+    ref = om.forward(omm, tokens, rows, oc, out_rows=rows[out_idx])
+    lg = to_f64(lg_out)
+    el = row_rel_err(lg, ref["logits"])
+    print(f"{case}: rows={len(rows)} outputs={len(out_idx)} worst logit row {el:.2e}")
+    assert el <= _tol(shape)
+    srt = np.sort(ref["logits"], axis=1)
+    gate = margin_gate(srt[:, -1], srt[:, -1] - srt[:, -2], shape.dtype)
+    assert not np.any(gate & (lg.argmax(1) != ref["logits"].argmax(1)))
