@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define EC_VERSION 10100            /* 1.1.0 */
+#define EC_VERSION 10200            /* 1.2.0: timing group EC_T_LAST, last layer over the output rows */
 #define EC_MAX_TOKENS_PER_STEP 64   /* upper bound on tokens decoded per step */
 #define EC_MAX_LAYERS 256
 #define EC_MAX_SEQ 16               /* upper bound on sequences per ec_step_batch call */

@@ -39,7 +39,7 @@ def test_library_resolves_every_symbol_at_load():
 
 
 def test_version_and_error_string(lib):
-    assert lib.ec_version() == 10100
+    assert lib.ec_version() == 10200
     assert isinstance(lib.ec_last_error(), bytes)
 
 
