@@ -585,6 +585,8 @@ def main():
     kernels = {}
     if not args.no_breakdown:
         kernels = breakdown_report(dec, prompt, args.breakdown == "both")
+        if args.breakdown == "both":
+            kernels["skip_rows_profile"] = skip_rows_profile(dm, dec.cache)
 
     drift_res = None
     if not args.no_drift:
@@ -644,6 +646,53 @@ def roofline_object(dom, dk):
     log(f"[bench] dominant kernel {dom}: {avg_ms * 1e3:.1f} us/launch over the timed region "
         f"({dk['launches']} launches), {roofline['frac']:.3f} of peak")
     return roofline
+
+
+def skip_rows_profile(dm, cache, rs=(17, 32, 64, 96, 128, 192, 256), reps=5):
+    """Partial forwards of a skip step at several row counts r, on the decoder's cache.
+
+    rows = the last r positions, outputs = the first min(32, max(1, r - 16)) of them (a skip
+    step recomputes its masked positions plus the k = 16 most recent ones; the candidates are
+    masked). Per r: the device time per forward (HIP events around `reps` back-to-back calls,
+    untimed groups), the time per kernel group (a second pass with every group event-timed) and
+    the fraction of the step's roof, max(flops / MFMA peak, bytes / HBM peak), with the LM head's
+    stored logits in place of the fused entropy epilogue of ec_step.
+    """
+    import torch
+    from entropy_guided_kv_amd import api
+    m = dm.shape
+    L = cache.seq_len
+    tokens = torch.randint(0, m.vocab - 1, (L,), dtype=torch.int32, generator=torch.Generator().manual_seed(5)).cuda()
+    ws = None
+    out = {}
+    for r in rs:
+        n_out = min(32, max(1, r - 16))
+        rows = torch.arange(L - r, L, dtype=torch.int32, device="cuda")
+        oidx = torch.arange(n_out, dtype=torch.int32, device="cuda")
+        need = api.load().ec_forward_workspace_size(api.C.byref(dm.desc), r, n_out, L)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            api.ec_forward(dm, cache, tokens, rows, oidx, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            api.ec_forward(dm, cache, tokens, rows, oidx, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        api.ec_timing_read(reset=True)
+        api.ec_timing_enable(True)
+        for _ in range(reps):
+            api.ec_forward(dm, cache, tokens, rows, oidx, workspace=ws)
+        api.ec_timing_enable(False)
+        t = api.ec_timing_read(reset=True)
+        fl, by = step_work(m, L, r, n_out)
+        out[str(r)] = {"outputs": n_out, "ms": ms, "roofline_frac": t_roof(fl, by) * 1e3 / ms,
+                       "groups_ms": {k: x["ms"] / reps for k, x in t.items() if x["launches"]}}
+        log(f"[bench] skip forward r={r}: {ms:.3f} ms, {t_roof(fl, by) * 1e3 / ms:.3f} of its roof")
+    return out
 
 
 def breakdown_report(dec, prompt, with_skip=True):
