@@ -88,11 +88,15 @@ using AttnWide = AttnShape<4, 2, 4>;
 using AttnNarrow = AttnShape<2, 4, 2>;
 // planning figures fitted to MI355X measurements: time per K/V tile of one wave of
 // workgroups, and the cost of a key split beyond its tiles (the merge launch, plus the
-// partials' round trip per split and query at 32 heads)
-constexpr double kWideTileUs = 0.9;
-constexpr double kNarrowTileUs = 1.14;
-constexpr double kMergeUs = 4.0;
-constexpr double kPartialUs = 0.008;
+// partials' round trip per split and query at 32 heads). Fitted jointly to every forced
+// shape x split (1, 2, 3, 4, 8) inside the partial forwards of a 32-layer 8B-shaped model
+// (the layer's K/V no longer cached when its attention runs, as in a step): L = 1024 with
+// r = 17 .. 384 and L = 4096 with r = 96 .. 2048; the choices are the fastest measured
+// candidate at 12 of the 14 points and within 1 % at the other two.
+constexpr double kWideTileUs = 1.308;
+constexpr double kNarrowTileUs = 1.873;
+constexpr double kMergeUs = 2.501;
+constexpr double kPartialUs = 0.01127;
 
 // s_waitcnt vmcnt(min(n, K) * PER) for a wave-uniform run-time n >= 0
 template <int PER, int K>
