@@ -148,12 +148,15 @@ __device__ __forceinline__ void lds_stage_barrier() {
 // given the global address of the chunk that belongs there. NSTG stages rotate;
 // AHEAD of them are in flight. With LATE the stage refilled after the barrier of
 // K-step t is the one read during step t-1 (no LDS wait before the barrier);
-// otherwise it is the one just read (deeper prefetch, an LDS wait first).
+// otherwise it is the one just read (deeper prefetch, an LDS wait first). With NSB > 0
+// the B tiles have a ring of their own, NSB = NSTG + 1 stages after the A stages: the
+// weights, streamed from HBM, are requested one K-step ahead of the activations, which
+// come from L2 (the 256x192 refresh tile: 2 A + 3 B stages, 136 KB).
 //
 // Fragment reads of the next 16-wide K slice are issued in the middle of the
 // current slice's MFMAs; the first slice of K-step t+1 is read right after the
 // barrier that publishes it.
-template <int BM, int BN, int WM, int WN, int NSTG, bool LATE, int EPI, bool SPLIT, int BKS = 64>
+template <int BM, int BN, int WM, int WN, int NSTG, bool LATE, int EPI, bool SPLIT, int BKS = 64, int NSB = 0>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K,
                  int k_chunk, int splits, EpiArgs epi, float* __restrict__ part) {
@@ -173,6 +176,14 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % WM == 0 && BN % WN == 0, "tile shape");
   static_assert(LPA >= 1 && LPB >= 1 && LPA * NT == BM * CPR && LPB * NT == BN * CPR, "load split");
   static_assert(AHEAD >= 2 && (AHEAD - 1) * LPT < 64, "pipeline depth");
+  // NSB > 0: the B (weight) tiles get a ring of their own, NSB stages deep, after the NSTG
+  // stages of A tiles; both rings refill the stage read during the K-step that just ended
+  constexpr bool ASYM = NSB > 0;
+  constexpr int SA = BM * ROWB, SB = BN * ROWB;
+  constexpr int B_RING = ASYM ? NSTG * SA : 0;
+  constexpr int LDS_BYTES = ASYM ? NSTG * SA + NSB * SB : NSTG * STAGE;
+  // (the waits of the separate ring below are written for 2 A stages and 3 B stages)
+  static_assert(!ASYM || (!LATE && NSTG == 2 && NSB == 3 && NSTG * LPA + NSB * LPB < 64), "separate B ring");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int MT = (M + BM - 1) / BM;
@@ -228,13 +239,21 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
     const int r = q / CPR, c = (q % CPR) ^ ((r >> SWS) & (CPR - 1));
     ob[i] = (int)(((int64_t)min(n0 + r, N - 1) * K + kbeg + c * 8) * 2);
   }
-  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
-    unsigned char* base = smem + stage * STAGE;
+  auto issue_a = [&](int kt, int stage) __attribute__((always_inline)) {
+    unsigned char* base = smem + stage * (ASYM ? SA : STAGE);
     const int ks = (kt + rot < nk ? kt + rot : kt + rot - nk) * BKS * 2;
 #pragma unroll
     for (int i = 0; i < LPA; ++i) buffer_load_lds16(rA, base + (i * NW + wave) * 1024, oa[i], ks);
+  };
+  auto issue_b = [&](int kt, int stage) __attribute__((always_inline)) {
+    unsigned char* base = ASYM ? smem + B_RING + stage * SB : smem + stage * STAGE + BM * ROWB;
+    const int ks = (kt + rot < nk ? kt + rot : kt + rot - nk) * BKS * 2;
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) buffer_load_lds16(rB, base + BM * ROWB + (i * NW + wave) * 1024, ob[i], ks);
+    for (int i = 0; i < LPB; ++i) buffer_load_lds16(rB, base + (i * NW + wave) * 1024, ob[i], ks);
+  };
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    issue_a(kt, stage);
+    issue_b(kt, stage);
   };
 
   // fragment addresses: A/B operand of lane = row lane%32 of the tile, K chunk
@@ -242,7 +261,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   const int lrow = lane % 32, hi = lane / 32;
   const int swr = (lrow >> SWS) & (CPR - 1);
   const int a_row = (wm * WM + lrow) * ROWB;
-  const int b_row = BM * ROWB + (wn * WN + lrow) * ROWB;
+  const int b_row = (ASYM ? 0 : BM * ROWB) + (wn * WN + lrow) * ROWB;
   int koff[NS];
 #pragma unroll
   for (int kk = 0; kk < NS; ++kk) koff[kk] = ((2 * kk + hi) ^ swr) * 16;
@@ -256,22 +275,28 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   bf16x8 fa[2][TM], fb[2][TN];
-  auto rdfrag = [&](int stage, int kk, int slot) __attribute__((always_inline)) {
-    const unsigned char* base = smem + stage * STAGE;
+  // fragment reads of K slice kk from the A stage at base_a and the B stage at base_b
+  auto rdfrag = [&](const unsigned char* base_a, const unsigned char* base_b, int kk, int slot)
+                    __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      fa[slot][i] = *reinterpret_cast<const bf16x8*>(base + a_row + i * 32 * ROWB + koff[kk]);
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(base_a + a_row + i * 32 * ROWB + koff[kk]);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      fb[slot][j] = *reinterpret_cast<const bf16x8*>(base + b_row + j * 32 * ROWB + koff[kk]);
+      fb[slot][j] = *reinterpret_cast<const bf16x8*>(base_b + b_row + j * 32 * ROWB + koff[kk]);
+  };
+  auto a_stage = [&](int st) __attribute__((always_inline)) { return smem + st * (ASYM ? SA : STAGE); };
+  auto b_stage = [&](int st) __attribute__((always_inline)) {
+    return ASYM ? smem + B_RING + st * SB : smem + st * STAGE;
   };
   // MFMAs on fragment slot ms; the reads of (stage, kk) into slot rs go after RD_AT of them
-  auto slice = [&](int ms, int stage, int kk, int rs) __attribute__((always_inline)) {
+  auto slice = [&](int ms, const unsigned char* base_a, const unsigned char* base_b, int kk, int rs)
+                   __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < TM * TN; ++q) {
       if (q == RD_AT) {
         __builtin_amdgcn_sched_barrier(0);
-        rdfrag(stage, kk, rs);
+        rdfrag(base_a, base_b, kk, rs);
         __builtin_amdgcn_sched_barrier(0);
       }
       const int i = q / TN, j = q % TN;
@@ -301,27 +326,54 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
     }
   }
 
+  if constexpr (ASYM) {
+    // loads in issue order: A0 B0 A1 B1 B2 (prologue), then A(t+NSTG) B(t+NSB) after the
+    // barrier of step t: when step t+1 is due, the only loads issued after A(t+1) are
+    // those of B(t+2), and B(t+1) is older than A(t+1)
 #pragma unroll
-  for (int st = 0; st < AHEAD; ++st)
-    if (st < nk) issue(st, st);
-  if (nk >= AHEAD) wait_vmcnt<(AHEAD - 1) * LPT>(); else wait_vmcnt<0>();
-  lds_stage_barrier();
-  rdfrag(0, 0, 0);
-
-  for (int t = 0; t < nk; ++t) {
-    const int stage = t % NSTG;
-#pragma unroll
-    for (int kk = 0; kk + 1 < NS; ++kk) slice(kk & 1, stage, kk + 1, (kk + 1) & 1);
-    if (t + 1 < nk) {
-      if (!LATE) wait_lgkmcnt0();
-      // this lane's loads of step t+1 have landed once at most the later steps'
-      // (t+2 .. min(t+AHEAD-1, nk-1)) are outstanding
-      if (t + AHEAD - 1 < nk) wait_vmcnt<(AHEAD - 2) * LPT>(); else wait_vmcnt<0>();
-      lds_stage_barrier();
-      if (t + AHEAD < nk) issue(t + AHEAD, (t + AHEAD) % NSTG);
+    for (int st = 0; st < NSB; ++st) {
+      if (st < NSTG && st < nk) issue_a(st, st);
+      if (st < nk) issue_b(st, st);
     }
-    // on the last step the read of stage (t+1) % NSTG stays inside LDS and is unused
-    slice((NS - 1) & 1, (t + 1) % NSTG, 0, 0);
+    if (nk >= NSB) wait_vmcnt<(NSTG - 1) * LPA + (NSB - 1) * LPB>(); else wait_vmcnt<0>();
+    lds_stage_barrier();
+    rdfrag(a_stage(0), b_stage(0), 0, 0);
+    for (int t = 0; t < nk; ++t) {
+      const int sa = t % NSTG, sb = t % NSB;
+#pragma unroll
+      for (int kk = 0; kk + 1 < NS; ++kk) slice(kk & 1, a_stage(sa), b_stage(sb), kk + 1, (kk + 1) & 1);
+      if (t + 1 < nk) {
+        wait_lgkmcnt0();
+        if (t + 2 < nk) wait_vmcnt<LPB>(); else wait_vmcnt<0>();
+        lds_stage_barrier();
+        if (t + NSTG < nk) issue_a(t + NSTG, sa);
+        if (t + NSB < nk) issue_b(t + NSB, sb);
+      }
+      slice((NS - 1) & 1, a_stage((t + 1) % NSTG), b_stage((t + 1) % NSB), 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < AHEAD; ++st)
+      if (st < nk) issue(st, st);
+    if (nk >= AHEAD) wait_vmcnt<(AHEAD - 1) * LPT>(); else wait_vmcnt<0>();
+    lds_stage_barrier();
+    rdfrag(a_stage(0), b_stage(0), 0, 0);
+
+    for (int t = 0; t < nk; ++t) {
+      const int stage = t % NSTG;
+#pragma unroll
+      for (int kk = 0; kk + 1 < NS; ++kk) slice(kk & 1, a_stage(stage), b_stage(stage), kk + 1, (kk + 1) & 1);
+      if (t + 1 < nk) {
+        if (!LATE) wait_lgkmcnt0();
+        // this lane's loads of step t+1 have landed once at most the later steps'
+        // (t+2 .. min(t+AHEAD-1, nk-1)) are outstanding
+        if (t + AHEAD - 1 < nk) wait_vmcnt<(AHEAD - 2) * LPT>(); else wait_vmcnt<0>();
+        lds_stage_barrier();
+        if (t + AHEAD < nk) issue(t + AHEAD, (t + AHEAD) % NSTG);
+      }
+      // on the last step the read of stage (t+1) % NSTG stays inside LDS and is unused
+      slice((NS - 1) & 1, a_stage((t + 1) % NSTG), b_stage((t + 1) % NSTG), 0, 0);
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -335,7 +387,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   constexpr int ES = WN + 4;                 // slab row stride (floats)
   constexpr int C4 = WN / 4;                 // 4-column units per slab row
   constexpr int PL_BYTES = EPI == EPI_ENTROPY ? BM * WAVES_N * (int)sizeof(EntPart) : 0;
-  static_assert(NW * 32 * ES * 4 + PL_BYTES <= NSTG * STAGE, "epilogue staging exceeds the LDS tile buffers");
+  static_assert(NW * 32 * ES * 4 + PL_BYTES <= LDS_BYTES, "epilogue staging exceeds the LDS tile buffers");
   static_assert(EPI != EPI_ENTROPY || !SPLIT, "the entropy epilogue needs whole K");
   float* slab = reinterpret_cast<float*>(smem) + wave * 32 * ES;
   const int d = epi.d_model, D = epi.head_dim, half = D / 2;
@@ -796,11 +848,12 @@ Plan plan_bf16(int M, int N, int K, int kind) {
   return best;
 }
 
-template <int BM, int BN, int WM, int WN, int NSTG, bool LATE, int EPI, int BKS = 64>
+template <int BM, int BN, int WM, int WN, int NSTG, bool LATE, int EPI, int BKS = 64, int NSB = 0>
 ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, int M, int N, int K,
                       const EpiArgs& epi, float* part, hipStream_t s) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  constexpr size_t lds = (size_t)NSTG * (BM + BN) * BKS * 2;
+  constexpr size_t lds = NSB > 0 ? ((size_t)NSTG * BM + (size_t)NSB * BN) * BKS * 2
+                                 : (size_t)NSTG * (BM + BN) * BKS * 2;
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int grid = p.MT * p.NT * p.S;
   // one limit record per kernel: the split and whole-K kernels share a function type,
@@ -814,9 +867,9 @@ ec_status launch_bf16(const Plan& p, const bf16* A, const bf16* B, int M, int N,
     return EC_OK;
   };
   if constexpr (EPI != EPI_ENTROPY) {
-    if (p.S > 1) return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, true, BKS>, split);
+    if (p.S > 1) return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, true, BKS, NSB>, split);
   }
-  return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, false, BKS>, whole);
+  return run(gemm_bf16_kernel<BM, BN, WM, WN, NSTG, LATE, EPI, false, BKS, NSB>, whole);
 }
 
 template <int EPI>
@@ -827,7 +880,7 @@ ec_status launch_cfg(const Plan& p, const bf16* A, const bf16* B, int M, int N, 
     return launch_bf16<64, 128, 32, 32, 6, true, EPI>(p, A, B, M, N, K, epi, part, s);
   } else {
     switch (p.cfg) {
-      case T256x192: return launch_bf16<256, 192, 64, 96, 2, false, EPI>(p, A, B, M, N, K, epi, part, s);
+      case T256x192: return launch_bf16<256, 192, 64, 96, 2, false, EPI, 64, 3>(p, A, B, M, N, K, epi, part, s);
       case T256x128: return launch_bf16<256, 128, 64, 64, 3, false, EPI>(p, A, B, M, N, K, epi, part, s);
       case T128x128: return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
       // all-rows tiles of skinny products: four wavefronts stacked along M share one weight slice
