@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 
 METRIC = "denoising steps/s and gen tokens/s at L=1024,k=16 (1 GPU); % HBM/MFMA peak"
 # kernel the library launches for each timed group at M = 1024 (must match the profile's tag)
-KERNEL_TAGS = {"gateup": "gemm_bf16_kernel<256,192,64,96,2,false,EPI_SWIGLU,false,64,3>"}
+KERNEL_TAGS = {"gateup": "gemm_bf16_kernel<256,192,64,96,2,false,EPI_SWIGLU,false,64,4>"}
 DOMINANT = "gateup"  # the SwiGLU GEMM: the largest kernel group of a refresh step
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E

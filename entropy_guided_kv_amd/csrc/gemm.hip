@@ -149,9 +149,9 @@ __device__ __forceinline__ void lds_stage_barrier() {
 // AHEAD of them are in flight. With LATE the stage refilled after the barrier of
 // K-step t is the one read during step t-1 (no LDS wait before the barrier);
 // otherwise it is the one just read (deeper prefetch, an LDS wait first). With NSB > 0
-// the B tiles have a ring of their own, NSB = NSTG + 1 stages after the A stages: the
-// weights, streamed from HBM, are requested one K-step ahead of the activations, which
-// come from L2 (the 256x192 refresh tile: 2 A + 3 B stages, 136 KB).
+// the B tiles have a ring of their own, NSB stages after the A stages: the weights,
+// streamed from HBM, are requested NSB - NSTG K-steps ahead of the activations, which
+// come from L2 (the 256x192 refresh tile: 2 A + 4 B stages, all 160 KB of LDS).
 //
 // Fragment reads of the next 16-wide K slice are issued in the middle of the
 // current slice's MFMAs; the first slice of K-step t+1 is read right after the
@@ -182,8 +182,9 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   constexpr int SA = BM * ROWB, SB = BN * ROWB;
   constexpr int B_RING = ASYM ? NSTG * SA : 0;
   constexpr int LDS_BYTES = ASYM ? NSTG * SA + NSB * SB : NSTG * STAGE;
-  // (the waits of the separate ring below are written for 2 A stages and 3 B stages)
-  static_assert(!ASYM || (!LATE && NSTG == 2 && NSB == 3 && NSTG * LPA + NSB * LPB < 64), "separate B ring");
+  // (the waits of the separate ring below are written for 2 A stages and 3 or 4 B stages)
+  static_assert(!ASYM || (!LATE && NSTG == 2 && (NSB == 3 || NSB == 4) && NSTG * LPA + NSB * LPB < 64),
+                "separate B ring");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int MT = (M + BM - 1) / BM;
@@ -327,9 +328,10 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   }
 
   if constexpr (ASYM) {
-    // loads in issue order: A0 B0 A1 B1 B2 (prologue), then A(t+NSTG) B(t+NSB) after the
-    // barrier of step t: when step t+1 is due, the only loads issued after A(t+1) are
-    // those of B(t+2), and B(t+1) is older than A(t+1)
+    // loads in issue order: A0 B0 A1 B1 B2 .. B(NSB-1) (prologue), then A(t+2) B(t+NSB)
+    // after the barrier of step t: when step t+1 is due, B(t+1) is older than A(t+1), and
+    // the only loads issued after A(t+1) are those of B(t+NSB-1) (in the prologue also
+    // B2 .. B(NSB-2), which the wait then covers too)
 #pragma unroll
     for (int st = 0; st < NSB; ++st) {
       if (st < NSTG && st < nk) issue_a(st, st);
@@ -344,7 +346,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
       for (int kk = 0; kk + 1 < NS; ++kk) slice(kk & 1, a_stage(sa), b_stage(sb), kk + 1, (kk + 1) & 1);
       if (t + 1 < nk) {
         wait_lgkmcnt0();
-        if (t + 2 < nk) wait_vmcnt<LPB>(); else wait_vmcnt<0>();
+        if (t + NSB - 1 < nk) wait_vmcnt<LPB>(); else wait_vmcnt<0>();
         lds_stage_barrier();
         if (t + NSTG < nk) issue_a(t + NSTG, sa);
         if (t + NSB < nk) issue_b(t + NSB, sb);
@@ -880,7 +882,7 @@ ec_status launch_cfg(const Plan& p, const bf16* A, const bf16* B, int M, int N, 
     return launch_bf16<64, 128, 32, 32, 6, true, EPI>(p, A, B, M, N, K, epi, part, s);
   } else {
     switch (p.cfg) {
-      case T256x192: return launch_bf16<256, 192, 64, 96, 2, false, EPI, 64, 3>(p, A, B, M, N, K, epi, part, s);
+      case T256x192: return launch_bf16<256, 192, 64, 96, 2, false, EPI, 64, 4>(p, A, B, M, N, K, epi, part, s);
       case T256x128: return launch_bf16<256, 128, 64, 64, 3, false, EPI>(p, A, B, M, N, K, epi, part, s);
       case T128x128: return launch_bf16<128, 128, 32, 64, 4, true, EPI>(p, A, B, M, N, K, epi, part, s);
       // all-rows tiles of skinny products: four wavefronts stacked along M share one weight slice
