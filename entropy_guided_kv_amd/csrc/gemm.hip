@@ -182,9 +182,8 @@ gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, 
   constexpr int SA = BM * ROWB, SB = BN * ROWB;
   constexpr int B_RING = ASYM ? NSTG * SA : 0;
   constexpr int LDS_BYTES = ASYM ? NSTG * SA + NSB * SB : NSTG * STAGE;
-  // (the waits of the separate ring below are written for 2 A stages and 3 or 4 B stages)
-  static_assert(!ASYM || (!LATE && NSTG == 2 && (NSB == 3 || NSB == 4) && NSTG * LPA + NSB * LPB < 64),
-                "separate B ring");
+  // (the waits of the separate ring below are written for 2 A stages and at least 3 B stages)
+  static_assert(!ASYM || (!LATE && NSTG == 2 && NSB >= 3 && NSTG * LPA + NSB * LPB < 64), "separate B ring");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int MT = (M + BM - 1) / BM;
